@@ -1,0 +1,248 @@
+"""Pins of the CPU oracle: checks against things other than the oracle itself.
+
+Every function takes an oracle handle (``oracle.COracle``) so that the same
+checks can be run against deliberately broken builds (see
+``test_oracle_mutants.py``). Each raises AssertionError on a mismatch.
+
+What fixes each expected value:
+
+* ``pin_brute``          a second, dense formulation (``oracle.brute``).
+* ``pin_rowsum``         softmax rows sum to one, so their head mean does too.
+* ``pin_support``        non-zeros only at selected, in-range, visible keys;
+                         visibility from torch's lower-right causal bias.
+* ``pin_torch_softmax``  torch.softmax over the selected keys' scores
+                         (scores from torch matmul), averaged over heads.
+* ``pin_sdpa_full``      selecting every key reduces the operation to the
+                         head mean of attention weights: torch
+                         scaled_dot_product_attention with V = identity and
+                         the lower-right causal bias mapped to compressed keys.
+* ``pin_q_zero``         q = 0 gives 1/|T| on the used keys.
+* ``pin_arbitrary_lse``  with an lse shifted by d_g the row sum is the head
+                         mean of exp(-d_g).
+* ``pin_permutation``    entry order and a joint head permutation do not
+                         change the result.
+* ``pin_hand``           hand-derived closed forms (tests/golden).
+"""
+
+from __future__ import annotations
+
+import numpy as np
+import torch
+from torch.nn.attention.bias import causal_lower_right
+
+from oracle import brute
+from tests import cases as C
+
+
+# ----------------------------------------------------------------------------
+# independent helpers (library definitions, not the oracle's code)
+
+def library_visibility(s1, s2, r, res, mask_mode):
+    """(s1, s2) bool: compressed key j visible to query i.
+
+    torch's lower-right causal bias over the original key positions
+    (s2*r + res of them); a compressed key is visible when the last original
+    position it covers is.
+    """
+    if mask_mode == 0:
+        return np.ones((s1, s2), dtype=bool)
+    L = s2 * r + res
+    clr = causal_lower_right(s1, L)._materialize(torch.device("cpu")).numpy()
+    last = (np.arange(s2) + 1) * r - 1
+    return clr[:, last]
+
+
+def used_entries(p):
+    """Per row: (first k row, first output column, local key ids of the used
+    entries in entry order)."""
+    R, K = p.rows, p.topk
+    idx = p.sparse_indices.reshape(R, K)
+    tl = None if p.topk_length is None else p.topk_length.reshape(R)
+    out = [None] * R
+    for (b, q0, q1, k0, k1) in C.seq_bounds(p):
+        s2 = k1 - k0
+        res = 0 if p.cmp_residual_k is None else int(p.cmp_residual_k[b])
+        vis = library_visibility(q1 - q0, s2, p.cmp_ratio, res, p.mask_mode)
+        for r in range(q0, q1):
+            n = K if tl is None else min(max(int(tl[r]), 0), K)
+            js = []
+            for t in range(n):
+                j = int(idx[r, t])
+                if 0 <= j < s2 and vis[r - q0, j]:
+                    js.append(j)
+            out[r] = (k0, C.out_col0(p, b), js)
+    return out
+
+
+def _q_k(p):
+    R, G, D = p.rows, p.groups, p.head_dim
+    return (p.q.reshape(R, G, D).double(), p.k.reshape(-1, D).double())
+
+
+def _scale32(p):
+    return float(np.float32(p.softmax_scale))
+
+
+# ----------------------------------------------------------------------------
+# pins
+
+def pin_brute(orc, problems):
+    for name, p in problems:
+        p = C.clone(p)
+        l32, _ = orc.lse(p)
+        lb = brute.lse(p)
+        fin = np.isfinite(lb)
+        assert np.array_equal(fin, np.isfinite(l32)), name
+        np.testing.assert_allclose(l32[fin], lb[fin], rtol=2e-7, atol=1e-7, err_msg=name)
+        p.softmax_lse = l32.reshape(p.lse_shape())
+        o = orc.l1norm(p)
+        ob = brute.l1norm(p, p.softmax_lse)
+        np.testing.assert_allclose(o, ob, rtol=2e-7, atol=1e-12, err_msg=name)
+
+
+def pin_rowsum(orc, problems):
+    for name, p in problems:
+        p = C.clone(p)
+        orc.fill_lse(p)
+        o = orc.l1norm(p).astype(np.float64)
+        used = used_entries(p)
+        for r, (k0, c0, js) in enumerate(used):
+            if js:
+                assert abs(o[r].sum() - 1.0) <= 2e-6, (name, r, o[r].sum())
+            else:
+                assert not o[r].any(), (name, r)
+
+
+def pin_support(orc, problems):
+    for name, p in problems:
+        p = C.clone(p)
+        orc.fill_lse(p)
+        o = orc.l1norm(p)
+        used = used_entries(p)
+        for r, (k0, c0, js) in enumerate(used):
+            allowed = np.zeros(p.out_width, dtype=bool)
+            allowed[[c0 + j for j in js]] = True
+            assert not o[r][~allowed].any(), (name, r)
+            assert (o[r][allowed] > 0).all(), (name, r)
+            assert (o[r] <= 1.0).all(), (name, r)
+
+
+def expected_by_torch_softmax(p):
+    """(R, W) float64: head mean of torch.softmax over the used keys."""
+    qd, kd = _q_k(p)
+    sc = _scale32(p)
+    out = np.zeros((p.rows, p.out_width))
+    for r, (k0, c0, js) in enumerate(used_entries(p)):
+        if not js:
+            continue
+        J = torch.tensor(js, dtype=torch.long)
+        s = (qd[r] @ kd[k0 + J].T) * sc                 # (G, |J|)
+        w = torch.softmax(s, dim=-1).mean(dim=0).numpy()
+        np.add.at(out[r], c0 + np.asarray(js), w)
+    return out
+
+
+def pin_torch_softmax(orc, problems):
+    for name, p in problems:
+        p = C.clone(p)
+        orc.fill_lse(p)
+        o = orc.l1norm(p)
+        e = expected_by_torch_softmax(p)
+        np.testing.assert_allclose(o, e, rtol=3e-6, atol=1e-9, err_msg=name)
+
+
+def pin_sdpa_full(orc, problems):
+    for name, p in problems:
+        f = C.full_selection(p)
+        orc.fill_lse(f)
+        o = orc.l1norm(f)
+        qd, kd = _q_k(f)
+        sc = _scale32(f)
+        for (b, q0, q1, k0, k1) in C.seq_bounds(f):
+            s1, s2 = q1 - q0, k1 - k0
+            if s1 == 0 or s2 == 0:
+                continue
+            res = 0 if f.cmp_residual_k is None else int(f.cmp_residual_k[b])
+            vis = torch.from_numpy(library_visibility(s1, s2, f.cmp_ratio, res,
+                                                      f.mask_mode))
+            qq = qd[q0:q1].permute(1, 0, 2).unsqueeze(0)             # (1, G, s1, D)
+            kk = kd[k0:k1].expand(f.groups, s2, -1).unsqueeze(0)      # (1, G, s2, D)
+            vv = torch.eye(s2, dtype=torch.float64).expand(1, f.groups, s2, s2)
+            w = torch.nn.functional.scaled_dot_product_attention(
+                qq, kk, vv, attn_mask=vis, scale=sc)                  # (1, G, s1, s2)
+            w = w[0].mean(dim=0).numpy()                              # (s1, s2)
+            live = vis.any(dim=1).numpy()
+            c0 = C.out_col0(f, b)
+            np.testing.assert_allclose(o[q0:q1][live, c0:c0 + s2], w[live], rtol=3e-6,
+                                       atol=1e-9, err_msg=name)
+            assert not o[q0:q1][~live].any(), name
+
+
+def pin_q_zero(orc, problems):
+    for name, p in problems:
+        z = C.clone(p)
+        z.q = torch.zeros_like(z.q)
+        orc.fill_lse(z)
+        o = orc.l1norm(z)
+        for r, (k0, c0, js) in enumerate(used_entries(z)):
+            e = np.zeros(z.out_width)
+            if js:
+                np.add.at(e, c0 + np.asarray(js), 1.0 / len(js))
+            np.testing.assert_allclose(o[r], e, rtol=2e-7, atol=1e-12,
+                                       err_msg=f"{name} row {r}")
+
+
+def pin_arbitrary_lse(orc, problems):
+    for i, (name, p) in enumerate(problems):
+        a = C.clone(p)
+        l32, _ = orc.lse(a)
+        rng = np.random.Generator(np.random.PCG64(100 + i))
+        d = rng.uniform(-1.0, 1.0, size=l32.shape).astype(np.float32)
+        shifted = (l32 + d).astype(np.float32)
+        o = orc.l1norm(a, softmax_lse=shifted.reshape(a.lse_shape())).astype(np.float64)
+        # exp(lse_true - shifted) with lse_true ~ l32 within half an fp32 ulp
+        with np.errstate(invalid="ignore"):
+            expect = np.exp(l32.astype(np.float64) - shifted.astype(np.float64)).mean(axis=1)
+        for r, (k0, c0, js) in enumerate(used_entries(a)):
+            if js:
+                assert abs(o[r].sum() - expect[r]) <= 4e-6 * expect[r] + 1e-9, (name, r)
+
+
+def pin_permutation(orc, problems):
+    for i, (name, p) in enumerate(problems):
+        a = C.clone(p)
+        orc.fill_lse(a)
+        o = orc.l1norm(a)
+        rng = np.random.Generator(np.random.PCG64(200 + i))
+        # entry order within each row's first n entries
+        b = C.clone(a)
+        R, K = b.rows, b.topk
+        idx = b.sparse_indices.reshape(R, K)
+        tl = None if b.topk_length is None else b.topk_length.reshape(R)
+        for r in range(R):
+            n = K if tl is None else min(max(int(tl[r]), 0), K)
+            idx[r, :n] = idx[r, :n][rng.permutation(n)]
+        ob = orc.l1norm(b)
+        np.testing.assert_array_equal(o, ob, err_msg=name)
+        # joint head permutation of q and lse
+        c = C.clone(a)
+        perm = torch.from_numpy(rng.permutation(c.groups))
+        qf = c.q.reshape(c.rows, c.groups, c.head_dim)[:, perm]
+        c.q = qf.reshape(c.q.shape).contiguous()
+        lf = c.softmax_lse.reshape(c.rows, c.groups)[:, perm.numpy()]
+        c.softmax_lse = np.ascontiguousarray(lf).reshape(c.lse_shape())
+        oc = orc.l1norm(c)
+        np.testing.assert_allclose(o, oc, rtol=1e-6, atol=1e-12, err_msg=name)
+
+
+def pin_hand(orc):
+    for name, p, exp_lse, exp_out in C.load_hand_examples():
+        l32, _ = orc.lse(p)
+        np.testing.assert_allclose(l32, exp_lse, rtol=1e-7, err_msg=name)
+        p.softmax_lse = l32.reshape(p.lse_shape())
+        o = orc.l1norm(p)
+        np.testing.assert_allclose(o, exp_out, rtol=1e-6, atol=1e-12, err_msg=name)
+
+
+ALL_PINS = [pin_brute, pin_rowsum, pin_support, pin_torch_softmax, pin_sdpa_full,
+            pin_q_zero, pin_arbitrary_lse, pin_permutation]
