@@ -1,0 +1,203 @@
+#!/usr/bin/env python3
+"""Benchmark of the sparse softmax-L1Norm hot path on one MI355X.
+
+One step = one pass of the whole path over one batch of synthetic input:
+the metadata call (host work split) plus the main call (gather, MFMA QK,
+mask, exp(s - lse), head mean, zero-filled row write), inputs already in
+HBM. Default workload: DeepSeek-V3.2-shaped BSND (B=1, S1=S2=4096, N1=128,
+N2=1, D=512, topk=2048, right-down causal, bf16).
+
+Prints ONE JSON line. ``value`` is QK TFLOP/s = 2*N1*D*(valid pairs) / the
+average step time; the effective HBM GB/s of the same step is given too.
+``roofline`` reports the dominant kernel (the only kernel) against the
+MI355X dense bf16/fp16 MFMA peak or the HBM peak, whichever bounds the
+workload; its duration is measured with HIP events on the stream the kernel
+is launched on. ``cpu_baseline`` times the CPU oracle (the test checker, as
+it stands) on a bounded sample of the same workload's rows.
+
+softmax_lse: timing runs use a stand-in of the right shape and magnitude
+(log n + D*scale^2/2 per row), not the oracle's exact values; the work done
+does not depend on the values.
+"""
+
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+PEAK_MFMA_TFLOPS = {"bf16": 2500.0, "fp16": 2500.0}   # MI355X dense, published
+PEAK_HBM_GBPS = 8000.0                                  # MI355X HBM3E, published
+
+
+def log(msg):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def algorithmic(p):
+    """(QK flops, unique HBM bytes) of one call on Problem p."""
+    pairs = p.valid_pairs()
+    flops = 2.0 * p.heads_q * p.head_dim * pairs
+    nbytes = (p.q.numel() * p.q.element_size() + p.k.numel() * p.k.element_size()
+              + p.rows * p.groups * 4                       # softmax_lse
+              + p.sparse_indices.size * 4
+              + (p.topk_length.size * 4 if p.topk_length is not None else 0)
+              + (p.cu_seqlens_q.size * 8 if p.cu_seqlens_q is not None else 0)
+              + (p.cmp_residual_k.size * 4 if p.cmp_residual_k is not None else 0)
+              + p.rows * p.out_width * 4)                   # output, zero-filled
+    return flops, float(nbytes), pairs
+
+
+def cpu_baseline(p, target_s):
+    """Time the CPU oracle on evenly spaced rows of the workload."""
+    import oracle
+    R = p.rows
+    n = p.topk_length.reshape(R).astype(np.int64)
+    # calibrate on a few rows, then size the sample for ~target_s seconds
+    cal = np.linspace(0, R - 1, 8).astype(np.int64)
+    t0 = time.perf_counter()
+    oracle.l1norm(p, rows=cal)
+    t_cal = time.perf_counter() - t0
+    per_pair = t_cal / max(int(n[cal].sum()), 1)
+    want_pairs = target_s / max(per_pair, 1e-12)
+    count = int(np.clip(want_pairs / max(n.mean(), 1.0), 8, R))
+    rows = np.linspace(0, R - 1, count).astype(np.int64)
+    log(f"cpu baseline: oracle on {count} rows (~{count * n.mean() * per_pair:.1f} s)")
+    t0 = time.perf_counter()
+    oracle.l1norm(p, rows=rows)
+    t = time.perf_counter() - t0
+    pairs = int(n[rows].sum())
+    flops = 2.0 * p.heads_q * p.head_dim * pairs
+    return {"value": flops / t / 1e12, "unit": "TFLOP/s", "cores": oracle.num_threads(),
+            "kind": "oracle",
+            "sample": f"{count} evenly spaced rows of {R} ({pairs} valid pairs), "
+                      f"oracle_l1norm given lse, {t:.1f} s wall"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="dsv32")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    rank = int(os.environ.get("RANK", "0"))
+    if args.gpus != 1 or world != 1:
+        if rank == 0:
+            print("bench.py measures one GPU only: this path has no multi-GPU mode "
+                  "(query rows shard across GPUs with no exchange); run with --gpus 1",
+                  file=sys.stderr, flush=True)
+        sys.exit(2)
+
+    import torch
+    import sparse_mla_attention_02_amd as smla
+    import workloads
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+
+    log(f"generating workload {args.workload}")
+    p = workloads.generate(args.workload)
+    flops, nbytes, pairs = algorithmic(p)
+    lse = workloads.lse_standin(p)
+    p.softmax_lse = lse
+
+    def t(a):
+        return None if a is None else torch.from_numpy(np.ascontiguousarray(a)).to(dev)
+
+    q, k = p.q.to(dev), p.k.to(dev)
+    lse_d = t(lse)
+    idx, tlen = t(p.sparse_indices), t(p.topk_length)
+    cu_q, cu_k, res = t(p.cu_seqlens_q), t(p.cu_seqlens_k), t(p.cmp_residual_k)
+    cu_q_h = None if p.cu_seqlens_q is None else torch.from_numpy(p.cu_seqlens_q)
+    cu_k_h = None if p.cu_seqlens_k is None else torch.from_numpy(p.cu_seqlens_k)
+    out = torch.empty(p.out_shape(), dtype=torch.float32, device=dev)
+    stream = torch.cuda.current_stream(dev)
+
+    def step(before=None, after=None):
+        md = smla.smla_l1norm_metadata(
+            p.heads_q, p.heads_k, p.head_dim, cu_seqlens_q=cu_q_h, cu_seqlens_k=cu_k_h,
+            batch_size=p.batch, max_seqlen_q=p.max_seqlen_q, max_seqlen_k=p.max_seqlen_k,
+            topk=p.topk, layout_q=p.layout, layout_k=p.layout, mask_mode=p.mask_mode,
+            cmp_ratio=p.cmp_ratio, device=0)
+        if before is not None:
+            before.record(stream)
+        smla.smla_softmax_l1norm(
+            q, k, lse_d, sparse_indices=idx, cu_seqlens_q=cu_q, cu_seqlens_k=cu_k,
+            cmp_residual_k=res, topk_length=tlen, metadata=md,
+            softmax_scale=p.softmax_scale, max_seqlen_k=p.max_seqlen_k,
+            cmp_ratio=p.cmp_ratio, mask_mode=p.mask_mode, layout_q=p.layout,
+            layout_k=p.layout, out=out)
+        if after is not None:
+            after.record(stream)
+        return md
+
+    log(f"warmup {args.warmup} steps")
+    for _ in range(args.warmup):
+        md = step()
+    torch.cuda.synchronize()
+
+    # timed region: K steps, each kernel bracketed by events on its stream
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(args.steps)]
+    log(f"timing {args.steps} steps")
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(ev[i][0], ev[i][1])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    kernel_ms = [a.elapsed_time(b) for a, b in ev]
+    ms_step = wall * 1e3 / args.steps
+    kms = float(np.mean(kernel_ms))
+
+    tflops = flops / (ms_step * 1e-3) / 1e12
+    gbps = nbytes / (ms_step * 1e-3) / 1e9
+    k_tflops = flops / (kms * 1e-3) / 1e12
+    k_gbps = nbytes / (kms * 1e-3) / 1e9
+    intensity = flops / nbytes
+    ridge = PEAK_MFMA_TFLOPS[p.dtype] * 1e12 / (PEAK_HBM_GBPS * 1e9)
+    if intensity >= ridge:
+        roof = {"bound": "mfma", "achieved": round(k_tflops, 2),
+                "peak": PEAK_MFMA_TFLOPS[p.dtype], "unit": "TFLOP/s",
+                "frac": round(k_tflops / PEAK_MFMA_TFLOPS[p.dtype], 4)}
+    else:
+        roof = {"bound": "hbm", "achieved": round(k_gbps, 1), "peak": PEAK_HBM_GBPS,
+                "unit": "GB/s", "frac": round(k_gbps / PEAK_HBM_GBPS, 4)}
+    roof["traffic"] = None
+    roof["kernel"] = "smla_l1norm_kernel"
+    roof["kernel_ms"] = round(kms, 4)
+    roof["algorithmic_flops"] = flops
+    roof["algorithmic_bytes"] = nbytes
+
+    line = {
+        "metric": "QK TFLOP/s + HBM GB/s, sparse softmax-L1Norm N1=128 topk=2048 D=512",
+        "value": round(tflops, 2), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms_step, 4), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": p.dtype, "data": "synthetic",
+        "hbm_gbps": round(gbps, 1), "hbm_frac": round(gbps / PEAK_HBM_GBPS, 4),
+        "config": {"workload": p.name, "layout": p.layout, "batch": p.batch,
+                   "seqlen_q": p.seqlen_q, "seqlen_k": p.seqlen_k, "heads_q": p.heads_q,
+                   "heads_k": p.heads_k, "head_dim": p.head_dim, "topk": p.topk,
+                   "mask_mode": p.mask_mode, "cmp_ratio": p.cmp_ratio,
+                   "valid_pairs": pairs, "workgroups": int(md[4]),
+                   "lse": "stand-in"},
+        "roofline": roof,
+        "cpu_baseline": None,
+    }
+    if not args.no_cpu_baseline:
+        line["cpu_baseline"] = cpu_baseline(p, args.cpu_seconds)
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

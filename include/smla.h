@@ -1,0 +1,197 @@
+/*
+ * smla.h - C ABI of the sparse Flash-MLA Softmax-L1Norm library for MI355X
+ * (gfx950).
+ *
+ * The operation is the one the "SparseFlashMlaSoftmaxL1Norm" article (CANN
+ * ops-transformer, pnsm.cn) defines. For every query row it gathers the
+ * row's top-k selected rows of the single shared latent K (N2 = 1, D = 512),
+ * forms Q.K^T * scale for the G = N1/N2 query heads, masks the scores, turns
+ * them into probabilities with the forward pass's log-sum-exp as
+ * exp(s - lse), and averages the G probability rows into one fp32 row
+ * (section 三阶段计算公式, three-stage formula; output shapes from section
+ * 参数说明).
+ *
+ * As on the page, a call is split in two: a host metadata call that plans
+ * the work split (section 算子定位与配套关系, metadata fields), then the
+ * main call that runs on the GPU.
+ *
+ * Conventions for every entry point:
+ *  - Tensor pointers are DEVICE pointers unless the name ends in _host.
+ *    Tensors are dense, row-major and contiguous in the stated layout.
+ *  - The caller owns every buffer and the stream. The library allocates no
+ *    device memory and needs no workspace.
+ *  - All argument checks happen before anything is enqueued. On an error
+ *    nothing is written and nothing is launched; smla_last_error() gives a
+ *    message. A success of smla_softmax_l1norm means "enqueued on stream":
+ *    results are ready once the stream has synchronised.
+ *  - Calls are thread-safe and deterministic: the same inputs give the same
+ *    bits on every run (the page's 约束说明 section states determinism).
+ */
+#ifndef SMLA_H
+#define SMLA_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Number of int32 elements of a metadata buffer (64 on the page too). */
+#define SMLA_METADATA_SIZE 64
+
+/* Status codes. The first two reuse the numeric values of the page's aclnn
+ * errors (section 调用方式一 aclnn API): 161001 = an illegal null pointer,
+ * 161002 = an unsupported dtype / value or a missing required tensor. */
+typedef int32_t smla_status_t;
+enum {
+    SMLA_SUCCESS = 0,
+    SMLA_ERR_PARAM_NULLPTR = 161001,
+    SMLA_ERR_PARAM_INVALID = 161002,
+    SMLA_ERR_UNSUPPORTED = 161101, /* valid on the page, not built here (dense
+                                      path without sparse_indices, seqused_q/k) */
+    SMLA_ERR_RUNTIME = 561001      /* a HIP runtime call failed */
+};
+
+enum { SMLA_LAYOUT_BSND = 0, SMLA_LAYOUT_TND = 1 };
+enum { SMLA_DTYPE_FP16 = 0, SMLA_DTYPE_BF16 = 1 };
+enum { SMLA_MASK_NONE = 0, SMLA_MASK_RIGHT_DOWN_CAUSAL = 3 };
+
+/* Metadata layout (int32[64]).
+ * Fields 0..4 are the page's (section 算子定位与配套关系):
+ *   [0] total      number of query rows to balance, R * N2
+ *                  (R = B*S1 for BSND, T1 for TND)
+ *   [1] former     rows per regular workgroup = ceil(total / cores)
+ *   [2] remain     rows per tail workgroup    = floor(total / cores)
+ *   [3] remainNum  number of tail workgroups: cores - (total mod cores)
+ *                  when the division leaves a remainder, else 0
+ *   [4] cores      workgroups launched = min(total, core budget); the page
+ *                  caps this at 36 Ascend cores, here the budget is the
+ *                  number of co-resident workgroups of the kernel on the
+ *                  GPU (CU count x resident workgroups per CU)
+ * Fields 5.. are this library's own, checked by smla_softmax_l1norm:
+ *   [5] magic 0x534D4C41, [6] version, [7] layout, [8] N1, [9] N2, [10] D,
+ *   [11] B, [12] max_seqlen_q, [13] max_seqlen_k, [14] topk,
+ *   [15] mask_mode, [16] cmp_ratio, [17] R, [18] rows of k (B*S2 or T2),
+ *   [19] row order (1 = snake: workgroup w takes rows w, 2C-1-w, 2C+w, ...),
+ *   [20] head tiles per row (kernel variant), [21] device, [22] CU count,
+ *   [23] resident workgroups per CU; [24..63] zero.
+ */
+#define SMLA_META_MAGIC 0x534D4C41
+
+/*
+ * smla_l1norm_metadata - plan the work split (host only, no device work).
+ *
+ * Mirrors the page's sparse_flash_mla_softmax_l1_norm_metadata parameters
+ * (section "metadata 前置算子"), with the sequence tensors in HOST memory.
+ *
+ *   num_heads_q, num_heads_k, head_dim  N1 in [1,128], N2 == 1, D == 512
+ *   cu_seqlens_q_host, cu_seqlens_k_host  int32 (B+1), required for TND
+ *                                         (prefix sums, first entry 0);
+ *                                         ignored for BSND
+ *   seqused_q_host, seqused_k_host      must be NULL (not supported)
+ *   cmp_residual_k_host, topk_length_host  optional, only range-checked
+ *                                         lengths are not used for balance
+ *   batch_size     B (> 0): batches for BSND, sequences for TND (the
+ *                  length of cu_seqlens_q minus one)
+ *   max_seqlen_q, max_seqlen_k  S1, S2: required > 0 for BSND (the padded
+ *                  per-batch lengths); for TND 0 means "from cu_seqlens"
+ *   topk           K, number of indices per row; must be >= 1 (0 = dense,
+ *                  not supported)
+ *   layout_q, layout_k  SMLA_LAYOUT_*, must be equal
+ *   mask_mode      0 or 3; cmp_ratio in [1,128]
+ *   device         HIP device ordinal whose CU count sizes the grid
+ *   core_budget    workgroups to split over; 0 = the device's co-resident
+ *                  capacity for this problem's kernel variant
+ *   metadata_host  out: int32[SMLA_METADATA_SIZE], caller-owned
+ *
+ * Errors: SMLA_ERR_PARAM_NULLPTR (metadata_host NULL, TND without
+ * cu_seqlens), SMLA_ERR_PARAM_INVALID (out-of-range value, layout mismatch,
+ * inconsistent cu_seqlens), SMLA_ERR_UNSUPPORTED (seqused_*, topk == 0),
+ * SMLA_ERR_RUNTIME (device query failed; only when core_budget == 0).
+ */
+smla_status_t smla_l1norm_metadata(
+    int64_t num_heads_q, int64_t num_heads_k, int64_t head_dim,
+    const int32_t* cu_seqlens_q_host, const int32_t* cu_seqlens_k_host,
+    const int32_t* seqused_q_host, const int32_t* seqused_k_host,
+    const int32_t* cmp_residual_k_host, const int32_t* topk_length_host,
+    int64_t batch_size, int64_t max_seqlen_q, int64_t max_seqlen_k, int64_t topk,
+    int32_t layout_q, int32_t layout_k, int64_t mask_mode, int64_t cmp_ratio,
+    int32_t device, int32_t core_budget, int32_t* metadata_host);
+
+/*
+ * smla_softmax_l1norm - the main call; enqueues the kernel on `stream`.
+ *
+ * Mirrors the page's sparse_flash_mla_softmax_l1_norm / aclnn argument list
+ * (sections 参数说明 and 调用方式一 aclnn API). Shapes, all row-major:
+ *
+ *   q              (B,S1,N1,D) | (T1,N1,D), dtype `dtype`
+ *   k              (B,S2,N2,D) | (T2,N2,D), same dtype as q
+ *   softmax_lse    fp32 (B,N2,S1,G) | (N2,T1,G), natural-log forward lse
+ *   sparse_indices int32 (B,S1,N2,K) | (T1,N2,K); required (NULL selects
+ *                  the page's dense path, which returns SMLA_ERR_UNSUPPORTED).
+ *                  Entries index the keys of the row's own batch/sequence
+ *                  (0-based, local to a TND sequence); an entry is used iff
+ *                  its position is < topk_length, it lies in [0, S2_b) and
+ *                  the mask lets the key through. Used entries of one row
+ *                  must be distinct (duplicates are not supported).
+ *   cu_seqlens_q, cu_seqlens_k  int32 (B+1) device, required for TND
+ *   seqused_q, seqused_k        must be NULL (not supported)
+ *   cmp_residual_k int32 (B): original key length of batch b is
+ *                  S2_b*cmp_ratio + cmp_residual_k[b]; required when
+ *                  mask_mode == 3 and cmp_ratio != 1, else may be NULL (0)
+ *   topk_length    int32 (B,S1,N2) | (T1,N2): entries per row to look at,
+ *                  clamped to [0,K]; required when mask_mode == 0; when NULL
+ *                  every entry is looked at
+ *   metadata_host  int32[64] from smla_l1norm_metadata for the same shapes
+ *   dtype          SMLA_DTYPE_FP16 or SMLA_DTYPE_BF16
+ *   batch_size, seqlen_q, seqlen_k  B,S1,S2 (BSND) | B,T1,T2 (TND)
+ *   num_heads_q, num_heads_k, head_dim, topk  N1, N2 (== 1), D (== 512), K
+ *   softmax_scale  the page's FLOAT32 attribute; rounded to fp32 once
+ *   max_seqlen_k   accepted for the dense TND shape rule; must be >= 0
+ *   cmp_ratio      [1,128]; mask_mode 0 (none) or 3 (right-down causal:
+ *                  compressed key j of batch b is visible to query i iff
+ *                  (j+1)*cmp_ratio <= i + 1 + S2_b*cmp_ratio + res_b - S1_b)
+ *   layout_q, layout_k  SMLA_LAYOUT_*, must be equal
+ *   softmax_l1_norm fp32 out (B,S1,N2,S2) | (T1,N2,T2); every element is
+ *                  written (zeros outside the used entries). For TND a row's
+ *                  non-zeros lie in its own sequence's columns
+ *                  cu_seqlens_k[b] + j.
+ *   stream         hipStream_t (NULL = the default stream)
+ *
+ * Errors: SMLA_ERR_PARAM_INVALID when q, k, softmax_lse or softmax_l1_norm
+ * is NULL (as on the page) or a value/shape is out of range or does not
+ * match the metadata; SMLA_ERR_PARAM_NULLPTR when a conditionally required
+ * pointer is NULL (metadata, cu_seqlens for TND, cmp_residual_k,
+ * topk_length); SMLA_ERR_UNSUPPORTED for the dense path or seqused_*;
+ * SMLA_ERR_RUNTIME if the launch fails. An empty q (R == 0) or an empty
+ * output (S2/T2 == 0) returns SMLA_SUCCESS once the attributes are checked,
+ * before any pointer or the metadata is looked at, and launches nothing.
+ */
+smla_status_t smla_softmax_l1norm(
+    const void* q, const void* k, const float* softmax_lse,
+    const int32_t* sparse_indices, const int32_t* cu_seqlens_q,
+    const int32_t* cu_seqlens_k, const int32_t* seqused_q, const int32_t* seqused_k,
+    const int32_t* cmp_residual_k, const int32_t* topk_length,
+    const int32_t* metadata_host, int32_t dtype, int64_t batch_size, int64_t seqlen_q,
+    int64_t seqlen_k, int64_t num_heads_q, int64_t num_heads_k, int64_t head_dim,
+    int64_t topk, double softmax_scale, int64_t max_seqlen_k, int64_t cmp_ratio,
+    int64_t mask_mode, int32_t layout_q, int32_t layout_k, float* softmax_l1_norm,
+    void* stream);
+
+/* Elements of the output for the given shapes: B*S1*N2*S2 (BSND) or
+ * T1*N2*T2 (TND); -1 for an unknown layout or a negative size. Host only. */
+int64_t smla_output_numel(int32_t layout, int64_t batch_size, int64_t seqlen_q,
+                          int64_t num_heads_k, int64_t seqlen_k);
+
+/* Message for the last non-success status returned on this thread ("" if
+ * none). The pointer stays valid until the next call on this thread. */
+const char* smla_last_error(void);
+
+/* Library version, as MAJOR*10000 + MINOR*100 + PATCH. */
+int32_t smla_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SMLA_H */

@@ -1,0 +1,330 @@
+// Host side of the C ABI declared in include/smla.h: argument checks, the
+// metadata work split, and the kernel launch.
+//
+// Argument rules follow the "SparseFlashMlaSoftmaxL1Norm" article:
+// parameter table and shape notes (section 参数说明), constraints (section
+// 约束说明), metadata fields (section 算子定位与配套关系) and aclnn error
+// codes (section 调用方式一 aclnn API).
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <map>
+#include <mutex>
+#include <string>
+#include <tuple>
+
+#include "smla.h"
+#include "smla_internal.h"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+smla_status_t fail(smla_status_t code, const char* fmt, ...) {
+    char buf[512];
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(buf, sizeof(buf), fmt, ap);
+    va_end(ap);
+    g_last_error = buf;
+    return code;
+}
+
+smla_status_t ok() {
+    g_last_error.clear();
+    return SMLA_SUCCESS;
+}
+
+// Per (device, head tiles, layout): CU count and co-resident workgroups per
+// CU, queried once.
+std::mutex g_cap_mu;
+std::map<std::tuple<int, int, bool>, std::pair<int, int>> g_cap;
+
+hipError_t device_capacity(int device, int ht, bool tnd, int* cus, int* per_cu) {
+    {
+        std::lock_guard<std::mutex> lk(g_cap_mu);
+        auto it = g_cap.find({device, ht, tnd});
+        if (it != g_cap.end()) {
+            *cus = it->second.first;
+            *per_cu = it->second.second;
+            return hipSuccess;
+        }
+    }
+    int n = 0;
+    hipError_t e = hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, device);
+    if (e != hipSuccess) return e;
+    int cur = 0;
+    e = hipGetDevice(&cur);
+    if (e != hipSuccess) return e;
+    if (cur != device && (e = hipSetDevice(device)) != hipSuccess) return e;
+    int occ = 0;
+    e = smla::resident_per_cu(ht, true, tnd, &occ);
+    if (cur != device) (void)hipSetDevice(cur);
+    if (e != hipSuccess) return e;
+    if (occ <= 0) return hipErrorInvalidConfiguration;
+    std::lock_guard<std::mutex> lk(g_cap_mu);
+    g_cap[{device, ht, tnd}] = {n, occ};
+    *cus = n;
+    *per_cu = occ;
+    return hipSuccess;
+}
+
+constexpr int32_t kVersion = 1;
+constexpr int64_t kHeadDim = 512;
+
+// Shared checks of the scalar attributes of both calls.
+smla_status_t check_common(int64_t n1, int64_t n2, int64_t d, int32_t layout_q,
+                           int32_t layout_k, int64_t mask_mode, int64_t cmp_ratio) {
+    if (layout_q != SMLA_LAYOUT_BSND && layout_q != SMLA_LAYOUT_TND)
+        return fail(SMLA_ERR_PARAM_INVALID, "layout_q must be BSND or TND");
+    if (layout_k != layout_q)
+        return fail(SMLA_ERR_PARAM_INVALID, "layout_q and layout_k must be equal");
+    if (n2 != 1)
+        return fail(SMLA_ERR_PARAM_INVALID, "num_heads_k (N2) must be 1, got %lld",
+                    (long long)n2);
+    if (n1 < 1 || n1 > 128)
+        return fail(SMLA_ERR_PARAM_INVALID, "num_heads_q (N1) must be in [1,128], got %lld",
+                    (long long)n1);
+    if (n1 % n2 != 0)
+        return fail(SMLA_ERR_PARAM_INVALID, "N1 must be divisible by N2");
+    if (d != kHeadDim)
+        return fail(SMLA_ERR_PARAM_INVALID, "head_dim (D) must be 512, got %lld",
+                    (long long)d);
+    if (mask_mode != SMLA_MASK_NONE && mask_mode != SMLA_MASK_RIGHT_DOWN_CAUSAL)
+        return fail(SMLA_ERR_PARAM_INVALID, "mask_mode must be 0 or 3, got %lld",
+                    (long long)mask_mode);
+    if (cmp_ratio < 1 || cmp_ratio > 128)
+        return fail(SMLA_ERR_PARAM_INVALID, "cmp_ratio must be in [1,128], got %lld",
+                    (long long)cmp_ratio);
+    return SMLA_SUCCESS;
+}
+
+// Checks a host prefix-sum array of B+1 entries; returns its total and max step.
+smla_status_t check_cu(const int32_t* cu, int64_t B, const char* name, int64_t* total,
+                       int64_t* maxlen) {
+    if (cu[0] != 0) return fail(SMLA_ERR_PARAM_INVALID, "%s[0] must be 0", name);
+    int64_t mx = 0;
+    for (int64_t b = 0; b < B; ++b) {
+        const int64_t step = (int64_t)cu[b + 1] - cu[b];
+        if (step < 0)
+            return fail(SMLA_ERR_PARAM_INVALID, "%s must be non-decreasing", name);
+        if (step > mx) mx = step;
+    }
+    *total = cu[B];
+    *maxlen = mx;
+    return SMLA_SUCCESS;
+}
+
+}  // namespace
+
+extern "C" {
+
+int32_t smla_version(void) { return 10000 * 0 + 100 * 1 + 0; }
+
+const char* smla_last_error(void) { return g_last_error.c_str(); }
+
+int64_t smla_output_numel(int32_t layout, int64_t batch_size, int64_t seqlen_q,
+                          int64_t num_heads_k, int64_t seqlen_k) {
+    if (batch_size < 0 || seqlen_q < 0 || num_heads_k < 0 || seqlen_k < 0) return -1;
+    if (layout == SMLA_LAYOUT_BSND) return batch_size * seqlen_q * num_heads_k * seqlen_k;
+    if (layout == SMLA_LAYOUT_TND) return seqlen_q * num_heads_k * seqlen_k;
+    return -1;
+}
+
+smla_status_t smla_l1norm_metadata(
+    int64_t num_heads_q, int64_t num_heads_k, int64_t head_dim,
+    const int32_t* cu_seqlens_q_host, const int32_t* cu_seqlens_k_host,
+    const int32_t* seqused_q_host, const int32_t* seqused_k_host,
+    const int32_t* cmp_residual_k_host, const int32_t* topk_length_host,
+    int64_t batch_size, int64_t max_seqlen_q, int64_t max_seqlen_k, int64_t topk,
+    int32_t layout_q, int32_t layout_k, int64_t mask_mode, int64_t cmp_ratio,
+    int32_t device, int32_t core_budget, int32_t* metadata_host) {
+    (void)cmp_residual_k_host;
+    (void)topk_length_host;
+    if (!metadata_host) return fail(SMLA_ERR_PARAM_NULLPTR, "metadata_host is NULL");
+    smla_status_t st = check_common(num_heads_q, num_heads_k, head_dim, layout_q, layout_k,
+                                    mask_mode, cmp_ratio);
+    if (st != SMLA_SUCCESS) return st;
+    if (seqused_q_host || seqused_k_host)
+        return fail(SMLA_ERR_UNSUPPORTED, "seqused_q / seqused_k are not supported");
+    if (topk == 0)
+        return fail(SMLA_ERR_UNSUPPORTED, "topk == 0 (dense path) is not supported");
+    if (topk < 0) return fail(SMLA_ERR_PARAM_INVALID, "topk must be >= 1");
+    if (core_budget < 0) return fail(SMLA_ERR_PARAM_INVALID, "core_budget must be >= 0");
+
+    int64_t B = batch_size, R = 0, rows_k = 0, mq = max_seqlen_q, mk = max_seqlen_k;
+    if (layout_q == SMLA_LAYOUT_BSND) {
+        if (batch_size <= 0 || max_seqlen_q <= 0 || max_seqlen_k <= 0)
+            return fail(SMLA_ERR_PARAM_INVALID,
+                        "BSND needs batch_size, max_seqlen_q and max_seqlen_k > 0");
+        R = batch_size * max_seqlen_q;
+        rows_k = batch_size * max_seqlen_k;
+    } else {
+        if (!cu_seqlens_q_host || !cu_seqlens_k_host)
+            return fail(SMLA_ERR_PARAM_NULLPTR, "TND needs cu_seqlens_q and cu_seqlens_k");
+        if (batch_size <= 0)
+            return fail(SMLA_ERR_PARAM_INVALID,
+                        "TND needs batch_size = len(cu_seqlens_q) - 1 > 0");
+        int64_t tq, tk, mxq, mxk;
+        if ((st = check_cu(cu_seqlens_q_host, B, "cu_seqlens_q", &tq, &mxq)) != SMLA_SUCCESS)
+            return st;
+        if ((st = check_cu(cu_seqlens_k_host, B, "cu_seqlens_k", &tk, &mxk)) != SMLA_SUCCESS)
+            return st;
+        if (max_seqlen_q < 0 || max_seqlen_k < 0)
+            return fail(SMLA_ERR_PARAM_INVALID, "max_seqlen_q/k must be >= 0");
+        if (mq == 0) mq = mxq;
+        if (mk == 0) mk = mxk;
+        R = tq;
+        rows_k = tk;
+    }
+    if (R > INT32_MAX || rows_k > INT32_MAX || B > INT32_MAX)
+        return fail(SMLA_ERR_PARAM_INVALID, "sizes exceed the int32 metadata fields");
+
+    const int ht = smla::head_tiles_for(num_heads_q / num_heads_k);
+    int cus = 0, per_cu = 0;
+    int64_t budget = core_budget;
+    if (core_budget == 0) {
+        hipError_t e = device_capacity(device, ht, layout_q == SMLA_LAYOUT_TND, &cus, &per_cu);
+        if (e != hipSuccess)
+            return fail(SMLA_ERR_RUNTIME, "device %d capacity query failed: %s", device,
+                        hipGetErrorString(e));
+        budget = (int64_t)cus * per_cu;
+    }
+
+    const int64_t total = R * num_heads_k;
+    const int64_t cores = total < budget ? total : budget;
+    int32_t* m = metadata_host;
+    std::memset(m, 0, sizeof(int32_t) * SMLA_METADATA_SIZE);
+    m[0] = (int32_t)total;
+    if (cores > 0) {
+        const int64_t q = total / cores, rem = total % cores;
+        m[1] = (int32_t)(rem ? q + 1 : q);
+        m[2] = (int32_t)q;
+        m[3] = (int32_t)(rem ? cores - rem : 0);
+    }
+    m[4] = (int32_t)cores;
+    m[5] = SMLA_META_MAGIC;
+    m[6] = kVersion;
+    m[7] = layout_q;
+    m[8] = (int32_t)num_heads_q;
+    m[9] = (int32_t)num_heads_k;
+    m[10] = (int32_t)head_dim;
+    m[11] = (int32_t)B;
+    m[12] = (int32_t)mq;
+    m[13] = (int32_t)mk;
+    m[14] = (int32_t)topk;
+    m[15] = (int32_t)mask_mode;
+    m[16] = (int32_t)cmp_ratio;
+    m[17] = (int32_t)R;
+    m[18] = (int32_t)rows_k;
+    m[19] = 1;  // snake row order
+    m[20] = ht;
+    m[21] = device;
+    m[22] = cus;
+    m[23] = per_cu;
+    return ok();
+}
+
+smla_status_t smla_softmax_l1norm(
+    const void* q, const void* k, const float* softmax_lse,
+    const int32_t* sparse_indices, const int32_t* cu_seqlens_q,
+    const int32_t* cu_seqlens_k, const int32_t* seqused_q, const int32_t* seqused_k,
+    const int32_t* cmp_residual_k, const int32_t* topk_length,
+    const int32_t* metadata_host, int32_t dtype, int64_t batch_size, int64_t seqlen_q,
+    int64_t seqlen_k, int64_t num_heads_q, int64_t num_heads_k, int64_t head_dim,
+    int64_t topk, double softmax_scale, int64_t max_seqlen_k, int64_t cmp_ratio,
+    int64_t mask_mode, int32_t layout_q, int32_t layout_k, float* softmax_l1_norm,
+    void* stream) {
+    if (dtype != SMLA_DTYPE_FP16 && dtype != SMLA_DTYPE_BF16)
+        return fail(SMLA_ERR_PARAM_INVALID, "dtype must be FLOAT16 or BFLOAT16");
+    smla_status_t st = check_common(num_heads_q, num_heads_k, head_dim, layout_q, layout_k,
+                                    mask_mode, cmp_ratio);
+    if (st != SMLA_SUCCESS) return st;
+    if (max_seqlen_k < 0) return fail(SMLA_ERR_PARAM_INVALID, "max_seqlen_k must be >= 0");
+    if (seqused_q || seqused_k)
+        return fail(SMLA_ERR_UNSUPPORTED, "seqused_q / seqused_k are not supported");
+    if (batch_size < 0 || seqlen_q < 0 || seqlen_k < 0)
+        return fail(SMLA_ERR_PARAM_INVALID, "sizes must be >= 0");
+    const bool tnd = layout_q == SMLA_LAYOUT_TND;
+    if (tnd && batch_size < 1)
+        return fail(SMLA_ERR_PARAM_INVALID, "TND needs batch_size >= 1");
+
+    const int64_t R = tnd ? seqlen_q : batch_size * seqlen_q;
+    const int64_t rows_k = tnd ? seqlen_k : batch_size * seqlen_k;
+    const int64_t W = seqlen_k;
+    // empty q or empty output: nothing is read or written (page: an empty q
+    // returns directly)
+    if (R == 0 || W == 0) return ok();
+
+    if (!q || !k || !softmax_lse || !softmax_l1_norm)
+        return fail(SMLA_ERR_PARAM_INVALID,
+                    "q, k, softmax_lse and softmax_l1_norm are required");
+    if (!sparse_indices)
+        return fail(SMLA_ERR_UNSUPPORTED,
+                    "the dense path (no sparse_indices) is not supported");
+    if (topk < 1) return fail(SMLA_ERR_PARAM_INVALID, "topk must be >= 1 with sparse_indices");
+    if (!metadata_host)
+        return fail(SMLA_ERR_PARAM_NULLPTR,
+                    "metadata is required (from smla_l1norm_metadata)");
+    if (tnd && (!cu_seqlens_q || !cu_seqlens_k))
+        return fail(SMLA_ERR_PARAM_NULLPTR, "TND needs cu_seqlens_q and cu_seqlens_k");
+    if (mask_mode == SMLA_MASK_RIGHT_DOWN_CAUSAL && cmp_ratio != 1 && !cmp_residual_k)
+        return fail(SMLA_ERR_PARAM_NULLPTR,
+                    "cmp_residual_k is required when mask_mode == 3 and cmp_ratio != 1");
+    if (mask_mode == SMLA_MASK_NONE && !topk_length)
+        return fail(SMLA_ERR_PARAM_NULLPTR,
+                    "topk_length is required when mask_mode == 0 with sparse_indices");
+    if (R > INT32_MAX || rows_k > INT32_MAX || topk > INT32_MAX)
+        return fail(SMLA_ERR_PARAM_INVALID, "sizes exceed the supported range");
+
+    const int32_t* m = metadata_host;
+    if (m[5] != SMLA_META_MAGIC || m[6] != kVersion)
+        return fail(SMLA_ERR_PARAM_INVALID, "metadata was not made by smla_l1norm_metadata");
+    if (m[7] != layout_q || m[8] != num_heads_q || m[9] != num_heads_k ||
+        m[10] != head_dim || m[11] != batch_size || m[14] != topk ||
+        m[15] != mask_mode || m[16] != cmp_ratio || m[17] != R || m[18] != rows_k ||
+        m[0] != R * num_heads_k)
+        return fail(SMLA_ERR_PARAM_INVALID, "metadata does not match the call's shapes");
+    if (!tnd && (m[12] != seqlen_q || m[13] != seqlen_k))
+        return fail(SMLA_ERR_PARAM_INVALID, "metadata does not match S1/S2");
+    if (m[4] < 1 || m[4] > m[0])
+        return fail(SMLA_ERR_PARAM_INVALID, "metadata core count is out of range");
+
+    smla::KernelArgs a;
+    a.q = q;
+    a.k = k;
+    a.lse = softmax_lse;
+    a.idx = sparse_indices;
+    a.topk_len = topk_length;
+    a.cu_q = cu_seqlens_q;
+    a.cu_k = cu_seqlens_k;
+    a.cmp_res = cmp_residual_k;
+    a.out = softmax_l1_norm;
+    a.R = R;
+    a.W = W;
+    a.rows_k = rows_k;
+    a.B = (int32_t)batch_size;
+    a.S1 = tnd ? 0 : (int32_t)seqlen_q;
+    a.S2 = tnd ? 0 : (int32_t)seqlen_k;
+    a.G = (int32_t)(num_heads_q / num_heads_k);
+    a.K = (int32_t)topk;
+    a.mask_mode = (int32_t)mask_mode;
+    a.cmp_ratio = (int32_t)cmp_ratio;
+    const float scale32 = (float)softmax_scale;  // the attribute is FLOAT32
+    a.c_scale = scale32 * 1.4426950408889634f;
+    a.inv_g = 1.0f / (float)a.G;
+    a.num_wg = m[4];
+    a.snake = m[19];
+
+    const int ht = smla::head_tiles_for(a.G);
+    hipError_t e = smla::launch(a, ht, dtype == SMLA_DTYPE_BF16, tnd,
+                                static_cast<hipStream_t>(stream));
+    if (e != hipSuccess)
+        return fail(SMLA_ERR_RUNTIME, "kernel launch failed: %s", hipGetErrorString(e));
+    return ok();
+}
+
+}  // extern "C"

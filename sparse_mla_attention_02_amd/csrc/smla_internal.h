@@ -1,0 +1,45 @@
+// Internal interface between the C-ABI host code and the gfx950 kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace smla {
+
+// Everything a kernel launch needs, passed by value as the kernel argument.
+struct KernelArgs {
+    const void* q;            // (R, G, 512) bf16/fp16, N2 == 1 so N1 == G
+    const void* k;            // (rows_k, 512) bf16/fp16
+    const float* lse;         // (R, G) fp32
+    const int32_t* idx;       // (R, K) int32
+    const int32_t* topk_len;  // (R) or nullptr
+    const int32_t* cu_q;      // (B+1) for TND
+    const int32_t* cu_k;      // (B+1) for TND
+    const int32_t* cmp_res;   // (B) or nullptr
+    float* out;               // (R, W) fp32
+    int64_t R;                // query rows
+    int64_t W;                // output row width (S2 or T2)
+    int64_t rows_k;           // rows of k (B*S2 or T2)
+    int32_t B;                // batches or sequences
+    int32_t S1, S2;           // BSND per-batch lengths
+    int32_t G;                // query heads per kv head
+    int32_t K;                // indices per row
+    int32_t mask_mode;        // 0 or 3
+    int32_t cmp_ratio;        // [1, 128]
+    float c_scale;            // softmax_scale * log2(e)
+    float inv_g;              // 1 / G
+    int32_t num_wg;           // workgroups launched (metadata field 4)
+    int32_t snake;            // row order: 1 = snake, 0 = plain strided
+};
+
+// Head tiles of 32 heads each that one row needs: 1, 2 or 4.
+inline int head_tiles_for(int64_t G) { return G <= 32 ? 1 : (G <= 64 ? 2 : 4); }
+
+// Enqueue the kernel variant for (head_tiles, bf16, tnd).
+hipError_t launch(const KernelArgs& a, int head_tiles, bool bf16, bool tnd,
+                  hipStream_t stream);
+
+// Co-resident workgroups per CU of that variant.
+hipError_t resident_per_cu(int head_tiles, bool bf16, bool tnd, int* out);
+
+}  // namespace smla

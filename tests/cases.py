@@ -68,15 +68,18 @@ def inject_edges(p, seed=0, invisible=True, out_of_range=True, shorten=True):
     tlen = None if c.topk_length is None else c.topk_length.reshape(R)
     for (b, q0, q1, k0, k1) in seq_bounds(c):
         s2 = k1 - k0
+        res = 0 if c.cmp_residual_k is None else int(c.cmp_residual_k[b])
         for r in range(q0, q1):
             u = rng.random()
             n = int(tlen[r]) if tlen is not None else K
             pads = np.nonzero(idx[r] < 0)[0]
-            if invisible and c.mask_mode == 3 and u < 0.3 and len(pads) and s2 > 0:
-                # put the last (most likely invisible) key into the first pad and
-                # extend topk_length over it
+            # first key past the row's causal prefix (the recipe's rule)
+            L = workloads.visible_prefix(r - q0, q1 - q0, s2, c.mask_mode, c.cmp_ratio, res)
+            if invisible and c.mask_mode == 3 and u < 0.3 and len(pads) and L < s2:
+                # put an invisible key into the first pad and extend
+                # topk_length over it
                 t = pads[0]
-                idx[r, t] = s2 - 1
+                idx[r, t] = L
                 if tlen is not None:
                     tlen[r] = max(n, t + 1)
             elif out_of_range and 0.3 <= u < 0.5 and len(pads):

@@ -1,0 +1,279 @@
+"""The C-ABI library on the CPU: exported symbols, metadata fields, and every
+argument check (no GPU needed, no kernel is ever launched).
+
+Every error-path call below starts from a valid call whose metadata has a
+core count of 0, which the library rejects as its last check before a
+launch; so even a missing check could not launch a kernel on the dummy
+pointers used here.
+"""
+
+import ctypes
+import json
+import os
+import re
+import subprocess
+
+import numpy as np
+import pytest
+
+import sparse_mla_attention_02_amd as smla
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "smla.h")
+PAGE = json.load(open(os.path.join(ROOT, "tests", "golden", "page_example.json")))
+
+LIB = smla._lib
+FAKE = ctypes.c_void_p(0x1000)   # never dereferenced: every call fails validation
+
+
+def header_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(smla_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_exports_every_declared_symbol():
+    names = header_functions()
+    assert {"smla_l1norm_metadata", "smla_softmax_l1norm"} <= set(names)
+    lib = ctypes.CDLL(smla.library_path())
+    for n in names:
+        assert hasattr(lib, n), n
+    out = subprocess.run(["nm", "-D", "--defined-only", smla.library_path()],
+                         capture_output=True, text=True, check=True).stdout
+    exported = set(re.findall(r" T (\w+)$", out, flags=re.M))
+    assert set(names) <= exported
+
+
+def test_status_codes_match_page():
+    assert smla.SMLA_ERR_PARAM_NULLPTR == PAGE["error_codes"]["ACLNN_ERR_PARAM_NULLPTR"]
+    assert smla.SMLA_ERR_PARAM_INVALID == PAGE["error_codes"]["ACLNN_ERR_PARAM_INVALID"]
+    assert smla.SMLA_METADATA_SIZE == PAGE["metadata_size"]
+    hdr = open(HEADER).read()
+    for name, val in [("SMLA_ERR_PARAM_NULLPTR", 161001), ("SMLA_ERR_PARAM_INVALID", 161002),
+                      ("SMLA_METADATA_SIZE", 64)]:
+        assert re.search(rf"{name}\s*=?\s*{val}\b", hdr), name
+
+
+def test_output_numel_page_example():
+    ex = PAGE["tnd_example"]
+    T1, N1, D = ex["q_shape"]
+    T2, N2, _ = ex["k_shape"]
+    assert LIB.smla_output_numel(1, 1, T1, N2, T2) == int(np.prod(ex["softmax_l1_norm_shape"]))
+    assert LIB.smla_output_numel(0, 2, 3, 1, 5) == 30
+    assert LIB.smla_output_numel(7, 1, 1, 1, 1) == -1
+    assert LIB.smla_output_numel(0, -1, 1, 1, 1) == -1
+
+
+def test_output_shape_helper_page_example():
+    import torch
+    ex = PAGE["tnd_example"]
+    q = torch.empty(ex["q_shape"], device="meta")
+    k = torch.empty(ex["k_shape"], device="meta")
+    assert smla.output_shape(q, k, "TND") == tuple(ex["softmax_l1_norm_shape"])
+    qb = torch.empty(2, 7, 16, 512, device="meta")
+    kb = torch.empty(2, 9, 1, 512, device="meta")
+    assert smla.output_shape(qb, kb, "BSND") == (2, 7, 1, 9)
+
+
+def test_python_defaults_match_page():
+    import inspect
+    sig = inspect.signature(smla.sparse_flash_mla_softmax_l1_norm)
+    for name, val in PAGE["attribute_defaults"].items():
+        assert sig.parameters[name].default == val, name
+
+
+# ---------------------------------------------------------------- metadata
+
+def meta(**kw):
+    args = dict(num_heads_q=128, num_heads_k=1, head_dim=512, batch_size=1,
+                max_seqlen_q=4096, max_seqlen_k=4096, topk=2048, mask_mode=3,
+                core_budget=36)
+    args.update(kw)
+    return smla.smla_l1norm_metadata(**args)
+
+
+@pytest.mark.parametrize("total,budget", [(4096, 36), (35, 36), (36, 36), (37, 36),
+                                          (100, 7), (1, 512), (8192, 512), (11536, 512)])
+def test_metadata_fields_follow_page_formulas(total, budget):
+    m = meta(batch_size=1, max_seqlen_q=total, core_budget=budget).numpy()
+    cores = min(total, budget)
+    assert m[0] == total
+    assert m[4] == cores
+    assert m[1] == -(-total // cores)          # ceil
+    assert m[2] == total // cores              # floor
+    # tail workgroups run floor(total/cores) rows, the rest ceil
+    assert m[1] * (m[4] - m[3]) + m[2] * m[3] == m[0]
+    assert 0 <= m[3] < max(m[4], 1)
+    assert m[5] == 0x534D4C41 and m[8] == 128 and m[9] == 1 and m[10] == 512
+    assert (m[24:] == 0).all()
+
+
+def test_metadata_page_example_tnd():
+    import torch
+    ex = PAGE["tnd_example"]
+    cq = torch.tensor([0, ex["q_shape"][0]], dtype=torch.int32)
+    ck = torch.tensor([0, ex["k_shape"][0]], dtype=torch.int32)
+    m = smla.smla_l1norm_metadata(
+        ex["q_shape"][1], ex["k_shape"][1], ex["q_shape"][2], cu_seqlens_q=cq,
+        cu_seqlens_k=ck, cmp_residual_k=torch.zeros(1, dtype=torch.int32),
+        max_seqlen_q=16, max_seqlen_k=ex["max_seqlen_k"], topk=2048,
+        cmp_ratio=ex["cmp_ratio"], mask_mode=ex["mask_mode"], layout_q="TND",
+        layout_k="TND", core_budget=PAGE["page_max_core_num"]).numpy()
+    assert tuple(m.shape) == tuple(ex["metadata_shape"])
+    assert m[0] == 16 and m[4] == 16 and m[1] == 1 and m[2] == 1 and m[3] == 0
+    assert m[7] == 1 and m[11] == 1 and m[17] == 16 and m[18] == 2048
+
+
+def test_metadata_tnd_derives_lengths():
+    import torch
+    cq = torch.tensor([0, 1024, 4024, 4536, 11536], dtype=torch.int32)
+    m = smla.smla_l1norm_metadata(64, 1, 512, cu_seqlens_q=cq, cu_seqlens_k=cq, topk=2048,
+                                  mask_mode=3, layout_q="TND", layout_k="TND",
+                                  core_budget=512).numpy()
+    assert m[0] == 11536 and m[11] == 4 and m[12] == 7000 and m[13] == 7000
+    assert m[17] == 11536 and m[18] == 11536 and m[20] == 2
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(num_heads_k=2), 161002), (dict(num_heads_q=0), 161002),
+    (dict(num_heads_q=129), 161002), (dict(head_dim=256), 161002),
+    (dict(mask_mode=1), 161002), (dict(cmp_ratio=0), 161002), (dict(cmp_ratio=129), 161002),
+    (dict(layout_q="TND"), 161002), (dict(layout_q="XYZ", layout_k="XYZ"), 161002),
+    (dict(topk=0), 161101), (dict(topk=-3), 161002), (dict(max_seqlen_q=0), 161002),
+    (dict(batch_size=0), 161002), (dict(core_budget=-1), 161002),
+])
+def test_metadata_errors(kw, code):
+    with pytest.raises(smla.SmlaError) as e:
+        meta(**kw)
+    assert e.value.status == code
+
+
+def test_metadata_error_paths_raw():
+    import torch
+    m = np.zeros(64, dtype=np.int32)
+    f = LIB.smla_l1norm_metadata
+    # metadata pointer NULL
+    assert f(128, 1, 512, None, None, None, None, None, None, 1, 8, 8, 4, 0, 0, 0, 1, 0, 36,
+             None) == 161001
+    # seqused given
+    one = np.zeros(1, dtype=np.int32)
+    assert f(128, 1, 512, None, None, one.ctypes.data, None, None, None, 1, 8, 8, 4, 0, 0, 0,
+             1, 0, 36, m.ctypes.data) == 161101
+    # TND without cu_seqlens
+    assert f(128, 1, 512, None, None, None, None, None, None, 1, 0, 0, 4, 1, 1, 0, 1, 0, 36,
+             m.ctypes.data) == 161001
+    # cu_seqlens not starting at 0 / decreasing
+    bad0 = np.array([1, 5], dtype=np.int32)
+    good = np.array([0, 5], dtype=np.int32)
+    assert f(128, 1, 512, bad0.ctypes.data, good.ctypes.data, None, None, None, None, 1, 0, 0,
+             4, 1, 1, 0, 1, 0, 36, m.ctypes.data) == 161002
+    dec = np.array([0, 5, 3], dtype=np.int32)
+    assert f(128, 1, 512, dec.ctypes.data, dec.ctypes.data, None, None, None, None, 2, 0, 0,
+             4, 1, 1, 0, 1, 0, 36, m.ctypes.data) == 161002
+    assert b"non-decreasing" in LIB.smla_last_error()
+
+
+def test_metadata_device_query_without_gpu():
+    import torch
+    if torch.cuda.is_available():
+        pytest.skip("a GPU is present")
+    with pytest.raises(smla.SmlaError) as e:
+        meta(core_budget=0)
+    assert e.value.status == 561001
+
+
+# ---------------------------------------------------------------- main call
+
+def base_args(layout=0, G=128, K=2048, mask=3, ratio=1, B=1, S1=64, S2=64):
+    """A call that passes every check except the final core-count check."""
+    md = np.zeros(64, dtype=np.int32)
+    R = B * S1 if layout == 0 else S1
+    rows_k = B * S2 if layout == 0 else S2
+    md[[0, 4, 5, 6, 7, 8, 9, 10, 11, 12, 13, 14, 15, 16, 17, 18, 19]] = [
+        R, 0, 0x534D4C41, 1, layout, G, 1, 512, B, S1, S2, K, mask, ratio, R, rows_k, 1]
+    a = dict(q=FAKE, k=FAKE, lse=FAKE, idx=FAKE, cu_q=None, cu_k=None, sq=None, sk=None,
+             res=None, tlen=FAKE, meta=md, dtype=1, B=B, S1=S1, S2=S2, N1=G, N2=1, D=512,
+             K=K, scale=0.044, maxk=0, ratio=ratio, mask=mask, lq=layout, lk=layout,
+             out=FAKE, stream=None)
+    if layout == 1:
+        a["cu_q"] = FAKE
+        a["cu_k"] = FAKE
+    return a
+
+
+def call(a):
+    md = a["meta"]
+    mp = md.ctypes.data if md is not None else None
+    return LIB.smla_softmax_l1norm(
+        a["q"], a["k"], a["lse"], a["idx"], a["cu_q"], a["cu_k"], a["sq"], a["sk"], a["res"],
+        a["tlen"], mp, a["dtype"], a["B"], a["S1"], a["S2"], a["N1"], a["N2"], a["D"], a["K"],
+        a["scale"], a["maxk"], a["ratio"], a["mask"], a["lq"], a["lk"], a["out"], a["stream"])
+
+
+def test_base_call_stops_at_core_count():
+    for layout in (0, 1):
+        assert call(base_args(layout)) == 161002
+        assert b"core count" in LIB.smla_last_error()
+
+
+def _with(**kw):
+    a = base_args(**{k: v for k, v in kw.items() if k in ("layout", "mask", "ratio", "G")})
+    for k, v in kw.items():
+        if k not in ("layout", "mask", "ratio", "G"):
+            a[k] = v
+    return a
+
+
+@pytest.mark.parametrize("kw,code,msg", [
+    (dict(q=None), 161002, b"required"), (dict(k=None), 161002, b"required"),
+    (dict(lse=None), 161002, b"required"), (dict(out=None), 161002, b"required"),
+    (dict(dtype=2), 161002, b"dtype"), (dict(lk=1), 161002, b"equal"),
+    (dict(lq=4, lk=4), 161002, b"layout"), (dict(N2=2), 161002, b"N2"),
+    (dict(N1=0), 161002, b"N1"), (dict(N1=129), 161002, b"N1"), (dict(D=256), 161002, b"512"),
+    (dict(mask=1), 161002, b"mask_mode"), (dict(ratio=0), 161002, b"cmp_ratio"),
+    (dict(ratio=129), 161002, b"cmp_ratio"), (dict(maxk=-1), 161002, b"max_seqlen_k"),
+    (dict(sq=FAKE), 161101, b"seqused"), (dict(sk=FAKE), 161101, b"seqused"),
+    (dict(idx=None), 161101, b"dense"), (dict(K=0), 161002, b"topk"),
+    (dict(meta=None), 161001, b"metadata"),
+    (dict(layout=1, cu_q=None), 161001, b"cu_seqlens"),
+    (dict(layout=1, cu_k=None), 161001, b"cu_seqlens"),
+    (dict(mask=3, ratio=4, res=None), 161001, b"cmp_residual_k"),
+    (dict(mask=0, tlen=None), 161001, b"topk_length"),
+    (dict(B=-1), 161002, b"sizes"), (dict(layout=1, B=0), 161002, b"batch_size"),
+])
+def test_main_call_errors(kw, code, msg):
+    a = _with(**kw)
+    assert call(a) == code, LIB.smla_last_error()
+    assert msg in LIB.smla_last_error()
+
+
+@pytest.mark.parametrize("field,value", [(5, 0), (6, 9), (7, 1), (8, 64), (9, 2), (10, 128),
+                                         (11, 2), (12, 65), (13, 63), (14, 16), (15, 0),
+                                         (16, 2), (17, 1), (18, 1), (0, 3)])
+def test_metadata_mismatch_is_rejected(field, value):
+    a = base_args()
+    a["meta"][field] = value
+    assert call(a) == 161002
+    err = LIB.smla_last_error()
+    assert b"does not match" in err or b"not made by" in err, err
+
+
+def test_empty_q_returns_without_looking_at_pointers():
+    a = base_args(S1=0)
+    for k in ("q", "k", "lse", "idx", "tlen", "out"):
+        a[k] = None
+    a["meta"] = None
+    assert call(a) == 0
+    a = base_args(layout=1, S1=0)
+    for k in ("q", "k", "lse", "idx", "tlen", "out", "cu_q", "cu_k"):
+        a[k] = None
+    a["meta"] = None
+    assert call(a) == 0
+    # empty output (no keys)
+    a = base_args(S2=0)
+    a["meta"] = None
+    assert call(a) == 0
+    # still checks attributes first
+    a = base_args(S1=0)
+    a["N2"] = 2
+    assert call(a) == 161002
