@@ -57,8 +57,10 @@ def cpu_baseline(p, target_s):
     import oracle
     R = p.rows
     n = p.topk_length.reshape(R).astype(np.int64)
-    # calibrate on a few rows, then size the sample for ~target_s seconds
-    cal = np.linspace(0, R - 1, 8).astype(np.int64)
+    # calibrate on a few rows per thread, then size the sample for ~target_s
+    threads = oracle.num_threads()
+    cal = np.linspace(0, R - 1, min(R, 4 * threads)).astype(np.int64)
+    oracle.l1norm(p, rows=cal[:threads])       # warm the thread pool
     t0 = time.perf_counter()
     oracle.l1norm(p, rows=cal)
     t_cal = time.perf_counter() - t0
@@ -72,7 +74,7 @@ def cpu_baseline(p, target_s):
     t = time.perf_counter() - t0
     pairs = int(n[rows].sum())
     flops = 2.0 * p.heads_q * p.head_dim * pairs
-    return {"value": flops / t / 1e12, "unit": "TFLOP/s", "cores": oracle.num_threads(),
+    return {"value": flops / t / 1e12, "unit": "TFLOP/s", "cores": threads,
             "kind": "oracle",
             "sample": f"{count} evenly spaced rows of {R} ({pairs} valid pairs), "
                       f"oracle_l1norm given lse, {t:.1f} s wall"}

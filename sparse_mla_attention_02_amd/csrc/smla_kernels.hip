@@ -30,10 +30,16 @@ namespace {
 typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8_t;
 typedef __attribute__((ext_vector_type(8))) _Float16 f16x8_t;
 typedef __attribute__((ext_vector_type(16))) float f32x16_t;
+typedef __attribute__((ext_vector_type(4))) float f32x4_t;
+typedef __attribute__((ext_vector_type(4))) unsigned int u32x4_t;
 
 constexpr int kD = 512;             // head dim (only value supported)
 constexpr int kChunks = kD * 2 / 16;  // 16-byte chunks per row of K / head of Q
 constexpr int kTile = 32;           // keys per tile (MFMA N)
+// LDS pitch of one K row in 16-byte chunks: one spare chunk per row so that
+// the 16 lanes of an LDS read phase (16 different rows, same chunk) hit 16
+// different bank groups (row * 65 mod 16 = row mod 16)
+constexpr int kPitch = kChunks + 1;
 constexpr float kLog2e = 1.4426950408889634f;
 
 template <bool BF16>
@@ -117,16 +123,68 @@ __device__ __forceinline__ int64_t row_of(const KernelArgs& a, int64_t it, int w
     return base + ((a.snake && (it & 1)) ? (a.num_wg - 1 - w) : w);
 }
 
+#define SMLA_LDS(p) ((__attribute__((address_space(3))) void*)(p))
+
+// Buffer resource over the k rows of one batch / sequence (raw byte
+// addressing; word 3 is the gfx9-family value for untyped buffer access).
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t k_rsrc(const uint4* k4, int64_t kbase) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<uint4*>(k4 + kbase * kChunks),
+                                             (short)0, 0x7fffffff, 0x00020000);
+}
+
+// Gather one 32-key tile of K into LDS with direct buffer->LDS loads: slot kk
+// (key kk of the tile) is moved by wave kk % HT with one instruction (64
+// lanes x 16 B = the whole 1 KB row, lane l -> chunk l; the row offset is a
+// scalar).
+template <int HT>
+__device__ __forceinline__ void gather_tile(uint4* __restrict__ dst, __amdgpu_buffer_rsrc_t rs,
+                                            int32_t idx_reg, int wave, int lane) {
+#pragma unroll
+    for (int i = 0; i < kTile / HT; ++i) {
+        const int kk = wave + i * HT;
+        const int32_t j = __builtin_amdgcn_readlane(idx_reg, kk);
+        if (j >= 0)
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, SMLA_LDS(dst + kk * kPitch), 16,
+                                                     lane << 4, j << 10, 0, 0);
+    }
+}
+
+// S^T tile (this wave's 32 heads x 32 keys) = Q_tile . K_tile^T over D = 512.
+template <bool BF16>
+__device__ __forceinline__ f32x16_t qk_tile(const uint4* __restrict__ src, const uint4* qa,
+                                            int col, int half) {
+    f32x16_t acc = {};
+    const uint4* row = src + col * kPitch + half;
+#pragma unroll
+    for (int s = 0; s < kChunks / 2; ++s) {
+        const uint4 b = row[2 * s];
+        acc = mfma_32x32x16<BF16>(qa[s], b, acc);
+    }
+    // keep only kLead operand reads in flight ahead of the MFMAs (bounds the
+    // VGPRs the B operands take): kLead reads, then MFMA/read pairs
+    constexpr int kLead = 4;
+    __builtin_amdgcn_sched_group_barrier(0x100, kLead, 0);
+#pragma unroll
+    for (int s = 0; s < kChunks / 2 - kLead; ++s) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+    }
+    __builtin_amdgcn_sched_group_barrier(0x008, kLead, 0);
+    return acc;
+}
+
 template <int HT, bool BF16, bool TND>
-__global__ __launch_bounds__(64 * HT) void smla_l1norm_kernel(KernelArgs a) {
+__global__ __launch_bounds__(64 * HT, 2) void smla_l1norm_kernel(KernelArgs a) {
     constexpr int NT = 64 * HT;
-    __shared__ uint4 ktile[kTile * kChunks];  // 32 keys x 1 KB, chunk-swizzled
-    __shared__ int32_t tkey[kTile];           // key of each tile slot, -1 if unused
-    __shared__ float red[HT][kTile];          // per-head-tile partial sums
+    // two K tiles (distinct objects, so loads into one never wait on reads of
+    // the other) and the per-head-tile partial sums of the last two tiles
+    __shared__ uint4 kbuf0[kTile * kPitch];
+    __shared__ uint4 kbuf1[kTile * kPitch];
+    __shared__ float red[2][HT][kTile];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
-    const int wave = tid >> 6;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: lives in an SGPR
     const int half = lane >> 5;   // which 8-element k-group of the MFMA operand
     const int col = lane & 31;    // key slot of the MFMA B operand / output column
     const uint4* __restrict__ k4 = static_cast<const uint4*>(a.k);
@@ -137,18 +195,37 @@ __global__ __launch_bounds__(64 * HT) void smla_l1norm_kernel(KernelArgs a) {
         if (r >= a.R) continue;
         const RowInfo ri = decode_row<TND>(a, r);
         float* __restrict__ orow = a.out + r * a.W;
+        const int32_t* __restrict__ irow = a.idx + r * a.K;
+        const int ntiles = (ri.n + kTile - 1) / kTile;
+
+        // key of slot `col` of a tile if that entry is used, else -1
+        auto tile_key = [&](int tile) -> int32_t {
+            const int t = tile * kTile + col;
+            const int32_t j = (tile < ntiles && t < ri.n) ? irow[t] : -1;
+            return (uint32_t)j < (uint32_t)ri.vis ? j : -1;
+        };
+        int32_t key_cur = tile_key(0);
+        int32_t key_nxt = tile_key(1);
 
         // zero-fill the whole output row
-        for (int64_t c = tid; c < a.W; c += NT) orow[c] = 0.0f;
+        if ((a.W & 3) == 0) {
+            f32x4_t* o4 = reinterpret_cast<f32x4_t*>(orow);
+            const f32x4_t z = {0.f, 0.f, 0.f, 0.f};
+            for (int64_t c = tid; c < (a.W >> 2); c += NT) __builtin_nontemporal_store(z, o4 + c);
+        } else {
+            for (int64_t c = tid; c < a.W; c += NT) orow[c] = 0.0f;
+        }
 
         // this wave's 32 heads of Q as MFMA A operands: lane (m, half) holds
         // head m, elements 16*s + 8*half .. +8 for k-step s
         const int head = wave * 32 + col;
         uint4 qa[kChunks / 2];
         if (head < a.G) {
-            const uint4* qp = q4 + (r * a.G + head) * kChunks;
+            const u32x4_t* qp =
+                reinterpret_cast<const u32x4_t*>(q4 + (r * a.G + head) * kChunks);
 #pragma unroll
-            for (int s = 0; s < kChunks / 2; ++s) qa[s] = qp[2 * s + half];
+            for (int s = 0; s < kChunks / 2; ++s)
+                qa[s] = __builtin_bit_cast(uint4, __builtin_nontemporal_load(qp + 2 * s + half));
         } else {
 #pragma unroll
             for (int s = 0; s < kChunks / 2; ++s) qa[s] = make_uint4(0, 0, 0, 0);
@@ -163,60 +240,60 @@ __global__ __launch_bounds__(64 * HT) void smla_l1norm_kernel(KernelArgs a) {
             l2[e] = h < a.G ? a.lse[r * a.G + h] * kLog2e : __builtin_inff();
         }
 
-        // zero stores of every wave complete before any selected column is
-        // written (same addresses, different waves)
-        __builtin_amdgcn_s_waitcnt(0);
-        __syncthreads();
+        const __amdgpu_buffer_rsrc_t krs = k_rsrc(k4, ri.kbase);
+        if (ntiles > 0) gather_tile<HT>(kbuf0, krs, key_cur, wave, lane);
 
-        const int32_t* __restrict__ irow = a.idx + r * a.K;
-        for (int t0 = 0; t0 < ri.n; t0 += kTile) {
-            // gather: wave-instruction i moves key slot kk = wave + i*HT
-#pragma unroll 4
-            for (int kk = wave; kk < kTile; kk += HT) {
-                const int t = t0 + kk;
-                const int32_t j = t < ri.n ? irow[t] : -1;
-                if ((uint32_t)j < (uint32_t)ri.vis) {
-                    const uint4 v = k4[(ri.kbase + j) * kChunks + lane];
-                    ktile[kk * kChunks + (lane ^ (kk & 15))] = v;
+        int32_t key_prev = -1;
+        // one tile: finish the previous tile's head sum, start the next
+        // tile's gather, then QK^T + exp + head sum of this tile
+        auto body = [&](int tile, const uint4* cur, uint4* nxt) {
+            // all gathers landed, zero-fill stores and partial sums done
+            __builtin_amdgcn_s_waitcnt(0);
+            __syncthreads();
+            if constexpr (HT > 1) {
+                if (tile > 0 && wave == 0 && lane < kTile) {
+                    const int pb = (tile - 1) & 1;
+                    float tot = red[pb][0][lane];
+#pragma unroll
+                    for (int w = 1; w < HT; ++w) tot += red[pb][w][lane];
+                    if (key_prev >= 0) orow[ri.col0 + key_prev] = tot * a.inv_g;
                 }
             }
-            if (tid < kTile) {
-                const int t = t0 + tid;
-                const int32_t j = t < ri.n ? irow[t] : -1;
-                tkey[tid] = (uint32_t)j < (uint32_t)ri.vis ? j : -1;
-            }
-            __syncthreads();
+            if (tile + 1 < ntiles) gather_tile<HT>(nxt, krs, key_nxt, wave, lane);
+            const int32_t key_nn = tile_key(tile + 2);
 
-            // S^T tile (32 heads x 32 keys) = Q_tile . K_tile^T over D = 512
-            f32x16_t acc = {};
-#pragma unroll
-            for (int s = 0; s < kChunks / 2; ++s) {
-                const uint4 b = ktile[col * kChunks + ((2 * s + half) ^ (col & 15))];
-                acc = mfma_32x32x16<BF16>(qa[s], b, acc);
-            }
-
+            const f32x16_t acc = qk_tile<BF16>(cur, qa, col, half);
             // exp(s - lse) = 2^(acc*scale*log2e - lse*log2e), summed over heads
             float sum = 0.0f;
 #pragma unroll
             for (int e = 0; e < 16; ++e)
                 sum += __builtin_amdgcn_exp2f(__builtin_fmaf(acc[e], a.c_scale, -l2[e]));
             sum += __shfl_xor(sum, 32);
-
-            float tot = sum;
             if constexpr (HT > 1) {
-                if (lane < kTile) red[wave][lane] = sum;
-                __syncthreads();
-                if (tid < kTile) {
-                    tot = red[0][tid];
+                if (lane < kTile) red[tile & 1][wave][lane] = sum;
+            } else {
+                if (lane < kTile && key_cur >= 0) orow[ri.col0 + key_cur] = sum * a.inv_g;
+            }
+            key_prev = key_cur;
+            key_cur = key_nxt;
+            key_nxt = key_nn;
+        };
+        for (int tile = 0; tile < ntiles; tile += 2) {
+            body(tile, kbuf0, kbuf1);
+            if (tile + 1 < ntiles) body(tile + 1, kbuf1, kbuf0);
+        }
+        // head sum of the last tile; also keeps the next row's first gather
+        // from overwriting a tile some wave still reads
+        __builtin_amdgcn_s_waitcnt(0);
+        __syncthreads();
+        if constexpr (HT > 1) {
+            if (ntiles > 0 && wave == 0 && lane < kTile) {
+                const int pb = (ntiles - 1) & 1;
+                float tot = red[pb][0][lane];
 #pragma unroll
-                    for (int w = 1; w < HT; ++w) tot += red[w][tid];
-                }
+                for (int w = 1; w < HT; ++w) tot += red[pb][w][lane];
+                if (key_prev >= 0) orow[ri.col0 + key_prev] = tot * a.inv_g;
             }
-            if (tid < kTile) {
-                const int32_t j = tkey[tid];
-                if (j >= 0) orow[ri.col0 + j] = tot * a.inv_g;
-            }
-            __syncthreads();
         }
     }
 }
