@@ -38,15 +38,16 @@ smla_status_t ok() {
     return SMLA_SUCCESS;
 }
 
-// Per (device, head tiles, layout): CU count and co-resident workgroups per
-// CU, queried once.
+// Per (device, head tiles, layout, pipelined kernel): CU count and
+// co-resident workgroups per CU, queried once.
 std::mutex g_cap_mu;
-std::map<std::tuple<int, int, bool>, std::pair<int, int>> g_cap;
+std::map<std::tuple<int, int, bool, bool>, std::pair<int, int>> g_cap;
 
-hipError_t device_capacity(int device, int ht, bool tnd, int* cus, int* per_cu) {
+hipError_t device_capacity(int device, int ht, bool tnd, int64_t topk, int* cus, int* per_cu) {
+    const bool pipe = smla::uses_pipe(ht, topk);
     {
         std::lock_guard<std::mutex> lk(g_cap_mu);
-        auto it = g_cap.find({device, ht, tnd});
+        auto it = g_cap.find({device, ht, tnd, pipe});
         if (it != g_cap.end()) {
             *cus = it->second.first;
             *per_cu = it->second.second;
@@ -61,12 +62,12 @@ hipError_t device_capacity(int device, int ht, bool tnd, int* cus, int* per_cu) 
     if (e != hipSuccess) return e;
     if (cur != device && (e = hipSetDevice(device)) != hipSuccess) return e;
     int occ = 0;
-    e = smla::resident_per_cu(ht, true, tnd, &occ);
+    e = smla::resident_per_cu(ht, true, tnd, topk, &occ);
     if (cur != device) (void)hipSetDevice(cur);
     if (e != hipSuccess) return e;
     if (occ <= 0) return hipErrorInvalidConfiguration;
     std::lock_guard<std::mutex> lk(g_cap_mu);
-    g_cap[{device, ht, tnd}] = {n, occ};
+    g_cap[{device, ht, tnd, pipe}] = {n, occ};
     *cus = n;
     *per_cu = occ;
     return hipSuccess;
@@ -187,7 +188,8 @@ smla_status_t smla_l1norm_metadata(
     int cus = 0, per_cu = 0;
     int64_t budget = core_budget;
     if (core_budget == 0) {
-        hipError_t e = device_capacity(device, ht, layout_q == SMLA_LAYOUT_TND, &cus, &per_cu);
+        hipError_t e =
+            device_capacity(device, ht, layout_q == SMLA_LAYOUT_TND, topk, &cus, &per_cu);
         if (e != hipSuccess)
             return fail(SMLA_ERR_RUNTIME, "device %d capacity query failed: %s", device,
                         hipGetErrorString(e));

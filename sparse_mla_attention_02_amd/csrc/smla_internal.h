@@ -39,7 +39,11 @@ inline int head_tiles_for(int64_t G) { return G <= 32 ? 1 : (G <= 64 ? 2 : 4); }
 hipError_t launch(const KernelArgs& a, int head_tiles, bool bf16, bool tnd,
                   hipStream_t stream);
 
-// Co-resident workgroups per CU of that variant.
-hipError_t resident_per_cu(int head_tiles, bool bf16, bool tnd, int* out);
+// Whether rows of (head_tiles, topk) run on the pipelined one-workgroup-per-CU
+// kernel (otherwise on the general kernel).
+bool uses_pipe(int head_tiles, int64_t topk);
+
+// Co-resident workgroups per CU of the variant used for (head_tiles, topk).
+hipError_t resident_per_cu(int head_tiles, bool bf16, bool tnd, int64_t topk, int* out);
 
 }  // namespace smla

@@ -11,18 +11,24 @@
 //    persistent grid walks rows in the order the metadata fixes;
 //  - each wave keeps its 32 heads x 512 of Q in VGPRs as MFMA A operands
 //    (32 x 16 B per lane) for the whole row;
-//  - keys are processed in tiles of 32: the workgroup gathers the 32
-//    selected 1 KB rows of K into an XOR-swizzled LDS tile (one wave
-//    instruction moves one whole row, fully coalesced), then every wave runs
-//    32 v_mfma_f32_32x32x16 over D = 512 with its Q tile against the shared
-//    K tile;
-//  - the accumulator holds 16 heads x 1 key per lane; scale, the lse
-//    subtraction and exp are fused as one FMA + v_exp_f32 (base 2), the 16
-//    heads are summed in registers, the two half-waves by a cross-lane swap
-//    and the head tiles through LDS;
-//  - the output row is zero-filled first and the selected columns are then
-//    written by single stores (indices of a row are distinct).
+//  - keys are processed in tiles of 32. Tile t+1 is gathered into one of two
+//    LDS tiles with direct buffer->LDS loads (one instruction moves one whole
+//    1 KB row) while the waves run the 32 v_mfma_f32_32x32x16 of tile t
+//    (D = 512) against the other; indices are prefetched two tiles ahead;
+//  - the accumulator holds 16 heads x 1 key per lane. The epilogue of tile
+//    t-1 (scale and lse folded into one FMA, v_exp_f32 in base 2, sum over
+//    the lane's 16 heads) is interleaved with the MFMAs of tile t; half-wave
+//    and head-tile partial sums meet in LDS after the next barrier and are
+//    added in a fixed order (deterministic, no atomics);
+//  - the values of a row collect in LDS; at the end of the row the row is
+//    assembled in LDS (zeros + values at their columns) and written once
+//    with coalesced stores. Columns no index can reach are zero-filled with
+//    streaming stores up front. Rows with more than kVcap indices fall back
+//    to zero-fill then single stores (indices of a row are distinct).
 #include "smla_internal.h"
+
+#include <type_traits>
+
 
 namespace smla {
 namespace {
@@ -41,6 +47,8 @@ constexpr int kTile = 32;           // keys per tile (MFMA N)
 // different bank groups (row * 65 mod 16 = row mod 16)
 constexpr int kPitch = kChunks + 1;
 constexpr float kLog2e = 1.4426950408889634f;
+constexpr int kVcap = 2048;         // values of one row kept in LDS for assembly
+constexpr int kStage = kTile * kPitch * 4 - 4;  // floats of one K tile usable as row stage
 
 template <bool BF16>
 __device__ __forceinline__ f32x16_t mfma_32x32x16(uint4 a, uint4 b, f32x16_t c) {
@@ -62,6 +70,30 @@ struct RowInfo {
     int32_t n;      // entries of the index row to look at
 };
 
+// Streaming zero stores of row[c0, c1): scalar head/tail, 16-byte body.
+__device__ __forceinline__ void zero_span(float* __restrict__ row, int64_t c0, int64_t c1,
+                                          int tid, int nt) {
+    if (c1 <= c0) return;
+    const int64_t head = ((16 - (reinterpret_cast<uintptr_t>(row + c0) & 15)) & 15) >> 2;
+    const int64_t h = head < c1 - c0 ? head : c1 - c0;
+    if (tid < h) row[c0 + tid] = 0.0f;
+    const int64_t b0 = c0 + h;
+    const int64_t n4 = (c1 - b0) >> 2;
+    f32x4_t* o4 = reinterpret_cast<f32x4_t*>(row + b0);
+    const f32x4_t z = {0.f, 0.f, 0.f, 0.f};
+    for (int64_t i = tid; i < n4; i += nt) __builtin_nontemporal_store(z, o4 + i);
+    const int64_t t0 = b0 + 4 * n4;
+    if (tid < c1 - t0) row[t0 + tid] = 0.0f;
+}
+
+// Read-only int32 data at a wave-uniform address: the constant address
+// space lets the compiler use scalar loads (waited with lgkmcnt, so they do
+// not queue behind the vector loads in flight).
+typedef const __attribute__((address_space(4))) int32_t* cint_ptr;
+__device__ __forceinline__ int32_t uload(const int32_t* p, int64_t i) {
+    return ((cint_ptr)p)[i];
+}
+
 // Row -> (batch, position) decode, mask limit and entry count.
 // Right-down causal with compression ratio r and residual res: the query at
 // position i of a sequence with s1 queries and s2 compressed keys is at
@@ -75,15 +107,15 @@ __device__ __forceinline__ RowInfo decode_row(const KernelArgs& a, int64_t r) {
         // largest b in [0, B) with cu_q[b] <= r
         int lo = 0, hi = a.B - 1;
         while (lo < hi) {
-            int mid = (lo + hi + 1) >> 1;
-            if (a.cu_q[mid] <= r) lo = mid; else hi = mid - 1;
+            const int mid = (lo + hi + 1) >> 1;
+            if (uload(a.cu_q, mid) <= r) lo = mid; else hi = mid - 1;
         }
         b = lo;
-        const int64_t q0 = a.cu_q[b];
-        s1 = (int64_t)a.cu_q[b + 1] - q0;
+        const int64_t q0 = uload(a.cu_q, b);
+        s1 = (int64_t)uload(a.cu_q, b + 1) - q0;
         i = r - q0;
-        kbase = a.cu_k[b];
-        s2 = (int64_t)a.cu_k[b + 1] - kbase;
+        kbase = uload(a.cu_k, b);
+        s2 = (int64_t)uload(a.cu_k, b + 1) - kbase;
         // never reach past the k tensor or the output row
         if (kbase < 0) kbase = 0;
         if (s2 > a.rows_k - kbase) s2 = a.rows_k - kbase;
@@ -100,16 +132,17 @@ __device__ __forceinline__ RowInfo decode_row(const KernelArgs& a, int64_t r) {
     }
     int64_t vis = s2;
     if (a.mask_mode == 3) {
-        const int64_t res = a.cmp_res ? (int64_t)a.cmp_res[b] : 0;
+        const int64_t res = a.cmp_res ? (int64_t)uload(a.cmp_res, b) : 0;
         const int64_t p1 = i + 1 + s2 * a.cmp_ratio + res - s1;
         vis = p1 > 0 ? p1 / a.cmp_ratio : 0;
         if (vis > s2) vis = s2;
     }
     int32_t n = a.K;
     if (a.topk_len) {
-        n = a.topk_len[r];
+        n = uload(a.topk_len, r);
         n = n < 0 ? 0 : (n > a.K ? a.K : n);
     }
+    if (vis == 0) n = 0;  // nothing visible: no entry can be used
     RowInfo ri;
     ri.kbase = kbase;
     ri.col0 = col0;
@@ -125,62 +158,89 @@ __device__ __forceinline__ int64_t row_of(const KernelArgs& a, int64_t it, int w
 
 #define SMLA_LDS(p) ((__attribute__((address_space(3))) void*)(p))
 
-// Buffer resource over the k rows of one batch / sequence (raw byte
-// addressing; word 3 is the gfx9-family value for untyped buffer access).
+// Buffer resource over `bytes` bytes at `base` (raw byte addressing; word 3
+// is the gfx9-family value for untyped buffer access). Lane offsets at or
+// past `bytes` read as zero.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const void* base, uint32_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes,
+                                             0x00020000);
+}
+
+// Buffer resource over the k rows of one batch / sequence; rows are selected
+// with the scalar offset.
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t k_rsrc(const uint4* k4, int64_t kbase) {
-    return __builtin_amdgcn_make_buffer_rsrc(const_cast<uint4*>(k4 + kbase * kChunks),
-                                             (short)0, 0x7fffffff, 0x00020000);
+    return rsrc(k4 + kbase * kChunks, 0x7fffffffu);
 }
 
-// Gather one 32-key tile of K into LDS with direct buffer->LDS loads: slot kk
-// (key kk of the tile) is moved by wave kk % HT with one instruction (64
-// lanes x 16 B = the whole 1 KB row, lane l -> chunk l; the row offset is a
-// scalar).
-template <int HT>
-__device__ __forceinline__ void gather_tile(uint4* __restrict__ dst, __amdgpu_buffer_rsrc_t rs,
-                                            int32_t idx_reg, int wave, int lane) {
+// One 32-key tile of K is gathered into LDS with direct buffer->LDS loads:
+// slot kk (key kk of the tile) is moved by wave kk % HT with one instruction
+// (64 lanes x 16 B = the whole 1 KB row, lane l -> chunk l; the row offset
+// is a scalar).
+
+// exp(s - lse) = 2^(acc*scale*log2e - lse*log2e), summed over the lane's 16
+// heads (padded heads have lse2 = +inf and give 0)
+__device__ __forceinline__ float head_sum(const f32x16_t& acc, const float* l2, float c) {
+    float sum = 0.0f;
 #pragma unroll
-    for (int i = 0; i < kTile / HT; ++i) {
-        const int kk = wave + i * HT;
-        const int32_t j = __builtin_amdgcn_readlane(idx_reg, kk);
-        if (j >= 0)
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, SMLA_LDS(dst + kk * kPitch), 16,
-                                                     lane << 4, j << 10, 0, 0);
-    }
+    for (int e = 0; e < 16; ++e) sum += __builtin_amdgcn_exp2f(__builtin_fmaf(acc[e], c, -l2[e]));
+    return sum;
 }
 
-// S^T tile (this wave's 32 heads x 32 keys) = Q_tile . K_tile^T over D = 512.
-template <bool BF16>
+// S^T tile (this wave's 32 heads x 32 keys) = Q_tile . K_tile^T over D = 512,
+// with the previous tile's head_sum and (GATHER) the gather of the next tile
+// scheduled between the MFMAs: this wave's kTile/HT key rows are issued one
+// per kGap MFMAs, so the loads stream through the texture unit while the
+// matrix core runs instead of arriving in one burst after the barrier.
+template <bool BF16, bool GATHER, int HT, int LEAD = 4>
 __device__ __forceinline__ f32x16_t qk_tile(const uint4* __restrict__ src, const uint4* qa,
-                                            int col, int half) {
+                                            int col, int half, const f32x16_t& prev,
+                                            const float* l2, float c, float* prev_sum,
+                                            uint4* __restrict__ gdst,
+                                            __amdgpu_buffer_rsrc_t krs, int32_t rows,
+                                            int wave, int lane) {
+    constexpr int kSlots = kTile / HT;                 // rows this wave gathers
+    constexpr int kGap = kSlots >= 16 ? 1 : 16 / kSlots;  // MFMAs between gathers
     f32x16_t acc = {};
     const uint4* row = src + col * kPitch + half;
 #pragma unroll
     for (int s = 0; s < kChunks / 2; ++s) {
         const uint4 b = row[2 * s];
         acc = mfma_32x32x16<BF16>(qa[s], b, acc);
+        if constexpr (GATHER) {
+            if (s % kGap == 0 && s / kGap < kSlots) {
+                const int kk = wave + (s / kGap) * HT;
+                const int32_t j = __builtin_amdgcn_readlane(rows, kk);
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(krs, SMLA_LDS(gdst + kk * kPitch), 16,
+                                                         lane << 4, j << 10, 0, 0);
+            }
+        }
     }
-    // keep only kLead operand reads in flight ahead of the MFMAs (bounds the
-    // VGPRs the B operands take): kLead reads, then MFMA/read pairs
-    constexpr int kLead = 4;
+    *prev_sum = head_sum(prev, l2, c);
+    // kLead operand reads ahead of the MFMAs; between MFMAs one read, two
+    // VALU instructions of the previous tile's epilogue, and the gathers
+    constexpr int kLead = LEAD;
     __builtin_amdgcn_sched_group_barrier(0x100, kLead, 0);
 #pragma unroll
-    for (int s = 0; s < kChunks / 2 - kLead; ++s) {
+    for (int s = 0; s < kChunks / 2; ++s) {
         __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+        if (s < kChunks / 2 - kLead) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x002, 2, 0);
+        if (GATHER && s % kGap == 0 && s / kGap < kSlots)
+            __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
     }
-    __builtin_amdgcn_sched_group_barrier(0x008, kLead, 0);
     return acc;
 }
 
-template <int HT, bool BF16, bool TND>
+template <int HT, bool BF16, bool TND, bool STAGED>
 __global__ __launch_bounds__(64 * HT, 2) void smla_l1norm_kernel(KernelArgs a) {
     constexpr int NT = 64 * HT;
+    constexpr int kPerThread = kVcap / NT;  // index re-reads per thread in the row assembly
     // two K tiles (distinct objects, so loads into one never wait on reads of
-    // the other) and the per-head-tile partial sums of the last two tiles
+    // the other); kbuf0 doubles as the row stage at the end of a row
     __shared__ uint4 kbuf0[kTile * kPitch];
     __shared__ uint4 kbuf1[kTile * kPitch];
-    __shared__ float red[2][HT][kTile];
+    __shared__ float red[2][2 * HT][kTile];   // half-wave partial sums, last two tiles
+    __shared__ float vals[kVcap + 64];        // the row's values by entry; then a sink
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -189,92 +249,136 @@ __global__ __launch_bounds__(64 * HT, 2) void smla_l1norm_kernel(KernelArgs a) {
     const int col = lane & 31;    // key slot of the MFMA B operand / output column
     const uint4* __restrict__ k4 = static_cast<const uint4*>(a.k);
     const uint4* __restrict__ q4 = static_cast<const uint4*>(a.q);
+    constexpr bool staged = STAGED;  // rows assembled in LDS (needs K <= kVcap)
+    float* const stage = reinterpret_cast<float*>(kbuf0);
 
-    for (int64_t it = 0; it * a.num_wg < a.R; ++it) {
-        const int64_t r = row_of(a, it, blockIdx.x);
+    // this wave's head of lane (m, half) and the heads of its 16 accumulator
+    // elements (element e of the 32x32 accumulator is head 8*(e/4) + 4*half + e%4);
+    // heads past G read zeros (bounds-checked loads) and get an lse of +inf
+    const int head = wave * 32 + col;
+
+    // Raw Q (MFMA A operands: lane (m, half) holds head m, elements 16*s +
+    // 8*half .. +8 for k-step s) and lse of row r; loads are only issued here
+    uint4 qa[kChunks / 2];
+    float lse_raw[16];
+    auto load_row_operands = [&](int64_t r) {
+        const __amdgpu_buffer_rsrc_t rq = rsrc(q4 + r * a.G * kChunks, (uint32_t)a.G * 1024u);
+        const uint32_t qoff = (uint32_t)head * 1024u + (uint32_t)half * 16u;
+#pragma unroll
+        for (int s = 0; s < kChunks / 2; ++s)
+            qa[s] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(
+                                                  rq, qoff + 32u * s, 0, 2 /* nt */));
+        const __amdgpu_buffer_rsrc_t rl = rsrc(a.lse + r * a.G, (uint32_t)a.G * 4u);
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+            const int h = wave * 32 + 8 * (e >> 2) + 4 * half + (e & 3);
+            lse_raw[e] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(
+                                                       rl, (uint32_t)h * 4u, 0, 0));
+        }
+    };
+
+    int64_t it = 0;
+    int64_t r = row_of(a, 0, blockIdx.x);
+    load_row_operands(r < a.R ? r : a.R - 1);
+
+    for (; it * a.num_wg < a.R; ++it) {
+        r = row_of(a, it, blockIdx.x);
         if (r >= a.R) continue;
+        const int64_t r_next = (it + 1) * a.num_wg < a.R ? row_of(a, it + 1, blockIdx.x) : a.R;
         const RowInfo ri = decode_row<TND>(a, r);
         float* __restrict__ orow = a.out + r * a.W;
         const int32_t* __restrict__ irow = a.idx + r * a.K;
         const int ntiles = (ri.n + kTile - 1) / kTile;
+        // columns [seg0, seg1) can hold values; everything else is zero
+        const int64_t seg0 = ri.col0;
+        const int64_t seg1 = ri.col0 + (ntiles > 0 ? ri.vis : 0);
 
-        // key of slot `col` of a tile if that entry is used, else -1
-        auto tile_key = [&](int tile) -> int32_t {
-            const int t = tile * kTile + col;
-            const int32_t j = (tile < ntiles && t < ri.n) ? irow[t] : -1;
-            return (uint32_t)j < (uint32_t)ri.vis ? j : -1;
+        // raw index of slot `col` of a tile (any value; checked where used)
+        const __amdgpu_buffer_rsrc_t ridx = rsrc(irow, (uint32_t)a.K * 4u);
+        auto tile_idx = [&](int tile) -> int32_t {
+            return __builtin_amdgcn_raw_buffer_load_b32(ridx, (uint32_t)(tile * kTile + col) * 4u,
+                                                        0, 0);
         };
-        int32_t key_cur = tile_key(0);
-        int32_t key_nxt = tile_key(1);
+        // is slot kk of a tile, holding raw index j, a used entry?
+        auto used = [&](int tile, int kk, int32_t j) -> bool {
+            return tile * kTile + kk < ri.n && (uint32_t)j < (uint32_t)ri.vis;
+        };
+        // key row to gather for slot `col`: its index if used, else row 0
+        // (fetched but never read)
+        auto gather_row = [&](int tile, int32_t j) -> int32_t {
+            return used(tile, col, j) ? j : 0;
+        };
+        int32_t key_cur = tile_idx(0);
+        int32_t key_nxt = tile_idx(1);
 
-        // zero-fill the whole output row
-        if ((a.W & 3) == 0) {
-            f32x4_t* o4 = reinterpret_cast<f32x4_t*>(orow);
-            const f32x4_t z = {0.f, 0.f, 0.f, 0.f};
-            for (int64_t c = tid; c < (a.W >> 2); c += NT) __builtin_nontemporal_store(z, o4 + c);
+        if (staged) {
+            zero_span(orow, 0, seg0, tid, NT);
+            zero_span(orow, seg1, a.W, tid, NT);
         } else {
-            for (int64_t c = tid; c < a.W; c += NT) orow[c] = 0.0f;
+            zero_span(orow, 0, a.W, tid, NT);
         }
 
-        // this wave's 32 heads of Q as MFMA A operands: lane (m, half) holds
-        // head m, elements 16*s + 8*half .. +8 for k-step s
-        const int head = wave * 32 + col;
-        uint4 qa[kChunks / 2];
-        if (head < a.G) {
-            const u32x4_t* qp =
-                reinterpret_cast<const u32x4_t*>(q4 + (r * a.G + head) * kChunks);
-#pragma unroll
-            for (int s = 0; s < kChunks / 2; ++s)
-                qa[s] = __builtin_bit_cast(uint4, __builtin_nontemporal_load(qp + 2 * s + half));
-        } else {
-#pragma unroll
-            for (int s = 0; s < kChunks / 2; ++s) qa[s] = make_uint4(0, 0, 0, 0);
-        }
-
-        // lse (base 2) of the 16 heads this lane's accumulator holds:
-        // element e of the 32x32 accumulator is head 8*(e/4) + 4*half + e%4
         float l2[16];
 #pragma unroll
         for (int e = 0; e < 16; ++e) {
             const int h = wave * 32 + 8 * (e >> 2) + 4 * half + (e & 3);
-            l2[e] = h < a.G ? a.lse[r * a.G + h] * kLog2e : __builtin_inff();
+            l2[e] = h < a.G ? lse_raw[e] * kLog2e : __builtin_inff();
         }
 
         const __amdgpu_buffer_rsrc_t krs = k_rsrc(k4, ri.kbase);
-        if (ntiles > 0) gather_tile<HT>(kbuf0, krs, key_cur, wave, lane);
+        auto gather = [&](uint4* dst, int tile, int32_t idx_reg) {
+            const int32_t rows = gather_row(tile, idx_reg);
+#pragma unroll
+            for (int i = 0; i < kTile / HT; ++i) {
+                const int kk = wave + i * HT;
+                const int32_t j = __builtin_amdgcn_readlane(rows, kk);
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(krs, SMLA_LDS(dst + kk * kPitch), 16,
+                                                         lane << 4, j << 10, 0, 0);
+            }
+        };
+        if (ntiles > 0) gather(kbuf0, 0, key_cur);
 
-        int32_t key_prev = -1;
-        // one tile: finish the previous tile's head sum, start the next
-        // tile's gather, then QK^T + exp + head sum of this tile
+        // Head-tile and half-wave partial sums of a tile, added in a fixed
+        // order; wave w finishes slots [w*32/HT, (w+1)*32/HT) with its first
+        // lanes. `key` is the tile's raw index register. The staged version
+        // has no branch: other lanes (and tiles < 0) write to the sink.
+        constexpr int kSlotsPerWave = kTile / HT;
+        auto reduce = [&](int tile, int32_t key) {
+            const int slot = (wave * kSlotsPerWave + lane) & (kTile - 1);
+            const int pb = tile & 1;
+            float tot = red[pb][0][slot];
+#pragma unroll
+            for (int w = 1; w < 2 * HT; ++w) tot += red[pb][w][slot];
+            const float v = tot * a.inv_g;
+            if constexpr (STAGED) {
+                const bool mine = lane < kSlotsPerWave && tile >= 0;
+                vals[mine ? tile * kTile + slot : kVcap + lane] = v;
+            } else {
+                const int32_t j = __shfl(key, slot);
+                if (lane < kSlotsPerWave && tile >= 0 && used(tile, slot, j))
+                    orow[ri.col0 + j] = v;
+            }
+        };
+
+        f32x16_t acc_prev = {};
+        int32_t key_p1 = -1, key_p2 = -1;  // raw indices of tiles t-1 and t-2
+        // One tile: finish tile-2's head sum, gather tile+1, QK^T of this
+        // tile with tile-1's epilogue.
         auto body = [&](int tile, const uint4* cur, uint4* nxt) {
-            // all gathers landed, zero-fill stores and partial sums done
+            // gathers of this tile landed, partial sums of tile-1 visible
             __builtin_amdgcn_s_waitcnt(0);
             __syncthreads();
-            if constexpr (HT > 1) {
-                if (tile > 0 && wave == 0 && lane < kTile) {
-                    const int pb = (tile - 1) & 1;
-                    float tot = red[pb][0][lane];
-#pragma unroll
-                    for (int w = 1; w < HT; ++w) tot += red[pb][w][lane];
-                    if (key_prev >= 0) orow[ri.col0 + key_prev] = tot * a.inv_g;
-                }
-            }
-            if (tile + 1 < ntiles) gather_tile<HT>(nxt, krs, key_nxt, wave, lane);
-            const int32_t key_nn = tile_key(tile + 2);
-
-            const f32x16_t acc = qk_tile<BF16>(cur, qa, col, half);
-            // exp(s - lse) = 2^(acc*scale*log2e - lse*log2e), summed over heads
-            float sum = 0.0f;
-#pragma unroll
-            for (int e = 0; e < 16; ++e)
-                sum += __builtin_amdgcn_exp2f(__builtin_fmaf(acc[e], a.c_scale, -l2[e]));
-            sum += __shfl_xor(sum, 32);
-            if constexpr (HT > 1) {
-                if (lane < kTile) red[tile & 1][wave][lane] = sum;
-            } else {
-                if (lane < kTile && key_cur >= 0) orow[ri.col0 + key_cur] = sum * a.inv_g;
-            }
-            key_prev = key_cur;
+            reduce(tile - 2, key_p2);
+            if (tile + 1 < ntiles) gather(nxt, tile + 1, key_nxt);
+            const int32_t key_nn = tile_idx(tile + 2);
+            float sum_prev;
+            const f32x16_t acc = qk_tile<BF16, false, HT>(cur, qa, col, half, acc_prev, l2,
+                                                          a.c_scale, &sum_prev, nullptr, krs, 0,
+                                                          wave, lane);
+            red[(tile - 1) & 1][2 * wave + half][col] = sum_prev;  // tile 0: unused slot
+            acc_prev = acc;
+            key_p2 = key_p1;
+            key_p1 = key_cur;
             key_cur = key_nxt;
             key_nxt = key_nn;
         };
@@ -282,33 +386,495 @@ __global__ __launch_bounds__(64 * HT, 2) void smla_l1norm_kernel(KernelArgs a) {
             body(tile, kbuf0, kbuf1);
             if (tile + 1 < ntiles) body(tile + 1, kbuf1, kbuf0);
         }
-        // head sum of the last tile; also keeps the next row's first gather
-        // from overwriting a tile some wave still reads
-        __builtin_amdgcn_s_waitcnt(0);
-        __syncthreads();
-        if constexpr (HT > 1) {
-            if (ntiles > 0 && wave == 0 && lane < kTile) {
-                const int pb = (ntiles - 1) & 1;
-                float tot = red[pb][0][lane];
+        if (ntiles > 0)
+            red[(ntiles - 1) & 1][2 * wave + half][col] = head_sum(acc_prev, l2, a.c_scale);
+
+        // indices for the row assembly, then the next row's Q and lse: all
+        // in flight together; waits below cover only the indices
+        int32_t jre[kPerThread];
+        if (staged) {
 #pragma unroll
-                for (int w = 1; w < HT; ++w) tot += red[pb][w][lane];
-                if (key_prev >= 0) orow[ri.col0 + key_prev] = tot * a.inv_g;
+            for (int i = 0; i < kPerThread; ++i)
+                jre[i] = __builtin_amdgcn_raw_buffer_load_b32(ridx, (uint32_t)(tid + i * NT) * 4u,
+                                                              0, 0);
+        }
+        // unconditional (a clamped row when this is the last one), so the new
+        // operands take over the registers of the old ones
+        load_row_operands(r_next < a.R ? r_next : r);
+
+        __syncthreads();  // partial sums in LDS (the barrier waits for LDS writes)
+        if (ntiles >= 2) reduce(ntiles - 2, key_p2);
+        if (ntiles >= 1) reduce(ntiles - 1, key_p1);
+
+        if (staged) {
+            // assemble columns [seg0, seg1) in LDS and write them once. Stage
+            // index of column c is c - c0 + m0, m0 aligning 16-byte groups of
+            // the output row with 16-byte groups of the stage.
+            for (int64_t c0 = seg0; c0 < seg1; c0 += kStage - 4) {
+                const int64_t len = (seg1 - c0 < kStage - 4) ? seg1 - c0 : kStage - 4;
+                const int m0 = (int)((r * a.W + c0) & 3);
+                __syncthreads();  // vals complete; previous chunk written out
+                for (int i = tid; i < (len + m0 + 3) >> 2; i += NT)
+                    reinterpret_cast<f32x4_t*>(stage)[i] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+                __syncthreads();
+#pragma unroll
+                for (int i = 0; i < kPerThread; ++i) {
+                    const int t = tid + i * NT;
+                    const int32_t j = jre[i];
+                    if (t < ri.n && (uint32_t)j < (uint32_t)ri.vis) {
+                        const int64_t c = ri.col0 + j - c0;
+                        if (c >= 0 && c < len) stage[c + m0] = vals[t];
+                    }
+                }
+                __syncthreads();
+                // 16-byte groups q cover columns c0 - m0 + 4q .. +3
+                const int ngroups = (int)((len + m0 + 3) >> 2);
+                for (int qg = tid; qg < ngroups; qg += NT) {
+                    const int64_t cb = c0 - m0 + 4 * (int64_t)qg;
+                    if (cb >= c0 && cb + 4 <= c0 + len) {
+                        const f32x4_t v = reinterpret_cast<const f32x4_t*>(stage)[qg];
+                        __builtin_nontemporal_store(v, reinterpret_cast<f32x4_t*>(orow + cb));
+                    } else {
+#pragma unroll
+                        for (int e = 0; e < 4; ++e)
+                            if (cb + e >= c0 && cb + e < c0 + len) orow[cb + e] = stage[4 * qg + e];
+                    }
+                }
+            }
+            __syncthreads();  // the next row's first gather reuses kbuf0
+        }
+        // end of row
+    }
+    // end of kernel
+}
+
+// ---------------------------------------------------------------------------
+// Pipelined kernel for rows of 65..128 heads with at most kVcap indices.
+//
+// One workgroup of 4 waves per CU: one wave per SIMD, so each wave has the
+// whole register file (Q of the current and of the next row, a deep operand
+// read-ahead) and the workgroup has all of LDS: four K tiles. The gather of
+// tile t+3 is spread over the MFMAs of tile t, so three tiles of compute
+// cover its latency. A barrier per tile publishes the gathered tile and frees
+// the oldest buffer; before it each wave waits only for its own loads of
+// that tile (vmcnt = the loads it issued after them), never for later ones.
+// At the end of a row the next row's first three gathers are issued before
+// this row's LDS assembly, which uses the fourth buffer as its stage, so the
+// pipeline does not drain between rows.
+
+// s_waitcnt with vmcnt(n) and lgkmcnt(0), expcnt untouched (immediate: vmcnt
+// bits [3:0] and [15:14], expcnt [6:4], lgkmcnt [11:8]); then a barrier with
+// no memory fence, so loads into LDS still in flight stay in flight.
+template <int N>
+__device__ __forceinline__ void waitcnt_vm_lgkm0() {
+    static_assert(N >= 0 && N <= 63, "vmcnt is six bits");
+    __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (((N >> 4) & 3) << 14));
+}
+__device__ __forceinline__ void barrier_after_vmcnt(int n) {
+    switch (n) {
+        // the counts the pipelined kernel produces; anything else waits for all
+        case 2: waitcnt_vm_lgkm0<2>(); break;
+        case 10: waitcnt_vm_lgkm0<10>(); break;
+        case 18: waitcnt_vm_lgkm0<18>(); break;
+        case 53: waitcnt_vm_lgkm0<53>(); break;
+        case 61: waitcnt_vm_lgkm0<61>(); break;
+        case 63: waitcnt_vm_lgkm0<63>(); break;
+        default: waitcnt_vm_lgkm0<0>(); break;
+    }
+    asm volatile("s_barrier" ::: "memory");
+}
+// barrier that publishes this wave's LDS writes (loads into LDS excluded)
+__device__ __forceinline__ void lds_barrier() {
+    waitcnt_vm_lgkm0<63>();
+    asm volatile("s_barrier" ::: "memory");
+}
+
+// Marks a loaded register as used here, on every path: the compiler then
+// waits for its load at this point instead of before a later reuse of the
+// register, where the wait would also cover the loads in flight since.
+__device__ __forceinline__ void consume(int32_t v) { asm volatile("" ::"v"(v)); }
+
+// 64 consecutive int32 (256 bytes at byte offset `off` of the buffer
+// described by `desc`) straight into LDS at `dst`, lane i -> dst[i]; bytes
+// past the buffer's end read as zero. Written as inline assembly so that
+// the compiler's wait-count tracking does not see it: the compiler cannot
+// follow a ring of LDS slots across loop iterations and would otherwise
+// wait for every load in flight before reading any slot. Completion is
+// waited for explicitly, by the barrier that counts it.
+typedef __attribute__((ext_vector_type(4))) int32_t i32x4_t;
+__device__ __forceinline__ i32x4_t raw_desc(const void* base, uint32_t bytes) {
+    const uint64_t p = reinterpret_cast<uint64_t>(base);
+    return i32x4_t{(int32_t)(uint32_t)p, (int32_t)((uint32_t)(p >> 32) & 0xffffu), (int32_t)bytes,
+                   0x00020000};
+}
+__device__ __forceinline__ void load_256b_to_lds(i32x4_t desc, uint32_t off, int32_t* dst,
+                                                 int lane) {
+    const uint32_t m0 = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) int32_t*)dst;
+    asm volatile(
+        "s_mov_b32 m0, %0\n\t"
+        "s_nop 0\n\t"
+        "buffer_load_dword %1, %2, %3 offen lds"
+        :
+        : "s"(m0), "v"(lane << 2), "s"(desc), "s"(off)
+        : "memory", "m0");
+}
+
+// One tile on the pipelined path, in a fixed instruction order (scheduling
+// barriers keep each k-step together): MFMA of step s, LDS read of the B
+// operand of step s + kLead, one head of the previous tile's epilogue (steps
+// 0..15), one gathered key row of tile t+3 (even steps 0..14) and the
+// caller's `mid` work at step kMid.
+template <bool BF16, bool GATHER, typename Mid>
+__device__ __forceinline__ f32x16_t qk_tile_seq(const uint4* __restrict__ src, const uint4* qa,
+                                                int col, int half, const f32x16_t& prev,
+                                                const float* l2, float c, float* prev_sum,
+                                                uint4* __restrict__ gdst,
+                                                __amdgpu_buffer_rsrc_t krs, int32_t rows,
+                                                int wave, int lane, Mid mid) {
+    constexpr int kSteps = kChunks / 2;
+    constexpr int kLead = 8;
+    constexpr int kMid = 6;
+    const uint4* row = src + col * kPitch + half;
+    uint4 b[kSteps];
+#pragma unroll
+    for (int s = 0; s < kLead; ++s) b[s] = row[2 * s];
+    f32x16_t acc = {};
+    float sum = 0.0f;
+#pragma unroll
+    for (int s = 0; s < kSteps; ++s) {
+        __builtin_amdgcn_sched_barrier(0);
+        acc = mfma_32x32x16<BF16>(qa[s], b[s], acc);
+        if (s + kLead < kSteps) b[s + kLead] = row[2 * (s + kLead)];
+        if (s < 16) {
+            // the empty asm statements pin this head's exp and add to this
+            // step (pure arithmetic is otherwise free to drift to the end)
+            float e = __builtin_amdgcn_exp2f(__builtin_fmaf(prev[s], c, -l2[s]));
+            asm volatile("" : "+v"(e));
+            sum += e;
+            asm volatile("" : "+v"(sum));
+        }
+        if constexpr (GATHER) {
+            if ((s & 1) == 0 && s < 16) {
+                const int kk = wave + (s >> 1) * 4;
+                const int32_t j = __builtin_amdgcn_readlane(rows, kk);
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(krs, SMLA_LDS(gdst + kk * kPitch), 16,
+                                                         lane << 4, j << 10, 0, 0);
             }
         }
+        if (s == kMid) mid();
     }
+    __builtin_amdgcn_sched_barrier(0);
+    *prev_sum = sum;
+    return acc;
+}
+
+template <bool BF16, bool TND>
+__global__ __launch_bounds__(256, 1) void smla_pipe_kernel(KernelArgs a) {
+    constexpr int HT = 4;
+    constexpr int NT = 256;
+    constexpr int kPerThread = kVcap / NT;
+    constexpr int kSlotsPerWave = kTile / HT;
+    // vector-memory instructions one wave issues to prefetch the next row:
+    // Q (32), lse (16), indices of tiles 0..2 (3)
+    constexpr int kPrefetchOps = kChunks / 2 + 16 + 3;
+    __shared__ uint4 kb0[kTile * kPitch];
+    __shared__ uint4 kb1[kTile * kPitch];
+    __shared__ uint4 kb2[kTile * kPitch];
+    __shared__ uint4 kb3[kTile * kPitch];   // also the row stage at the end of a row
+    // ring of index rows: slot t % 4 holds the indices of tile t (and, in
+    // its upper half, of tile t+1, unused), loaded straight into LDS
+    __shared__ int32_t ki0[64];
+    __shared__ int32_t ki1[64];
+    __shared__ int32_t ki2[64];
+    __shared__ int32_t ki3[64];
+    __shared__ float red[2][2 * HT][kTile];
+    __shared__ float vals[kVcap + 64];
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int half = lane >> 5;
+    const int col = lane & 31;
+    const int head = wave * 32 + col;
+    const uint4* __restrict__ k4 = static_cast<const uint4*>(a.k);
+    const uint4* __restrict__ q4 = static_cast<const uint4*>(a.q);
+    float* const stage = reinterpret_cast<float*>(kb3);
+
+    // ---- state of the current row (c*) and of the prefetched next row (n*)
+    int64_t it = 0;
+    int64_t rc = row_of(a, 0, blockIdx.x);   // num_wg <= R, so rc < R
+    RowInfo ric = decode_row<TND>(a, rc);
+    uint4 qa[kChunks / 2], qn[kChunks / 2];
+    float lse_n[16];
+    int32_t nk0, nk1, nk2;                  // raw indices of the next row's tiles 0..2
+    int64_t rn = a.R;
+    RowInfo rin = ric;
+
+    auto idx_rsrc = [&](int64_t r) { return rsrc(a.idx + r * a.K, (uint32_t)a.K * 4u); };
+    auto load_idx = [&](__amdgpu_buffer_rsrc_t ridx, int tile) -> int32_t {
+        return __builtin_amdgcn_raw_buffer_load_b32(ridx, (uint32_t)(tile * kTile + col) * 4u, 0,
+                                                    0);
+    };
+    // indices of tiles `tile` and tile+1 (lanes 0..31, 32..63) into a ring slot
+    auto idx_desc = [&](int64_t r) { return raw_desc(a.idx + r * a.K, (uint32_t)a.K * 4u); };
+    auto load_idx_lds = [&](i32x4_t desc, int32_t* slot, int tile) {
+        load_256b_to_lds(desc, (uint32_t)(tile * kTile * 4), slot, lane);
+    };
+    // Q (MFMA A operands), lse and the indices of tiles 0..2 of row r:
+    // kPrefetchOps vector-memory instructions
+    auto load_row = [&](int64_t r, uint4* q, float* lse, int32_t& i0, int32_t& i1, int32_t& i2) {
+        const __amdgpu_buffer_rsrc_t rq = rsrc(q4 + r * a.G * kChunks, (uint32_t)a.G * 1024u);
+        const uint32_t qoff = (uint32_t)head * 1024u + (uint32_t)half * 16u;
+#pragma unroll
+        for (int s = 0; s < kChunks / 2; ++s)
+            q[s] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(
+                                                 rq, qoff + 32u * s, 0, 2 /* nt */));
+        const __amdgpu_buffer_rsrc_t rl = rsrc(a.lse + r * a.G, (uint32_t)a.G * 4u);
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+            const int h = wave * 32 + 8 * (e >> 2) + 4 * half + (e & 3);
+            lse[e] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(
+                                                   rl, (uint32_t)h * 4u, 0, 0));
+        }
+        const __amdgpu_buffer_rsrc_t ridx = idx_rsrc(r);
+        i0 = load_idx(ridx, 0);
+        i1 = load_idx(ridx, 1);
+        i2 = load_idx(ridx, 2);
+    };
+    // next row of this workgroup (decoded) and its operands; the scalar loads
+    // of the decode are waited for here, so that later LDS waits can count
+    auto prefetch_next = [&]() {
+        rn = (it + 1) * a.num_wg < a.R ? row_of(a, it + 1, blockIdx.x) : a.R;
+        const int64_t rl = rn < a.R ? rn : rc;  // the last row loads itself again (unused)
+        rin = decode_row<TND>(a, rl);
+        load_row(rl, qn, lse_n, nk0, nk1, nk2);
+        waitcnt_vm_lgkm0<63>();
+    };
+    auto ntiles_of = [](const RowInfo& ri) { return (ri.n + kTile - 1) / kTile; };
+    // key row for slot `col` of `tile` holding raw index j: j if used, else 0
+    auto gather_row = [](const RowInfo& ri, int tile, int32_t j) -> int32_t {
+        return (tile * kTile + (threadIdx.x & 31) < ri.n && (uint32_t)j < (uint32_t)ri.vis) ? j : 0;
+    };
+    auto gather = [&](uint4* dst, __amdgpu_buffer_rsrc_t krs, int32_t rows) {
+#pragma unroll
+        for (int i = 0; i < kSlotsPerWave; ++i) {
+            const int kk = wave + i * HT;
+            const int32_t j = __builtin_amdgcn_readlane(rows, kk);
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(krs, SMLA_LDS(dst + kk * kPitch), 16,
+                                                     lane << 4, j << 10, 0, 0);
+        }
+    };
+    // a row's first three gathers and the index rows of its tiles 3..5
+    auto start_row = [&](const RowInfo& ri, int64_t r) {
+        const __amdgpu_buffer_rsrc_t krs = k_rsrc(k4, ri.kbase);
+        const int nt = ntiles_of(ri);
+        if (nt > 0) gather(kb0, krs, gather_row(ri, 0, nk0));
+        if (nt > 1) gather(kb1, krs, gather_row(ri, 1, nk1));
+        if (nt > 2) gather(kb2, krs, gather_row(ri, 2, nk2));
+        const i32x4_t desc = idx_desc(r);
+        load_idx_lds(desc, ki3, 3);
+        load_idx_lds(desc, ki0, 4);
+        load_idx_lds(desc, ki1, 5);
+    };
+
+    // ---- first row: operands, then tiles 0..2 in flight
+    load_row(rc, qa, lse_n, nk0, nk1, nk2);
+    start_row(ric, rc);
+    // l2 of the current row: lse_n holds the current row's lse here
+    float l2[16];
+    auto set_l2 = [&]() {
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+            const int h = wave * 32 + 8 * (e >> 2) + 4 * half + (e & 3);
+            l2[e] = h < a.G ? lse_n[e] * kLog2e : __builtin_inff();
+        }
+    };
+    set_l2();
+
+    for (; it * a.num_wg < a.R && rc < a.R; ++it) {
+        const int ntiles = ntiles_of(ric);
+        // the tile after whose MFMAs the next row is prefetched
+        const int pf = ntiles > 3 ? 2 : ntiles - 1;
+        float* __restrict__ orow = a.out + rc * a.W;
+        const __amdgpu_buffer_rsrc_t ridx = idx_rsrc(rc);
+        const i32x4_t idesc = idx_desc(rc);
+        const __amdgpu_buffer_rsrc_t krs = k_rsrc(k4, ric.kbase);
+        const int64_t seg0 = ric.col0;
+        const int64_t seg1 = ric.col0 + (ntiles > 0 ? ric.vis : 0);
+
+        if (ntiles == 0) prefetch_next();
+
+        f32x16_t acc_prev = {};
+        // One tile: barrier; tile-2's head-tile sums (read now, added at
+        // step kMid); index row of tile+6 into the ring; the gather of
+        // tile+3 spread over the MFMAs of this tile; tile-1's epilogue.
+        auto body = [&](auto gtag, int tile, const uint4* cur, uint4* gdst,
+                        const int32_t* key_slot, int32_t* load_slot) {
+            constexpr bool kGather = decltype(gtag)::value;
+            // Vector-memory instructions issued after the gather of this
+            // tile (in tile-3; they complete in order): the index row and
+            // gather of tiles -2 and -1, and the prefetch if it came after.
+            // Tile 0 waits for everything (the previous row's stores
+            // included); tiles 1 and 2 were gathered before that wait.
+            int later = 63;
+            if (tile == 0) {
+                later = 0;
+            } else if (tile >= 3) {
+                later = 2 + 8 * (tile + 1 < ntiles) + 8 * (tile + 2 < ntiles);
+                if (pf >= tile - 3 && pf < tile) later = min(63, later + kPrefetchOps);
+            }
+            barrier_after_vmcnt(later);
+            const int slot = (wave * kSlotsPerWave + lane) & (kTile - 1);
+            const int pb = tile & 1;  // parity of tile - 2
+            float parts[2 * HT];
+#pragma unroll
+            for (int w = 0; w < 2 * HT; ++w) parts[w] = red[pb][w][slot];
+            const int32_t key = key_slot[col];
+            load_idx_lds(idesc, load_slot, tile + 6);
+            const int32_t rows = gather_row(ric, tile + 3, key);
+            float sum_prev;
+            const f32x16_t acc = qk_tile_seq<BF16, kGather>(
+                cur, qa, col, half, acc_prev, l2, a.c_scale, &sum_prev, gdst, krs, rows, wave,
+                lane, [&]() {
+                    float tot = parts[0];
+#pragma unroll
+                    for (int w = 1; w < 2 * HT; ++w) tot += parts[w];
+                    const bool mine = lane < kSlotsPerWave && tile >= 2;
+                    vals[mine ? (tile - 2) * kTile + slot : kVcap + lane] = tot * a.inv_g;
+                });
+            red[(tile - 1) & 1][2 * wave + half][col] = sum_prev;  // tile 0: unused slot
+            acc_prev = acc;
+        };
+        using G1 = std::integral_constant<bool, true>;
+        using G0 = std::integral_constant<bool, false>;
+        // tile t reads K buffer t%4, gathers into (t+3)%4, reads the index
+        // row of tile t+3 from ring slot (t+3)%4 and loads tile t+6 into
+        // slot (t+2)%4
+        for (int tile = 0; tile < ntiles; ++tile) {
+            const bool g = tile + 3 < ntiles;
+            switch (tile & 3) {
+                case 0:
+                    if (g) body(G1{}, tile, kb0, kb3, ki3, ki2);
+                    else body(G0{}, tile, kb0, kb3, ki3, ki2);
+                    break;
+                case 1:
+                    if (g) body(G1{}, tile, kb1, kb0, ki0, ki3);
+                    else body(G0{}, tile, kb1, kb0, ki0, ki3);
+                    break;
+                case 2:
+                    if (g) body(G1{}, tile, kb2, kb1, ki1, ki0);
+                    else body(G0{}, tile, kb2, kb1, ki1, ki0);
+                    break;
+                default:
+                    if (g) body(G1{}, tile, kb3, kb2, ki2, ki1);
+                    else body(G0{}, tile, kb3, kb2, ki2, ki1);
+                    break;
+            }
+            if (tile == pf) prefetch_next();
+        }
+        if (ntiles > 0)
+            red[(ntiles - 1) & 1][2 * wave + half][col] = head_sum(acc_prev, l2, a.c_scale);
+
+        // indices for this row's assembly
+        int32_t jre[kPerThread];
+#pragma unroll
+        for (int i = 0; i < kPerThread; ++i)
+            jre[i] = __builtin_amdgcn_raw_buffer_load_b32(ridx, (uint32_t)(tid + i * NT) * 4u, 0, 0);
+        // all MFMAs done and every gather and index row of this row has
+        // landed: K buffers and ring slots are free; partial sums visible
+        lds_barrier();
+        auto reduce = [&](int tile) {
+            const int slot = (wave * kSlotsPerWave + lane) & (kTile - 1);
+            const int pb = tile & 1;
+            float tot = red[pb][0][slot];
+#pragma unroll
+            for (int w = 1; w < 2 * HT; ++w) tot += red[pb][w][slot];
+            const bool mine = lane < kSlotsPerWave;
+            vals[mine ? tile * kTile + slot : kVcap + lane] = tot * a.inv_g;
+        };
+        if (ntiles >= 2) reduce(ntiles - 2);
+        if (ntiles >= 1) reduce(ntiles - 1);
+
+        // the next row's first three tiles
+        if (rn < a.R) start_row(rin, rn);
+        consume(nk0);
+        consume(nk1);
+        consume(nk2);
+
+        // assemble columns [seg0, seg1) of this row in LDS and write them once
+        // (the next tile 0 barrier frees the stage for the next row's tile 3)
+        for (int64_t c0 = seg0; c0 < seg1; c0 += kStage - 4) {
+            const int64_t len = (seg1 - c0 < kStage - 4) ? seg1 - c0 : kStage - 4;
+            const int m0 = (int)((rc * a.W + c0) & 3);
+            lds_barrier();  // values complete; previous chunk written out
+            for (int i = tid; i < (len + m0 + 3) >> 2; i += NT)
+                reinterpret_cast<f32x4_t*>(stage)[i] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+            lds_barrier();
+#pragma unroll
+            for (int i = 0; i < kPerThread; ++i) {
+                const int t = tid + i * NT;
+                const int32_t j = jre[i];
+                if (t < ric.n && (uint32_t)j < (uint32_t)ric.vis) {
+                    const int64_t c = ric.col0 + j - c0;
+                    if (c >= 0 && c < len) stage[c + m0] = vals[t];
+                }
+            }
+            lds_barrier();
+            const int ngroups = (int)((len + m0 + 3) >> 2);
+            for (int qg = tid; qg < ngroups; qg += NT) {
+                const int64_t cb = c0 - m0 + 4 * (int64_t)qg;
+                if (cb >= c0 && cb + 4 <= c0 + len) {
+                    const f32x4_t v = reinterpret_cast<const f32x4_t*>(stage)[qg];
+                    __builtin_nontemporal_store(v, reinterpret_cast<f32x4_t*>(orow + cb));
+                } else {
+#pragma unroll
+                    for (int e = 0; e < 4; ++e)
+                        if (cb + e >= c0 && cb + e < c0 + len) orow[cb + e] = stage[4 * qg + e];
+                }
+            }
+        }
+        zero_span(orow, 0, seg0, tid, NT);
+        zero_span(orow, seg1, a.W, tid, NT);
+#pragma unroll
+        for (int i = 0; i < kPerThread; ++i) consume(jre[i]);
+
+        // the next row becomes current
+        rc = rn;
+        ric = rin;
+#pragma unroll
+        for (int s = 0; s < kChunks / 2; ++s) qa[s] = qn[s];
+        set_l2();
+    }
+}
+
+template <bool BF16, bool TND>
+hipError_t launch_pipe_t(const KernelArgs& a, hipStream_t stream) {
+    hipLaunchKernelGGL((smla_pipe_kernel<BF16, TND>), dim3(a.num_wg), dim3(256), 0, stream, a);
+    return hipGetLastError();
+}
+
+template <bool BF16, bool TND>
+hipError_t occupancy_pipe_t(int* out) {
+    return hipOccupancyMaxActiveBlocksPerMultiprocessor(
+        out, reinterpret_cast<const void*>(&smla_pipe_kernel<BF16, TND>), 256, 0);
 }
 
 template <int HT, bool BF16, bool TND>
 hipError_t launch_t(const KernelArgs& a, hipStream_t stream) {
-    hipLaunchKernelGGL((smla_l1norm_kernel<HT, BF16, TND>), dim3(a.num_wg), dim3(64 * HT),
-                       0, stream, a);
+    if (a.K <= kVcap)
+        hipLaunchKernelGGL((smla_l1norm_kernel<HT, BF16, TND, true>), dim3(a.num_wg),
+                           dim3(64 * HT), 0, stream, a);
+    else
+        hipLaunchKernelGGL((smla_l1norm_kernel<HT, BF16, TND, false>), dim3(a.num_wg),
+                           dim3(64 * HT), 0, stream, a);
     return hipGetLastError();
 }
 
 template <int HT, bool BF16, bool TND>
 hipError_t occupancy_t(int* out) {
     return hipOccupancyMaxActiveBlocksPerMultiprocessor(
-        out, reinterpret_cast<const void*>(&smla_l1norm_kernel<HT, BF16, TND>), 64 * HT, 0);
+        out, reinterpret_cast<const void*>(&smla_l1norm_kernel<HT, BF16, TND, true>), 64 * HT,
+        0);
 }
 
 }  // namespace
@@ -331,11 +897,21 @@ hipError_t occupancy_t(int* out) {
         return hipErrorInvalidValue;                                                  \
     } while (0)
 
+bool uses_pipe(int ht, int64_t topk) { return ht == 4 && topk <= kVcap; }
+
 hipError_t launch(const KernelArgs& a, int ht, bool bf16, bool tnd, hipStream_t stream) {
+    if (uses_pipe(ht, a.K)) {
+        if (bf16) return tnd ? launch_pipe_t<true, true>(a, stream) : launch_pipe_t<true, false>(a, stream);
+        return tnd ? launch_pipe_t<false, true>(a, stream) : launch_pipe_t<false, false>(a, stream);
+    }
     SMLA_DISPATCH(launch_t, a, stream);
 }
 
-hipError_t resident_per_cu(int ht, bool bf16, bool tnd, int* out) {
+hipError_t resident_per_cu(int ht, bool bf16, bool tnd, int64_t topk, int* out) {
+    if (uses_pipe(ht, topk)) {
+        if (bf16) return tnd ? occupancy_pipe_t<true, true>(out) : occupancy_pipe_t<true, false>(out);
+        return tnd ? occupancy_pipe_t<false, true>(out) : occupancy_pipe_t<false, false>(out);
+    }
     SMLA_DISPATCH(occupancy_t, out);
 }
 
