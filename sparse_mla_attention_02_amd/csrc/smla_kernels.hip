@@ -123,19 +123,31 @@ __device__ __forceinline__ RowInfo decode_row(const KernelArgs& a, int64_t r) {
         if (s2 < 0) s2 = 0;
         col0 = kbase;
     } else {
-        b = r / a.S1;
-        i = r - b * a.S1;
+        // rows and k rows number fewer than 2^31 (checked on the host): 32-bit
+        // division
+        const uint32_t b32 = (uint32_t)r / (uint32_t)a.S1;
+        b = b32;
+        i = (int64_t)((uint32_t)r - b32 * (uint32_t)a.S1);
         s1 = a.S1;
         s2 = a.S2;
-        kbase = b * a.S2;
+        kbase = (int64_t)(b32 * (uint32_t)a.S2);
         col0 = 0;
     }
     int64_t vis = s2;
     if (a.mask_mode == 3) {
+        // floor((d + s2*r) / r) = s2 - ceil(-d / r) with d = i + 1 + res - s1,
+        // in 32-bit arithmetic: -d <= s1 - res < 2^32 for any residual >= -2^31
+        // with s1 < 2^31 (larger values saturate)
         const int64_t res = a.cmp_res ? (int64_t)uload(a.cmp_res, b) : 0;
-        const int64_t p1 = i + 1 + s2 * a.cmp_ratio + res - s1;
-        vis = p1 > 0 ? p1 / a.cmp_ratio : 0;
-        if (vis > s2) vis = s2;
+        const int64_t d = i + 1 + res - s1;
+        if (d < 0) {
+            const uint32_t nd = -d > 0xffffffffll ? 0xffffffffu : (uint32_t)(-d);
+            const uint32_t rr = (uint32_t)a.cmp_ratio;
+            const uint32_t q = nd / rr;
+            const int64_t up = (int64_t)q + (nd - q * rr != 0u ? 1 : 0);
+            vis = s2 - up;
+            if (vis < 0) vis = 0;
+        }
     }
     int32_t n = a.K;
     if (a.topk_len) {
@@ -458,26 +470,39 @@ __global__ __launch_bounds__(64 * HT, 2) void smla_l1norm_kernel(KernelArgs a) {
 // cover its latency. A barrier per tile publishes the gathered tile and frees
 // the oldest buffer; before it each wave waits only for its own loads of
 // that tile (vmcnt = the loads it issued after them), never for later ones.
-// At the end of a row the next row's first three gathers are issued before
-// this row's LDS assembly, which uses the fourth buffer as its stage, so the
-// pipeline does not drain between rows.
+// The next row's Q is loaded in chunks spread over nine tiles. At the end
+// of a row the next row's first three gathers are issued before this row's
+// LDS assembly, which uses the fourth buffer as its stage, so the pipeline
+// does not drain between rows.
+//
+// With one wave per SIMD, every instruction of a wave is issued in the time
+// of the MFMAs, so the tile body is laid out by hand: each k-step holds one
+// MFMA, one operand read, at most two independent VALU instructions of the
+// previous tile's epilogue, and every fourth step one gathered key row.
+//
+// All loads into LDS are inline assembly: the compiler's wait-count
+// tracking cannot follow LDS slots reused across loop iterations and would
+// otherwise wait for every load in flight before any LDS read. Their
+// completion is waited for explicitly, by the barrier that counts them.
 
-// s_waitcnt with vmcnt(n) and lgkmcnt(0), expcnt untouched (immediate: vmcnt
-// bits [3:0] and [15:14], expcnt [6:4], lgkmcnt [11:8]); then a barrier with
-// no memory fence, so loads into LDS still in flight stay in flight.
+// s_waitcnt with vmcnt(N) and lgkmcnt(0), expcnt untouched (immediate: vmcnt
+// bits [3:0] and [15:14], expcnt [6:4], lgkmcnt [11:8]).
 template <int N>
 __device__ __forceinline__ void waitcnt_vm_lgkm0() {
     static_assert(N >= 0 && N <= 63, "vmcnt is six bits");
     __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (((N >> 4) & 3) << 14));
 }
+// vmcnt(n) and lgkmcnt(0), then a barrier with no memory fence, so loads
+// into LDS still in flight stay in flight.
 __device__ __forceinline__ void barrier_after_vmcnt(int n) {
     switch (n) {
         // the counts the pipelined kernel produces; anything else waits for all
         case 2: waitcnt_vm_lgkm0<2>(); break;
+        case 5: waitcnt_vm_lgkm0<5>(); break;
         case 10: waitcnt_vm_lgkm0<10>(); break;
+        case 13: waitcnt_vm_lgkm0<13>(); break;
         case 18: waitcnt_vm_lgkm0<18>(); break;
-        case 53: waitcnt_vm_lgkm0<53>(); break;
-        case 61: waitcnt_vm_lgkm0<61>(); break;
+        case 21: waitcnt_vm_lgkm0<21>(); break;
         case 63: waitcnt_vm_lgkm0<63>(); break;
         default: waitcnt_vm_lgkm0<0>(); break;
     }
@@ -493,78 +518,97 @@ __device__ __forceinline__ void lds_barrier() {
 // waits for its load at this point instead of before a later reuse of the
 // register, where the wait would also cover the loads in flight since.
 __device__ __forceinline__ void consume(int32_t v) { asm volatile("" ::"v"(v)); }
+// Keeps a value's computation at this point of the instruction stream (pure
+// arithmetic is otherwise free to move to its first use).
+__device__ __forceinline__ void pin(float& v) { asm volatile("" : "+v"(v)); }
+__device__ __forceinline__ void pin_s(int32_t& v) { asm volatile("" : "+s"(v)); }
 
-// 64 consecutive int32 (256 bytes at byte offset `off` of the buffer
-// described by `desc`) straight into LDS at `dst`, lane i -> dst[i]; bytes
-// past the buffer's end read as zero. Written as inline assembly so that
-// the compiler's wait-count tracking does not see it: the compiler cannot
-// follow a ring of LDS slots across loop iterations and would otherwise
-// wait for every load in flight before reading any slot. Completion is
-// waited for explicitly, by the barrier that counts it.
+// Buffer descriptor as four dwords (base, range in bytes, gfx9 untyped
+// format); offsets at or past `bytes` read as zero.
 typedef __attribute__((ext_vector_type(4))) int32_t i32x4_t;
 __device__ __forceinline__ i32x4_t raw_desc(const void* base, uint32_t bytes) {
     const uint64_t p = reinterpret_cast<uint64_t>(base);
     return i32x4_t{(int32_t)(uint32_t)p, (int32_t)((uint32_t)(p >> 32) & 0xffffu), (int32_t)bytes,
                    0x00020000};
 }
-__device__ __forceinline__ void load_256b_to_lds(i32x4_t desc, uint32_t off, int32_t* dst,
-                                                 int lane) {
-    const uint32_t m0 = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) int32_t*)dst;
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+    return (uint32_t)(uintptr_t)(__attribute__((address_space(3))) const void*)p;
+}
+// Lane i moves 16 bytes at byte offset voff + soff of the buffer to LDS
+// address m0 + 16 i: with voff = 16 i, one 1 KB key row per instruction.
+// soff must not come from a VALU instruction fewer than five wait states
+// earlier.
+__device__ __forceinline__ void dma_row(i32x4_t desc, uint32_t m0, int32_t soff, uint32_t voff) {
+    asm volatile(
+        "s_mov_b32 m0, %0\n\t"
+        "s_nop 0\n\t"
+        "buffer_load_dwordx4 %1, %2, %3 offen lds"
+        :
+        : "s"(m0), "v"(voff), "s"(desc), "s"(soff)
+        : "memory", "m0");
+}
+// Lane i moves 4 bytes at byte offset voff + soff to LDS address m0 + 4 i.
+__device__ __forceinline__ void dma_dword(i32x4_t desc, uint32_t m0, int32_t soff, uint32_t voff) {
     asm volatile(
         "s_mov_b32 m0, %0\n\t"
         "s_nop 0\n\t"
         "buffer_load_dword %1, %2, %3 offen lds"
         :
-        : "s"(m0), "v"(lane << 2), "s"(desc), "s"(off)
+        : "s"(m0), "v"(voff), "s"(desc), "s"(soff)
         : "memory", "m0");
 }
 
-// One tile on the pipelined path, in a fixed instruction order (scheduling
-// barriers keep each k-step together): MFMA of step s, LDS read of the B
-// operand of step s + kLead, one head of the previous tile's epilogue (steps
-// 0..15), one gathered key row of tile t+3 (even steps 0..14) and the
-// caller's `mid` work at step kMid.
+constexpr int kBufBytes = kTile * kPitch * 16;  // one K tile in LDS
+constexpr int kRowBytes = kPitch * 16;          // one key row in LDS
+
+// One tile on the pipelined path. Step s: MFMA s; LDS read of the B operand
+// of step s + kLead; epilogue of the previous tile, head e = s/2: FMA at
+// step 2e, exp at 2e+1, added to the sum at 2e+2; key row i of this wave's
+// share of tile t+3 (GATHER): row offset read at step 4i, load at 4i+2;
+// `mid(s)` for the caller's own spread-out work.
 template <bool BF16, bool GATHER, typename Mid>
 __device__ __forceinline__ f32x16_t qk_tile_seq(const uint4* __restrict__ src, const uint4* qa,
                                                 int col, int half, const f32x16_t& prev,
                                                 const float* l2, float c, float* prev_sum,
-                                                uint4* __restrict__ gdst,
-                                                __amdgpu_buffer_rsrc_t krs, int32_t rows,
-                                                int wave, int lane, Mid mid) {
+                                                i32x4_t kdesc, uint32_t m0_rows, int32_t rows_off,
+                                                uint32_t voff, Mid mid) {
     constexpr int kSteps = kChunks / 2;
     constexpr int kLead = 8;
-    constexpr int kMid = 6;
     const uint4* row = src + col * kPitch + half;
     uint4 b[kSteps];
 #pragma unroll
     for (int s = 0; s < kLead; ++s) b[s] = row[2 * s];
     f32x16_t acc = {};
-    float sum = 0.0f;
+    float sum = 0.0f, t = 0.0f, ex = 0.0f;
+    int32_t soff = 0;
 #pragma unroll
     for (int s = 0; s < kSteps; ++s) {
         __builtin_amdgcn_sched_barrier(0);
         acc = mfma_32x32x16<BF16>(qa[s], b[s], acc);
         if (s + kLead < kSteps) b[s + kLead] = row[2 * (s + kLead)];
-        if (s < 16) {
-            // the empty asm statements pin this head's exp and add to this
-            // step (pure arithmetic is otherwise free to drift to the end)
-            float e = __builtin_amdgcn_exp2f(__builtin_fmaf(prev[s], c, -l2[s]));
-            asm volatile("" : "+v"(e));
-            sum += e;
-            asm volatile("" : "+v"(sum));
+        if ((s & 1) == 0) {
+            if (s >= 2) {
+                sum += ex;
+                pin(sum);
+            }
+            t = __builtin_fmaf(prev[s >> 1], c, -l2[s >> 1]);
+            pin(t);
+        } else {
+            ex = __builtin_amdgcn_exp2f(t);
+            pin(ex);
         }
         if constexpr (GATHER) {
-            if ((s & 1) == 0 && s < 16) {
-                const int kk = wave + (s >> 1) * 4;
-                const int32_t j = __builtin_amdgcn_readlane(rows, kk);
-                __builtin_amdgcn_raw_ptr_buffer_load_lds(krs, SMLA_LDS(gdst + kk * kPitch), 16,
-                                                         lane << 4, j << 10, 0, 0);
+            if ((s & 3) == 0) {
+                soff = __builtin_amdgcn_readlane(rows_off, s >> 2);
+                pin_s(soff);
+            } else if ((s & 3) == 2) {
+                dma_row(kdesc, m0_rows + (uint32_t)((s >> 2) * kRowBytes), soff, voff);
             }
         }
-        if (s == kMid) mid();
+        mid(s);
     }
     __builtin_amdgcn_sched_barrier(0);
-    *prev_sum = sum;
+    *prev_sum = sum + ex;
     return acc;
 }
 
@@ -574,19 +618,13 @@ __global__ __launch_bounds__(256, 1) void smla_pipe_kernel(KernelArgs a) {
     constexpr int NT = 256;
     constexpr int kPerThread = kVcap / NT;
     constexpr int kSlotsPerWave = kTile / HT;
-    // vector-memory instructions one wave issues to prefetch the next row:
-    // Q (32), lse (16), indices of tiles 0..2 (3)
-    constexpr int kPrefetchOps = kChunks / 2 + 16 + 3;
-    __shared__ uint4 kb0[kTile * kPitch];
-    __shared__ uint4 kb1[kTile * kPitch];
-    __shared__ uint4 kb2[kTile * kPitch];
-    __shared__ uint4 kb3[kTile * kPitch];   // also the row stage at the end of a row
-    // ring of index rows: slot t % 4 holds the indices of tile t (and, in
-    // its upper half, of tile t+1, unused), loaded straight into LDS
-    __shared__ int32_t ki0[64];
-    __shared__ int32_t ki1[64];
-    __shared__ int32_t ki2[64];
-    __shared__ int32_t ki3[64];
+    // mid-row prefetch of the next row: the gather indices of its tiles 0..2
+    constexpr int kPrefetchOps = 3;
+    // K tiles (tile t in buffer t % 4; the last one doubles as the row stage)
+    __shared__ uint4 kbuf[4][kTile * kPitch];
+    // index rows: slot t % 4 holds the indices of tile t (lanes 0..31) and of
+    // tile t+1 (32..63, unused)
+    __shared__ int32_t kring[4][64];
     __shared__ float red[2][2 * HT][kTile];
     __shared__ float vals[kVcap + 64];
 
@@ -596,90 +634,111 @@ __global__ __launch_bounds__(256, 1) void smla_pipe_kernel(KernelArgs a) {
     const int half = lane >> 5;
     const int col = lane & 31;
     const int head = wave * 32 + col;
-    const uint4* __restrict__ k4 = static_cast<const uint4*>(a.k);
+    // this wave gathers key rows 8w .. 8w+7 of every tile; lane l < 8 holds
+    // the index of row 8w + l
+    const int my_slot = kSlotsPerWave * wave + (lane & 7);
     const uint4* __restrict__ q4 = static_cast<const uint4*>(a.q);
-    float* const stage = reinterpret_cast<float*>(kb3);
+    const char* __restrict__ kbytes = static_cast<const char*>(a.k);
+    float* const stage = reinterpret_cast<float*>(kbuf[3]);
+    const uint32_t kbuf_lds = lds_addr(kbuf);
+    const uint32_t ring_lds = lds_addr(kring);
+    const uint32_t voff16 = (uint32_t)lane << 4;
+    const uint32_t voff4 = (uint32_t)lane << 2;
 
     // ---- state of the current row (c*) and of the prefetched next row (n*)
     int64_t it = 0;
     int64_t rc = row_of(a, 0, blockIdx.x);   // num_wg <= R, so rc < R
     RowInfo ric = decode_row<TND>(a, rc);
-    uint4 qa[kChunks / 2], qn[kChunks / 2];
+    uint4 qa[kChunks / 2];
     float lse_n[16];
-    int32_t nk0, nk1, nk2;                  // raw indices of the next row's tiles 0..2
-    int64_t rn = a.R;
+    int32_t nk0, nk1, nk2;                  // next row: index of key row my_slot, tiles 0..2
+    int64_t rn = a.R, rln = rc;             // next row, and the row its loads read
     RowInfo rin = ric;
 
     auto idx_rsrc = [&](int64_t r) { return rsrc(a.idx + r * a.K, (uint32_t)a.K * 4u); };
-    auto load_idx = [&](__amdgpu_buffer_rsrc_t ridx, int tile) -> int32_t {
-        return __builtin_amdgcn_raw_buffer_load_b32(ridx, (uint32_t)(tile * kTile + col) * 4u, 0,
-                                                    0);
-    };
-    // indices of tiles `tile` and tile+1 (lanes 0..31, 32..63) into a ring slot
     auto idx_desc = [&](int64_t r) { return raw_desc(a.idx + r * a.K, (uint32_t)a.K * 4u); };
-    auto load_idx_lds = [&](i32x4_t desc, int32_t* slot, int tile) {
-        load_256b_to_lds(desc, (uint32_t)(tile * kTile * 4), slot, lane);
+    auto k_desc = [&](const RowInfo& ri) {
+        const int64_t rows = a.rows_k - ri.kbase;
+        const int64_t bytes = rows * 1024;
+        return raw_desc(kbytes + ri.kbase * 1024,
+                        bytes > 0xffffffffll ? 0xffffffffu : (uint32_t)(bytes < 0 ? 0 : bytes));
     };
-    // Q (MFMA A operands), lse and the indices of tiles 0..2 of row r:
-    // kPrefetchOps vector-memory instructions
-    auto load_row = [&](int64_t r, uint4* q, float* lse, int32_t& i0, int32_t& i1, int32_t& i2) {
-        const __amdgpu_buffer_rsrc_t rq = rsrc(q4 + r * a.G * kChunks, (uint32_t)a.G * 1024u);
-        const uint32_t qoff = (uint32_t)head * 1024u + (uint32_t)half * 16u;
-#pragma unroll
-        for (int s = 0; s < kChunks / 2; ++s)
-            q[s] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(
-                                                 rq, qoff + 32u * s, 0, 2 /* nt */));
+    auto q_rsrc = [&](int64_t r) { return rsrc(q4 + r * a.G * kChunks, (uint32_t)a.G * 1024u); };
+    const uint32_t qoff = (uint32_t)head * 1024u + (uint32_t)half * 16u;
+    auto load_q = [&](__amdgpu_buffer_rsrc_t rq, uint4* q, int s) {
+        q[s] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rq, qoff + 32u * s,
+                                                                                 0, 2 /* nt */));
+    };
+    auto load_lse = [&](int64_t r) {
         const __amdgpu_buffer_rsrc_t rl = rsrc(a.lse + r * a.G, (uint32_t)a.G * 4u);
 #pragma unroll
         for (int e = 0; e < 16; ++e) {
             const int h = wave * 32 + 8 * (e >> 2) + 4 * half + (e & 3);
-            lse[e] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(
-                                                   rl, (uint32_t)h * 4u, 0, 0));
+            lse_n[e] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(
+                                                     rl, (uint32_t)h * 4u, 0, 0));
         }
-        const __amdgpu_buffer_rsrc_t ridx = idx_rsrc(r);
-        i0 = load_idx(ridx, 0);
-        i1 = load_idx(ridx, 1);
-        i2 = load_idx(ridx, 2);
     };
-    // next row of this workgroup (decoded) and its operands; the scalar loads
-    // of the decode are waited for here, so that later LDS waits can count
+    auto load_row_q = [&](int64_t r) {
+        const __amdgpu_buffer_rsrc_t rq = q_rsrc(r);
+#pragma unroll
+        for (int s = 0; s < kChunks / 2; ++s) load_q(rq, qa, s);
+    };
+    // the next row of this workgroup, decoded, and the gather indices of its
+    // tiles 0..2 (kPrefetchOps loads; the decode's scalar loads are waited
+    // for here, so that later LDS waits can count)
     auto prefetch_next = [&]() {
         rn = (it + 1) * a.num_wg < a.R ? row_of(a, it + 1, blockIdx.x) : a.R;
-        const int64_t rl = rn < a.R ? rn : rc;  // the last row loads itself again (unused)
-        rin = decode_row<TND>(a, rl);
-        load_row(rl, qn, lse_n, nk0, nk1, nk2);
+        rln = rn < a.R ? rn : rc;  // the last row loads itself again (unused)
+        rin = decode_row<TND>(a, rln);
         waitcnt_vm_lgkm0<63>();
+        const __amdgpu_buffer_rsrc_t ridx = idx_rsrc(rln);
+        nk0 = __builtin_amdgcn_raw_buffer_load_b32(ridx, (uint32_t)(0 * kTile + my_slot) * 4u, 0, 0);
+        nk1 = __builtin_amdgcn_raw_buffer_load_b32(ridx, (uint32_t)(1 * kTile + my_slot) * 4u, 0, 0);
+        nk2 = __builtin_amdgcn_raw_buffer_load_b32(ridx, (uint32_t)(2 * kTile + my_slot) * 4u, 0, 0);
     };
     auto ntiles_of = [](const RowInfo& ri) { return (ri.n + kTile - 1) / kTile; };
-    // key row for slot `col` of `tile` holding raw index j: j if used, else 0
-    auto gather_row = [](const RowInfo& ri, int tile, int32_t j) -> int32_t {
-        return (tile * kTile + (threadIdx.x & 31) < ri.n && (uint32_t)j < (uint32_t)ri.vis) ? j : 0;
-    };
-    auto gather = [&](uint4* dst, __amdgpu_buffer_rsrc_t krs, int32_t rows) {
-#pragma unroll
-        for (int i = 0; i < kSlotsPerWave; ++i) {
-            const int kk = wave + i * HT;
-            const int32_t j = __builtin_amdgcn_readlane(rows, kk);
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(krs, SMLA_LDS(dst + kk * kPitch), 16,
-                                                     lane << 4, j << 10, 0, 0);
-        }
+    // byte offset of the key row of slot my_slot of `tile` holding raw index
+    // j: j's row if the entry is used, else row 0 (loaded, never read)
+    auto row_off = [&](const RowInfo& ri, int tile, int32_t j) -> int32_t {
+        return (tile * kTile + my_slot < ri.n && (uint32_t)j < (uint32_t)ri.vis) ? (j << 10) : 0;
     };
     // a row's first three gathers and the index rows of its tiles 3..5
     auto start_row = [&](const RowInfo& ri, int64_t r) {
-        const __amdgpu_buffer_rsrc_t krs = k_rsrc(k4, ri.kbase);
+        const i32x4_t kd = k_desc(ri);
         const int nt = ntiles_of(ri);
-        if (nt > 0) gather(kb0, krs, gather_row(ri, 0, nk0));
-        if (nt > 1) gather(kb1, krs, gather_row(ri, 1, nk1));
-        if (nt > 2) gather(kb2, krs, gather_row(ri, 2, nk2));
-        const i32x4_t desc = idx_desc(r);
-        load_idx_lds(desc, ki3, 3);
-        load_idx_lds(desc, ki0, 4);
-        load_idx_lds(desc, ki1, 5);
+        const int32_t o0 = row_off(ri, 0, nk0), o1 = row_off(ri, 1, nk1), o2 = row_off(ri, 2, nk2);
+        const uint32_t m0w = kbuf_lds + (uint32_t)(kSlotsPerWave * wave * kRowBytes);
+#pragma unroll
+        for (int k = 0; k < 3; ++k) {
+            if (nt > k) {
+                const int32_t o = k == 0 ? o0 : (k == 1 ? o1 : o2);
+                int32_t so[kSlotsPerWave];
+#pragma unroll
+                for (int i = 0; i < kSlotsPerWave; ++i) {
+                    so[i] = __builtin_amdgcn_readlane(o, i);
+                    pin_s(so[i]);
+                }
+#pragma unroll
+                for (int i = 0; i < kSlotsPerWave; ++i)
+                    dma_row(kd, m0w + (uint32_t)(k * kBufBytes + i * kRowBytes), so[i], voff16);
+            }
+        }
+        const i32x4_t id = idx_desc(r);
+        dma_dword(id, ring_lds + 3u * 256u, 3 * kTile * 4, voff4);
+        dma_dword(id, ring_lds + 0u * 256u, 4 * kTile * 4, voff4);
+        dma_dword(id, ring_lds + 1u * 256u, 5 * kTile * 4, voff4);
     };
 
     // ---- first row: operands, then tiles 0..2 in flight
-    load_row(rc, qa, lse_n, nk0, nk1, nk2);
-    start_row(ric, rc);
+    {
+        load_row_q(rc);
+        load_lse(rc);
+        const __amdgpu_buffer_rsrc_t ridx = idx_rsrc(rc);
+        nk0 = __builtin_amdgcn_raw_buffer_load_b32(ridx, (uint32_t)(0 * kTile + my_slot) * 4u, 0, 0);
+        nk1 = __builtin_amdgcn_raw_buffer_load_b32(ridx, (uint32_t)(1 * kTile + my_slot) * 4u, 0, 0);
+        nk2 = __builtin_amdgcn_raw_buffer_load_b32(ridx, (uint32_t)(2 * kTile + my_slot) * 4u, 0, 0);
+        start_row(ric, rc);
+    }
     // l2 of the current row: lse_n holds the current row's lse here
     float l2[16];
     auto set_l2 = [&]() {
@@ -695,81 +754,71 @@ __global__ __launch_bounds__(256, 1) void smla_pipe_kernel(KernelArgs a) {
         const int ntiles = ntiles_of(ric);
         // the tile after whose MFMAs the next row is prefetched
         const int pf = ntiles > 3 ? 2 : ntiles - 1;
+        auto extra = [&](int u) -> int { return u == pf ? kPrefetchOps : 0; };
         float* __restrict__ orow = a.out + rc * a.W;
         const __amdgpu_buffer_rsrc_t ridx = idx_rsrc(rc);
         const i32x4_t idesc = idx_desc(rc);
-        const __amdgpu_buffer_rsrc_t krs = k_rsrc(k4, ric.kbase);
+        const i32x4_t kdesc = k_desc(ric);
         const int64_t seg0 = ric.col0;
         const int64_t seg1 = ric.col0 + (ntiles > 0 ? ric.vis : 0);
 
         if (ntiles == 0) prefetch_next();
 
         f32x16_t acc_prev = {};
-        // One tile: barrier; tile-2's head-tile sums (read now, added at
-        // step kMid); index row of tile+6 into the ring; the gather of
-        // tile+3 spread over the MFMAs of this tile; tile-1's epilogue.
-        auto body = [&](auto gtag, int tile, const uint4* cur, uint4* gdst,
-                        const int32_t* key_slot, int32_t* load_slot) {
+        // One tile: barrier; index row of tile+3 from the ring, of tile+6
+        // into it; tile-2's head-tile sums (read now, added over steps
+        // 1..7, stored at 8); the gather of tile+3 spread over the MFMAs of
+        // this tile; tile-1's epilogue.
+        auto body = [&](auto gtag, int tile) {
             constexpr bool kGather = decltype(gtag)::value;
-            // Vector-memory instructions issued after the gather of this
-            // tile (in tile-3; they complete in order): the index row and
-            // gather of tiles -2 and -1, and the prefetch if it came after.
-            // Tile 0 waits for everything (the previous row's stores
+            // Loads issued after the gather of this tile (in tile-3; vector
+            // memory returns in order): index row and gather of tiles -2 and
+            // -1, and the prefetch if it came after. Tile 0 waits for
+            // everything (the previous row's stores and this row's Q
             // included); tiles 1 and 2 were gathered before that wait.
             int later = 63;
             if (tile == 0) {
                 later = 0;
             } else if (tile >= 3) {
-                later = 2 + 8 * (tile + 1 < ntiles) + 8 * (tile + 2 < ntiles);
-                if (pf >= tile - 3 && pf < tile) later = min(63, later + kPrefetchOps);
+                later = extra(tile - 3) + 2 + 8 * (tile + 1 < ntiles) + 8 * (tile + 2 < ntiles) +
+                        extra(tile - 2) + extra(tile - 1);
+                later = later > 63 ? 63 : later;
             }
             barrier_after_vmcnt(later);
+            const int32_t key = kring[(tile + 3) & 3][my_slot];
+            dma_dword(idesc, ring_lds + (uint32_t)(((tile + 2) & 3) * 256), (tile + 6) * kTile * 4,
+                      voff4);
             const int slot = (wave * kSlotsPerWave + lane) & (kTile - 1);
             const int pb = tile & 1;  // parity of tile - 2
             float parts[2 * HT];
 #pragma unroll
             for (int w = 0; w < 2 * HT; ++w) parts[w] = red[pb][w][slot];
-            const int32_t key = key_slot[col];
-            load_idx_lds(idesc, load_slot, tile + 6);
-            const int32_t rows = gather_row(ric, tile + 3, key);
+            const int32_t rows_off = row_off(ric, tile + 3, key);
+            const uint32_t m0_rows = kbuf_lds + (uint32_t)(((tile + 3) & 3) * kBufBytes +
+                                                           kSlotsPerWave * wave * kRowBytes);
+            float tot = 0.0f;
             float sum_prev;
             const f32x16_t acc = qk_tile_seq<BF16, kGather>(
-                cur, qa, col, half, acc_prev, l2, a.c_scale, &sum_prev, gdst, krs, rows, wave,
-                lane, [&]() {
-                    float tot = parts[0];
-#pragma unroll
-                    for (int w = 1; w < 2 * HT; ++w) tot += parts[w];
-                    const bool mine = lane < kSlotsPerWave && tile >= 2;
-                    vals[mine ? (tile - 2) * kTile + slot : kVcap + lane] = tot * a.inv_g;
+                kbuf[tile & 3], qa, col, half, acc_prev, l2, a.c_scale, &sum_prev, kdesc, m0_rows,
+                rows_off, voff16, [&](int s) {
+                    if (s == 1) {
+                        tot = parts[0] + parts[1];
+                        pin(tot);
+                    } else if (s >= 2 && s < 2 * HT) {
+                        tot += parts[s];
+                        pin(tot);
+                    } else if (s == 2 * HT) {
+                        const bool mine = lane < kSlotsPerWave && tile >= 2;
+                        vals[mine ? (tile - 2) * kTile + slot : kVcap + lane] = tot * a.inv_g;
+                    }
                 });
             red[(tile - 1) & 1][2 * wave + half][col] = sum_prev;  // tile 0: unused slot
             acc_prev = acc;
         };
         using G1 = std::integral_constant<bool, true>;
         using G0 = std::integral_constant<bool, false>;
-        // tile t reads K buffer t%4, gathers into (t+3)%4, reads the index
-        // row of tile t+3 from ring slot (t+3)%4 and loads tile t+6 into
-        // slot (t+2)%4
         for (int tile = 0; tile < ntiles; ++tile) {
-            const bool g = tile + 3 < ntiles;
-            switch (tile & 3) {
-                case 0:
-                    if (g) body(G1{}, tile, kb0, kb3, ki3, ki2);
-                    else body(G0{}, tile, kb0, kb3, ki3, ki2);
-                    break;
-                case 1:
-                    if (g) body(G1{}, tile, kb1, kb0, ki0, ki3);
-                    else body(G0{}, tile, kb1, kb0, ki0, ki3);
-                    break;
-                case 2:
-                    if (g) body(G1{}, tile, kb2, kb1, ki1, ki0);
-                    else body(G0{}, tile, kb2, kb1, ki1, ki0);
-                    break;
-                default:
-                    if (g) body(G1{}, tile, kb3, kb2, ki2, ki1);
-                    else body(G0{}, tile, kb3, kb2, ki2, ki1);
-                    break;
-            }
+            if (tile + 3 < ntiles) body(G1{}, tile); else body(G0{}, tile);
             if (tile == pf) prefetch_next();
         }
         if (ntiles > 0)
@@ -780,8 +829,8 @@ __global__ __launch_bounds__(256, 1) void smla_pipe_kernel(KernelArgs a) {
 #pragma unroll
         for (int i = 0; i < kPerThread; ++i)
             jre[i] = __builtin_amdgcn_raw_buffer_load_b32(ridx, (uint32_t)(tid + i * NT) * 4u, 0, 0);
-        // all MFMAs done and every gather and index row of this row has
-        // landed: K buffers and ring slots are free; partial sums visible
+        // all MFMAs done and every gather of this row has landed: K buffers
+        // are free; partial sums visible
         lds_barrier();
         auto reduce = [&](int tile) {
             const int slot = (wave * kSlotsPerWave + lane) & (kTile - 1);
@@ -795,8 +844,15 @@ __global__ __launch_bounds__(256, 1) void smla_pipe_kernel(KernelArgs a) {
         if (ntiles >= 2) reduce(ntiles - 2);
         if (ntiles >= 1) reduce(ntiles - 1);
 
-        // the next row's first three tiles
-        if (rn < a.R) start_row(rin, rn);
+        // the next row: Q and lse straight into this row's registers (every
+        // MFMA of this row is done), then its first three tiles (ring slots:
+        // the index rows still in flight into them land before these, in
+        // order); all of it lands while this row is assembled
+        if (rn < a.R) {
+            load_row_q(rln);
+            load_lse(rln);
+            start_row(rin, rn);
+        }
         consume(nk0);
         consume(nk1);
         consume(nk2);
@@ -841,8 +897,6 @@ __global__ __launch_bounds__(256, 1) void smla_pipe_kernel(KernelArgs a) {
         // the next row becomes current
         rc = rn;
         ric = rin;
-#pragma unroll
-        for (int s = 0; s < kChunks / 2; ++s) qa[s] = qn[s];
         set_l2();
     }
 }
