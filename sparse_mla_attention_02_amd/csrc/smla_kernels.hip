@@ -627,13 +627,13 @@ __global__ __launch_bounds__(256, 1) void smla_pipe_kernel(KernelArgs a) {
     __shared__ int32_t kring[4][64];
     __shared__ float red[2][2 * HT][kTile];
     __shared__ float vals[kVcap + 64];
+    __shared__ float lsebuf[HT][64];       // the next row's lse, heads 32w.. in lsebuf[w]
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int half = lane >> 5;
     const int col = lane & 31;
-    const int head = wave * 32 + col;
     // this wave gathers key rows 8w .. 8w+7 of every tile; lane l < 8 holds
     // the index of row 8w + l
     const int my_slot = kSlotsPerWave * wave + (lane & 7);
@@ -642,6 +642,7 @@ __global__ __launch_bounds__(256, 1) void smla_pipe_kernel(KernelArgs a) {
     float* const stage = reinterpret_cast<float*>(kbuf[3]);
     const uint32_t kbuf_lds = lds_addr(kbuf);
     const uint32_t ring_lds = lds_addr(kring);
+    const uint32_t lse_lds = lds_addr(lsebuf);
     const uint32_t voff16 = (uint32_t)lane << 4;
     const uint32_t voff4 = (uint32_t)lane << 2;
 
@@ -650,7 +651,6 @@ __global__ __launch_bounds__(256, 1) void smla_pipe_kernel(KernelArgs a) {
     int64_t rc = row_of(a, 0, blockIdx.x);   // num_wg <= R, so rc < R
     RowInfo ric = decode_row<TND>(a, rc);
     uint4 qa[kChunks / 2];
-    float lse_n[16];
     int32_t nk0, nk1, nk2;                  // next row: index of key row my_slot, tiles 0..2
     int64_t rn = a.R, rln = rc;             // next row, and the row its loads read
     RowInfo rin = ric;
@@ -663,25 +663,36 @@ __global__ __launch_bounds__(256, 1) void smla_pipe_kernel(KernelArgs a) {
         return raw_desc(kbytes + ri.kbase * 1024,
                         bytes > 0xffffffffll ? 0xffffffffu : (uint32_t)(bytes < 0 ? 0 : bytes));
     };
-    auto q_rsrc = [&](int64_t r) { return rsrc(q4 + r * a.G * kChunks, (uint32_t)a.G * 1024u); };
-    const uint32_t qoff = (uint32_t)head * 1024u + (uint32_t)half * 16u;
-    auto load_q = [&](__amdgpu_buffer_rsrc_t rq, uint4* q, int s) {
-        q[s] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rq, qoff + 32u * s,
-                                                                                 0, 2 /* nt */));
+    // Q and lse of a row pass through LDS: loaded as whole 1 KB head rows
+    // (a load of Q straight into the MFMA operand layout would touch 32
+    // head rows per instruction, several times slower through the address
+    // unit), then read back per lane in the operand layout.
+    // Q of row r, heads [h0, h1), into the K buffers (head h -> buffer
+    // h / 32, row h % 32); heads past G read as zero
+    auto stage_q = [&](int64_t r, int h0, int h1) {
+        const i32x4_t qd = raw_desc(q4 + r * a.G * kChunks, (uint32_t)a.G * 1024u);
+        for (int h = h0 + wave; h < h1; h += HT)
+            dma_row(qd, kbuf_lds + (uint32_t)((h >> 5) * kBufBytes + (h & 31) * kRowBytes),
+                    h * 1024, voff16);
     };
-    auto load_lse = [&](int64_t r) {
-        const __amdgpu_buffer_rsrc_t rl = rsrc(a.lse + r * a.G, (uint32_t)a.G * 4u);
+    // lse of row r: heads 32w .. 32w+31 into lsebuf[w][0 .. 31]
+    auto stage_lse = [&](int64_t r) {
+        const i32x4_t ld = raw_desc(a.lse + r * a.G, (uint32_t)a.G * 4u);
+        dma_dword(ld, lse_lds + (uint32_t)(wave * 256), wave * 32 * 4, voff4);
+    };
+    // this wave's Q (MFMA A operands: lane (m, half) holds head 32w + m,
+    // elements 16s + 8 half .. +8 for k-step s) and lse (log2 units; padded
+    // heads get +inf) from LDS
+    float l2[16];
+    auto read_q_lse = [&]() {
+        const uint4* row = kbuf[wave] + col * kPitch + half;
+#pragma unroll
+        for (int s = 0; s < kChunks / 2; ++s) qa[s] = row[2 * s];
 #pragma unroll
         for (int e = 0; e < 16; ++e) {
-            const int h = wave * 32 + 8 * (e >> 2) + 4 * half + (e & 3);
-            lse_n[e] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(
-                                                     rl, (uint32_t)h * 4u, 0, 0));
+            const int hl = 8 * (e >> 2) + 4 * half + (e & 3);
+            l2[e] = wave * 32 + hl < a.G ? lsebuf[wave][hl] * kLog2e : __builtin_inff();
         }
-    };
-    auto load_row_q = [&](int64_t r) {
-        const __amdgpu_buffer_rsrc_t rq = q_rsrc(r);
-#pragma unroll
-        for (int s = 0; s < kChunks / 2; ++s) load_q(rq, qa, s);
     };
     // the next row of this workgroup, decoded, and the gather indices of its
     // tiles 0..2 (kPrefetchOps loads; the decode's scalar loads are waited
@@ -731,24 +742,17 @@ __global__ __launch_bounds__(256, 1) void smla_pipe_kernel(KernelArgs a) {
 
     // ---- first row: operands, then tiles 0..2 in flight
     {
-        load_row_q(rc);
-        load_lse(rc);
+        stage_q(rc, 0, HT * 32);
+        stage_lse(rc);
+        barrier_after_vmcnt(0);
+        read_q_lse();
+        lds_barrier();
         const __amdgpu_buffer_rsrc_t ridx = idx_rsrc(rc);
         nk0 = __builtin_amdgcn_raw_buffer_load_b32(ridx, (uint32_t)(0 * kTile + my_slot) * 4u, 0, 0);
         nk1 = __builtin_amdgcn_raw_buffer_load_b32(ridx, (uint32_t)(1 * kTile + my_slot) * 4u, 0, 0);
         nk2 = __builtin_amdgcn_raw_buffer_load_b32(ridx, (uint32_t)(2 * kTile + my_slot) * 4u, 0, 0);
         start_row(ric, rc);
     }
-    // l2 of the current row: lse_n holds the current row's lse here
-    float l2[16];
-    auto set_l2 = [&]() {
-#pragma unroll
-        for (int e = 0; e < 16; ++e) {
-            const int h = wave * 32 + 8 * (e >> 2) + 4 * half + (e & 3);
-            l2[e] = h < a.G ? lse_n[e] * kLog2e : __builtin_inff();
-        }
-    };
-    set_l2();
 
     for (; it * a.num_wg < a.R && rc < a.R; ++it) {
         const int ntiles = ntiles_of(ric);
@@ -844,18 +848,13 @@ __global__ __launch_bounds__(256, 1) void smla_pipe_kernel(KernelArgs a) {
         if (ntiles >= 2) reduce(ntiles - 2);
         if (ntiles >= 1) reduce(ntiles - 1);
 
-        // the next row: Q and lse straight into this row's registers (every
-        // MFMA of this row is done), then its first three tiles (ring slots:
-        // the index rows still in flight into them land before these, in
-        // order); all of it lands while this row is assembled
-        if (rn < a.R) {
-            load_row_q(rln);
-            load_lse(rln);
-            start_row(rin, rn);
+        // the next row's Q (heads 0..95, into K buffers 0..2) and lse land
+        // while this row is assembled in buffer 3
+        const bool more = rn < a.R;
+        if (more) {
+            stage_q(rln, 0, 3 * 32);
+            stage_lse(rln);
         }
-        consume(nk0);
-        consume(nk1);
-        consume(nk2);
 
         // assemble columns [seg0, seg1) of this row in LDS and write them once
         // (the next tile 0 barrier frees the stage for the next row's tile 3)
@@ -889,15 +888,30 @@ __global__ __launch_bounds__(256, 1) void smla_pipe_kernel(KernelArgs a) {
                 }
             }
         }
-        zero_span(orow, 0, seg0, tid, NT);
-        zero_span(orow, seg1, a.W, tid, NT);
 #pragma unroll
         for (int i = 0; i < kPerThread; ++i) consume(jre[i]);
+
+        // the rest of the next row's Q into buffer 3 once the stage is free;
+        // every wave reads its own heads back, then the K buffers take the
+        // next row's first three tiles (ring slots: the index rows still in
+        // flight into them land before these, in order)
+        if (more) {
+            lds_barrier();
+            stage_q(rln, 3 * 32, HT * 32);
+            barrier_after_vmcnt(0);
+            read_q_lse();
+            lds_barrier();
+            start_row(rin, rn);
+        }
+        consume(nk0);
+        consume(nk1);
+        consume(nk2);
+        zero_span(orow, 0, seg0, tid, NT);
+        zero_span(orow, seg1, a.W, tid, NT);
 
         // the next row becomes current
         rc = rn;
         ric = rin;
-        set_l2();
     }
 }
 
