@@ -23,6 +23,7 @@ does not depend on the values.
 from __future__ import annotations
 
 import argparse
+import hashlib
 import json
 import os
 import sys
@@ -32,6 +33,9 @@ import numpy as np
 
 PEAK_MFMA_TFLOPS = {"bf16": 2500.0, "fp16": 2500.0}   # MI355X dense, published
 PEAK_HBM_GBPS = 8000.0                                  # MI355X HBM3E, published
+KERNELS = {0: "smla_l1norm_kernel", 1: "smla_pipe_kernel"}  # metadata field 24
+HERE = os.path.dirname(os.path.abspath(__file__))
+KERNEL_SOURCE = os.path.join(HERE, "sparse_mla_attention_02_amd", "csrc", "smla_kernels.hip")
 
 
 def log(msg):
@@ -50,6 +54,32 @@ def algorithmic(p):
               + (p.cmp_residual_k.size * 4 if p.cmp_residual_k is not None else 0)
               + p.rows * p.out_width * 4)                   # output, zero-filled
     return flops, float(nbytes), pairs
+
+
+def measured_traffic(kernel, workload):
+    """HBM bytes per launch from the committed rocprofv3 counter summary
+    profiles/<kernel>_<workload>_hbm_traffic.md (FETCH_SIZE + WRITE_SIZE,
+    each scaled by the same counter's reading for a copy of known size), or
+    None when there is none or the kernel source has changed since."""
+    path = os.path.join(HERE, "profiles", f"{kernel}_{workload}_hbm_traffic.md")
+    if not os.path.exists(path):
+        return None
+    fields = {}
+    with open(path) as f:
+        for line in f:
+            line = line.strip().strip("`")
+            if ":" in line and line.split(":", 1)[0] in (
+                    "kernel_source_sha256", "fetch_bytes_per_launch", "write_bytes_per_launch"):
+                k, v = line.split(":", 1)
+                fields[k] = v.strip()
+    with open(KERNEL_SOURCE, "rb") as f:
+        sha = hashlib.sha256(f.read()).hexdigest()
+    if fields.get("kernel_source_sha256") != sha:
+        return None
+    try:
+        return int(fields["fetch_bytes_per_launch"]) + int(fields["write_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
 
 
 def cpu_baseline(p, target_s):
@@ -188,8 +218,9 @@ def main():
     else:
         roof = {"bound": "hbm", "achieved": round(k_gbps, 1), "peak": PEAK_HBM_GBPS,
                 "unit": "GB/s", "frac": round(k_gbps / PEAK_HBM_GBPS, 4)}
-    roof["traffic"] = None
-    roof["kernel"] = "smla_l1norm_kernel"
+    kernel = KERNELS.get(int(md[24]), "unknown")
+    roof["traffic"] = measured_traffic(kernel, p.name)
+    roof["kernel"] = kernel
     roof["kernel_ms"] = round(kms, 4)
     roof["algorithmic_flops"] = flops
     roof["algorithmic_bytes"] = nbytes

@@ -74,7 +74,10 @@ enum { SMLA_MASK_NONE = 0, SMLA_MASK_RIGHT_DOWN_CAUSAL = 3 };
  *   [15] mask_mode, [16] cmp_ratio, [17] R, [18] rows of k (B*S2 or T2),
  *   [19] row order (1 = snake: workgroup w takes rows w, 2C-1-w, 2C+w, ...),
  *   [20] head tiles per row (kernel variant), [21] device, [22] CU count,
- *   [23] resident workgroups per CU; [24..63] zero.
+ *   [23] resident workgroups per CU,
+ *   [24] kernel: 0 = general (one wave per 32-head tile, two workgroups
+ *        per CU), 1 = pipelined (65..128 heads and topk <= 2048: one
+ *        4-wave workgroup per CU, 4 K tiles in flight); [25..63] zero.
  */
 #define SMLA_META_MAGIC 0x534D4C41
 

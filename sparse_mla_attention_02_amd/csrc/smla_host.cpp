@@ -227,6 +227,7 @@ smla_status_t smla_l1norm_metadata(
     m[21] = device;
     m[22] = cus;
     m[23] = per_cu;
+    m[24] = smla::uses_pipe(ht, topk) ? 1 : 0;  // kernel variant
     return ok();
 }
 

@@ -105,7 +105,16 @@ def test_metadata_fields_follow_page_formulas(total, budget):
     assert m[1] * (m[4] - m[3]) + m[2] * m[3] == m[0]
     assert 0 <= m[3] < max(m[4], 1)
     assert m[5] == 0x534D4C41 and m[8] == 128 and m[9] == 1 and m[10] == 512
-    assert (m[24:] == 0).all()
+    assert m[24] == 1                          # 128 heads, topk 2048: pipelined kernel
+    assert (m[25:] == 0).all()
+
+
+@pytest.mark.parametrize("heads,topk,variant", [(128, 2048, 1), (65, 64, 1), (64, 2048, 0),
+                                                (128, 2049, 0), (1, 16, 0)])
+def test_metadata_names_the_kernel_variant(heads, topk, variant):
+    m = meta(num_heads_q=heads, topk=topk).numpy()
+    assert m[24] == variant
+    assert m[20] == (1 if heads <= 32 else 2 if heads <= 64 else 4)
 
 
 def test_metadata_page_example_tnd():
