@@ -134,7 +134,8 @@ smla_status_t smla_l1norm_metadata(
  *                  the page's dense path, which returns SMLA_ERR_UNSUPPORTED).
  *                  Entries index the keys of the row's own batch/sequence
  *                  (0-based, local to a TND sequence); an entry is used iff
- *                  its position is < topk_length, it lies in [0, S2_b) and
+ *                  its position is < the row's entry count (topk_length
+ *                  below), it lies in [0, S2_b) and
  *                  the mask lets the key through. Used entries of one row
  *                  must be distinct (duplicates are not supported).
  *   cu_seqlens_q, cu_seqlens_k  int32 (B+1) device, required for TND
@@ -142,9 +143,10 @@ smla_status_t smla_l1norm_metadata(
  *   cmp_residual_k int32 (B): original key length of batch b is
  *                  S2_b*cmp_ratio + cmp_residual_k[b]; required when
  *                  mask_mode == 3 and cmp_ratio != 1, else may be NULL (0)
- *   topk_length    int32 (B,S1,N2) | (T1,N2): entries per row to look at,
- *                  clamped to [0,K]; required when mask_mode == 0; when NULL
- *                  every entry is looked at
+ *   topk_length    int32 (B,S1,N2) | (T1,N2): entries per row to look at
+ *                  (selectBlockCount), clamped to [0,K]; required when
+ *                  mask_mode == 0; when NULL (mask_mode 3) a row looks at its
+ *                  first min(K, keys visible to it) entries
  *   metadata_host  int32[64] from smla_l1norm_metadata for the same shapes
  *   dtype          SMLA_DTYPE_FP16 or SMLA_DTYPE_BF16
  *   batch_size, seqlen_q, seqlen_k  B,S1,S2 (BSND) | B,T1,T2 (TND)

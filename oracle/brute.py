@@ -41,16 +41,6 @@ def _pieces(p, b, qs, ks):
     scale = float(np.float32(p.softmax_scale))
     S = scale * np.einsum("igd,jd->igj", q, k)               # (s1, G, s2)
 
-    idx = p.sparse_indices.reshape(R, K)[qs].astype(np.int64)
-    if p.topk_length is None:
-        n = np.full(s1, K, dtype=np.int64)
-    else:
-        n = np.clip(p.topk_length.reshape(R)[qs].astype(np.int64), 0, K)
-    counts = np.zeros((s1, s2), dtype=np.float64)
-    take = (np.arange(K)[None, :] < n[:, None]) & (idx >= 0) & (idx < s2)
-    rr, tt = np.nonzero(take)
-    np.add.at(counts, (rr, idx[rr, tt]), 1.0)
-
     if p.mask_mode == 3:
         r = p.cmp_ratio
         res = 0 if p.cmp_residual_k is None else int(p.cmp_residual_k[b])
@@ -59,6 +49,20 @@ def _pieces(p, b, qs, ks):
         vis = kend[None, :] <= qpos1[:, None]
     else:
         vis = np.ones((s1, s2), dtype=bool)
+
+    idx = p.sparse_indices.reshape(R, K)[qs].astype(np.int64)
+    if p.topk_length is None:
+        # selectBlockCount without topk_length: K, or (mask 3) no more than
+        # the number of keys the row sees
+        n = np.full(s1, K, dtype=np.int64)
+        if p.mask_mode == 3:
+            n = np.minimum(n, vis.sum(axis=1))
+    else:
+        n = np.clip(p.topk_length.reshape(R)[qs].astype(np.int64), 0, K)
+    counts = np.zeros((s1, s2), dtype=np.float64)
+    take = (np.arange(K)[None, :] < n[:, None]) & (idx >= 0) & (idx < s2)
+    rr, tt = np.nonzero(take)
+    np.add.at(counts, (rr, idx[rr, tt]), 1.0)
     return S, counts * vis
 
 

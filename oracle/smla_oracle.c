@@ -19,9 +19,11 @@
  * reason in the design notes of the repository):
  *   - indices of a TND sequence are local to that sequence: the k row is
  *     cu_seqlens_k[b] + idx and the output column is cu_seqlens_k[b] + idx;
- *   - an entry t of a row is used iff t < n (n = topk_length clamped to
- *     [0, K], or K when topk_length is absent), 0 <= idx < S2_b, and the key
- *     is visible; other entries contribute nothing;
+ *   - an entry t of a row is used iff t < n, 0 <= idx < S2_b, and the key
+ *     is visible; other entries contribute nothing. n (selectBlockCount) is
+ *     topk_length clamped to [0, K]; without topk_length it is K for mask 0
+ *     and min(K, number of keys visible to the row) for mask 3 (a row cannot
+ *     select more blocks than it sees);
  *   - right-down causal with compression ratio r and residual res: query i of
  *     a sequence with S1_b queries and S2_b compressed keys is at original
  *     position i + S2_b*r + res - S1_b; compressed key j (original positions
@@ -100,8 +102,13 @@ static int visible(const problem* p, const row_info* ri, int64_t j) {
 }
 
 /* number of leading entries of row r that are looked at */
-static int64_t selected_count(const problem* p, int64_t r) {
-    if (!p->topk_len) return p->K;
+static int64_t selected_count(const problem* p, const row_info* ri, int64_t r) {
+    if (!p->topk_len) {
+        if (p->mask_mode == 0) return p->K;
+        int64_t nvis = 0;  /* keys of the row's sequence it can see */
+        for (int64_t j = 0; j < ri->s2; ++j) nvis += visible(p, ri, j);
+        return nvis < p->K ? nvis : p->K;
+    }
     int64_t n = p->topk_len[r];
     if (n < 0) n = 0;
     if (n > p->K) n = p->K;
@@ -166,7 +173,7 @@ int oracle_lse(const float* q_rows, const float* k, const int32_t* idx,
         row_info ri;
         if (decode_row(&p, r, &ri) != 0) { bad |= 1; continue; }
         const float* qrow = q_rows + x * G * D;
-        int64_t n = selected_count(&p, r);
+        int64_t n = selected_count(&p, &ri, r);
         double* s = (double*)malloc(sizeof(double) * (size_t)(n > 0 ? n : 1));
         int32_t used = 0;
         for (int64_t t = 0; t < n; ++t) used += used_key(&p, &ri, r, t) >= 0;
@@ -223,7 +230,7 @@ int oracle_l1norm(const float* q_rows, const float* k, const float* lse_rows,
         const float* qrow = q_rows + x * G * D;
         const float* lse = lse_rows + x * G;
         double* acc = (double*)calloc((size_t)W, sizeof(double));
-        int64_t n = selected_count(&p, r);
+        int64_t n = selected_count(&p, &ri, r);
         for (int64_t t = 0; t < n; ++t) {
             int64_t j = used_key(&p, &ri, r, t);
             if (j < 0) continue;

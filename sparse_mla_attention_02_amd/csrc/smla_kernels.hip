@@ -149,10 +149,14 @@ __device__ __forceinline__ RowInfo decode_row(const KernelArgs& a, int64_t r) {
             if (vis < 0) vis = 0;
         }
     }
+    // entries to look at (selectBlockCount): topk_length clamped to [0, K];
+    // without it K, or under the causal mask no more than the visible keys
     int32_t n = a.K;
     if (a.topk_len) {
         n = uload(a.topk_len, r);
         n = n < 0 ? 0 : (n > a.K ? a.K : n);
+    } else if (a.mask_mode == 3 && vis < n) {
+        n = (int32_t)vis;
     }
     if (vis == 0) n = 0;  // nothing visible: no entry can be used
     RowInfo ri;

@@ -59,7 +59,10 @@ def inject_edges(p, seed=0, invisible=True, out_of_range=True, shorten=True):
       where the row is shortened, put a key beyond the row's causal prefix;
     * out_of_range: an index >= S2_b or a negative non -1 index;
     * shorten: cut topk_length of some rows by 2 (entries past it are left
-      in place and must be ignored).
+      in place and must be ignored);
+    * shadow (no topk_length, mask 3): blank the first entry of a row that
+      sees fewer than K keys and move its key just past the visible count,
+      where the entry count min(K, visible keys) leaves it unused.
     """
     c = clone(p)
     rng = np.random.Generator(np.random.PCG64(seed))
@@ -89,6 +92,10 @@ def inject_edges(p, seed=0, invisible=True, out_of_range=True, shorten=True):
                     tlen[r] = max(n, t + 1)
             elif shorten and 0.5 <= u < 0.7 and tlen is not None and n >= 2:
                 tlen[r] = n - 2
+            elif (0.7 <= u < 0.9 and tlen is None and c.mask_mode == 3 and 0 < L < K
+                  and idx[r, 0] >= 0):
+                idx[r, L] = idx[r, 0]
+                idx[r, 0] = -1
     return c
 
 

@@ -52,6 +52,23 @@ def library_visibility(s1, s2, r, res, mask_mode):
     return clr[:, last]
 
 
+def entry_counts(p):
+    """Per row: how many leading entries are looked at (topk_length clamped
+    to [0, K]; without it K, or under mask 3 min(K, keys visible to the row))."""
+    R, K = p.rows, p.topk
+    tl = None if p.topk_length is None else p.topk_length.reshape(R)
+    n = np.zeros(R, dtype=np.int64)
+    for (b, q0, q1, k0, k1) in C.seq_bounds(p):
+        res = 0 if p.cmp_residual_k is None else int(p.cmp_residual_k[b])
+        vis = library_visibility(q1 - q0, k1 - k0, p.cmp_ratio, res, p.mask_mode)
+        for r in range(q0, q1):
+            if tl is not None:
+                n[r] = min(max(int(tl[r]), 0), K)
+            else:
+                n[r] = K if p.mask_mode == 0 else min(K, int(vis[r - q0].sum()))
+    return n
+
+
 def used_entries(p):
     """Per row: (first k row, first output column, local key ids of the used
     entries in entry order)."""
@@ -64,7 +81,10 @@ def used_entries(p):
         res = 0 if p.cmp_residual_k is None else int(p.cmp_residual_k[b])
         vis = library_visibility(q1 - q0, s2, p.cmp_ratio, res, p.mask_mode)
         for r in range(q0, q1):
-            n = K if tl is None else min(max(int(tl[r]), 0), K)
+            if tl is not None:
+                n = min(max(int(tl[r]), 0), K)
+            else:  # mask 3: no more entries than visible keys
+                n = K if p.mask_mode == 0 else min(K, int(vis[r - q0].sum()))
             js = []
             for t in range(n):
                 j = int(idx[r, t])
@@ -218,9 +238,7 @@ def pin_permutation(orc, problems):
         b = C.clone(a)
         R, K = b.rows, b.topk
         idx = b.sparse_indices.reshape(R, K)
-        tl = None if b.topk_length is None else b.topk_length.reshape(R)
-        for r in range(R):
-            n = K if tl is None else min(max(int(tl[r]), 0), K)
+        for r, n in enumerate(entry_counts(b)):
             idx[r, :n] = idx[r, :n][rng.permutation(n)]
         ob = orc.l1norm(b)
         np.testing.assert_array_equal(o, ob, err_msg=name)

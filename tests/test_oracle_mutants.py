@@ -31,7 +31,8 @@ MUTANTS = {
     "ignore_residual": ("int64_t res = p->cmp_res ? p->cmp_res[ri->b] : 0;",
                         "int64_t res = 0;"),
     "ignore_cmp_ratio": ("int64_t r = p->cmp_ratio;", "int64_t r = 1;"),
-    "ignore_topk_length": ("if (!p->topk_len) return p->K;", "return p->K;"),
+    "ignore_topk_length": ("if (!p->topk_len) {", "if (1) {"),
+    "no_visible_cap": ("return nvis < p->K ? nvis : p->K;", "return p->K;"),
     "lse_no_max_shift": ("lse = m + log(sum);", "lse = log(sum);"),
     "no_mask": ("if (p->mask_mode == 0) return 1;", "return 1;"),
     "s1_for_s2": ("ri->i + 1 + ri->s2 * r + res - ri->s1",
