@@ -77,7 +77,8 @@ enum { SMLA_MASK_NONE = 0, SMLA_MASK_RIGHT_DOWN_CAUSAL = 3 };
  *   [23] resident workgroups per CU,
  *   [24] kernel: 0 = general (one wave per 32-head tile, two workgroups
  *        per CU), 1 = pipelined (65..128 heads and topk <= 2048: one
- *        4-wave workgroup per CU, 4 K tiles in flight); [25..63] zero.
+ *        4-wave workgroup per CU, 64 heads per wave, 64-key tiles);
+ *        [25..63] zero.
  */
 #define SMLA_META_MAGIC 0x534D4C41
 

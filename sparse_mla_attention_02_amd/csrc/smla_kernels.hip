@@ -465,27 +465,14 @@ __global__ __launch_bounds__(64 * HT, 2) void smla_l1norm_kernel(KernelArgs a) {
 }
 
 // ---------------------------------------------------------------------------
-// Pipelined kernel for rows of 65..128 heads with at most kVcap indices.
+// Helpers of the pipelined kernel below.
 //
-// One workgroup of 4 waves per CU: one wave per SIMD, so each wave has the
-// whole register file (Q of the current and of the next row, a deep operand
-// read-ahead) and the workgroup has all of LDS: four K tiles. The gather of
-// tile t+3 is spread over the MFMAs of tile t, so three tiles of compute
-// cover its latency. A barrier per tile publishes the gathered tile and frees
-// the oldest buffer; before it each wave waits only for its own loads of
-// that tile (vmcnt = the loads it issued after them), never for later ones.
-// The next row's Q is loaded in chunks spread over nine tiles. At the end
-// of a row the next row's first three gathers are issued before this row's
-// LDS assembly, which uses the fourth buffer as its stage, so the pipeline
-// does not drain between rows.
-//
-// With one wave per SIMD, every instruction of a wave is issued in the time
-// of the MFMAs, so the tile body is laid out by hand: each k-step holds one
-// MFMA, one operand read, at most two independent VALU instructions of the
-// previous tile's epilogue, and every fourth step one gathered key row.
+// One wave per SIMD issues every instruction in the time of the MFMAs, so
+// its tile body is laid out by hand (scheduling barriers per k-step, empty
+// asm statements that keep arithmetic in its step).
 //
 // All loads into LDS are inline assembly: the compiler's wait-count
-// tracking cannot follow LDS slots reused across loop iterations and would
+// tracking cannot follow LDS buffers reused across loop iterations and would
 // otherwise wait for every load in flight before any LDS read. Their
 // completion is waited for explicitly, by the barrier that counts them.
 
@@ -501,13 +488,7 @@ __device__ __forceinline__ void waitcnt_vm_lgkm0() {
 __device__ __forceinline__ void barrier_after_vmcnt(int n) {
     switch (n) {
         // the counts the pipelined kernel produces; anything else waits for all
-        case 2: waitcnt_vm_lgkm0<2>(); break;
-        case 5: waitcnt_vm_lgkm0<5>(); break;
-        case 10: waitcnt_vm_lgkm0<10>(); break;
-        case 13: waitcnt_vm_lgkm0<13>(); break;
-        case 18: waitcnt_vm_lgkm0<18>(); break;
-        case 21: waitcnt_vm_lgkm0<21>(); break;
-        case 63: waitcnt_vm_lgkm0<63>(); break;
+        case 8: waitcnt_vm_lgkm0<8>(); break;
         default: waitcnt_vm_lgkm0<0>(); break;
     }
     asm volatile("s_barrier" ::: "memory");
@@ -562,306 +543,313 @@ __device__ __forceinline__ void dma_dword(i32x4_t desc, uint32_t m0, int32_t sof
         : "memory", "m0");
 }
 
-constexpr int kBufBytes = kTile * kPitch * 16;  // one K tile in LDS
 constexpr int kRowBytes = kPitch * 16;          // one key row in LDS
 
-// One tile on the pipelined path. Step s: MFMA s; LDS read of the B operand
-// of step s + kLead; epilogue of the previous tile, head e = s/2: FMA at
-// step 2e, exp at 2e+1, added to the sum at 2e+2; key row i of this wave's
-// share of tile t+3 (GATHER): row offset read at step 4i, load at 4i+2;
-// `mid(s)` for the caller's own spread-out work.
-template <bool BF16, bool GATHER, typename Mid>
-__device__ __forceinline__ f32x16_t qk_tile_seq(const uint4* __restrict__ src, const uint4* qa,
-                                                int col, int half, const f32x16_t& prev,
-                                                const float* l2, float c, float* prev_sum,
-                                                i32x4_t kdesc, uint32_t m0_rows, int32_t rows_off,
-                                                uint32_t voff, Mid mid) {
+// ---------------------------------------------------------------------------
+// Wide pipelined kernel for rows of 65..128 heads with at most kVcap indices.
+//
+// LDS delivers 128 bytes per clock per CU: one 1 KB K-operand read per
+// 32-cycle MFMA on each of the four SIMDs already uses all of it, before the
+// gathers write into LDS. So each wave here takes 64 heads (two 32-row MFMA
+// blocks that share every K operand read) by 32 keys, and the four waves of
+// the workgroup cover 128 heads by a 64-key tile: wave w takes heads
+// 64 (w & 1) .. +63 and keys 32 (w >> 1) .. +31 of each tile. Two tiles live
+// in LDS; the gather of tile t+1 (16 rows per wave, loaded straight into
+// LDS) is spread over the first half of the MFMAs of tile t. The row's index
+// list sits in LDS (double-buffered: the next row's list is loaded during
+// this row), so the tile loop reads no other global memory.
+
+constexpr int kWideKeys = 64;                      // keys per tile
+constexpr int kWideBufBytes = kWideKeys * kRowBytes;
+
+// One 64-key tile of one wave: step s issues the two MFMAs of k-step s (one
+// shared B operand), the LDS read of the operand of step s + kLead, one
+// element of the previous tile's epilogue in three independent pieces (FMA
+// of element s, exp of element s-1, sum of element s-2), and for s = 1..16
+// the load of gathered row s-1 of tile t+1 (its row offset read one step
+// earlier) to LDS address m0_rows + (s-1) m0_step (a step of 0 sends a tile
+// that has nothing to gather to one dummy row); `mid(s)` is the caller's
+// spread-out work.
+template <bool BF16, typename Mid>
+__device__ __forceinline__ void qk_tile_wide(const uint4* __restrict__ src, const uint4* qa0,
+                                             const uint4* qa1, int col, int half,
+                                             const f32x16_t& prev0, const f32x16_t& prev1,
+                                             const float* l2, float c, float* prev_sum,
+                                             i32x4_t kdesc, uint32_t m0_rows, uint32_t m0_step,
+                                             int32_t rows_off, uint32_t voff, Mid mid,
+                                             f32x16_t& acc0, f32x16_t& acc1) {
     constexpr int kSteps = kChunks / 2;
     constexpr int kLead = 8;
     const uint4* row = src + col * kPitch + half;
     uint4 b[kSteps];
 #pragma unroll
     for (int s = 0; s < kLead; ++s) b[s] = row[2 * s];
-    f32x16_t acc = {};
+    acc0 = f32x16_t{};
+    acc1 = f32x16_t{};
     float sum = 0.0f, t = 0.0f, ex = 0.0f;
     int32_t soff = 0;
+    int32_t m0 = (int32_t)m0_rows;
+    pin_s(m0);
 #pragma unroll
     for (int s = 0; s < kSteps; ++s) {
         __builtin_amdgcn_sched_barrier(0);
-        acc = mfma_32x32x16<BF16>(qa[s], b[s], acc);
+        acc0 = mfma_32x32x16<BF16>(qa0[s], b[s], acc0);
+        acc1 = mfma_32x32x16<BF16>(qa1[s], b[s], acc1);
         if (s + kLead < kSteps) b[s + kLead] = row[2 * (s + kLead)];
-        if ((s & 1) == 0) {
-            if (s >= 2) {
-                sum += ex;
-                pin(sum);
-            }
-            t = __builtin_fmaf(prev[s >> 1], c, -l2[s >> 1]);
-            pin(t);
-        } else {
+        if (s >= 2) {
+            sum += ex;
+            pin(sum);
+        }
+        if (s >= 1) {
             ex = __builtin_amdgcn_exp2f(t);
             pin(ex);
         }
-        if constexpr (GATHER) {
-            if ((s & 3) == 0) {
-                soff = __builtin_amdgcn_readlane(rows_off, s >> 2);
-                pin_s(soff);
-            } else if ((s & 3) == 2) {
-                dma_row(kdesc, m0_rows + (uint32_t)((s >> 2) * kRowBytes), soff, voff);
-            }
+        t = __builtin_fmaf(s < 16 ? prev0[s] : prev1[s - 16], c, -l2[s]);
+        pin(t);
+        if (s >= 1 && s <= 16) {
+            dma_row(kdesc, (uint32_t)m0, soff, voff);
+            m0 += (int32_t)m0_step;
+            pin_s(m0);
+        }
+        if (s < 16) {
+            soff = __builtin_amdgcn_readlane(rows_off, s);
+            pin_s(soff);
         }
         mid(s);
     }
     __builtin_amdgcn_sched_barrier(0);
+    sum += ex;
+    ex = __builtin_amdgcn_exp2f(t);
     *prev_sum = sum + ex;
-    return acc;
 }
 
 template <bool BF16, bool TND>
-__global__ __launch_bounds__(256, 1) void smla_pipe_kernel(KernelArgs a) {
+__global__ __launch_bounds__(256, 1) void smla_wide_kernel(KernelArgs a) {
     constexpr int HT = 4;
     constexpr int NT = 256;
     constexpr int kPerThread = kVcap / NT;
-    constexpr int kSlotsPerWave = kTile / HT;
-    // mid-row prefetch of the next row: the gather indices of its tiles 0..2
-    constexpr int kPrefetchOps = 3;
-    // K tiles (tile t in buffer t % 4; the last one doubles as the row stage)
-    __shared__ uint4 kbuf[4][kTile * kPitch];
-    // index rows: slot t % 4 holds the indices of tile t (lanes 0..31) and of
-    // tile t+1 (32..63, unused)
-    __shared__ int32_t kring[4][64];
-    __shared__ float red[2][2 * HT][kTile];
-    __shared__ float vals[kVcap + 64];
-    __shared__ float lsebuf[HT][64];       // the next row's lse, heads 32w.. in lsebuf[w]
+    constexpr int kRowsPerWave = kWideKeys / HT;      // gathered rows per wave and tile
+    constexpr int kIdxOps = kVcap / 64 / HT;          // loads of one index list per wave
+    __shared__ uint4 kbuf[2][kWideKeys * kPitch];     // tile t in buffer t % 2
+    __shared__ int32_t ibuf[2][kVcap];                // index lists: this row, next row
+    __shared__ float red[2][4][kWideKeys];            // partial sums, last two tiles
+    __shared__ float vals[kVcap + 64];                // the row's values by entry; then a sink
+    __shared__ float lsebuf[HT * 32];                 // the next row's lse
+    __shared__ uint4 dummy[64];                       // loads of a tile with nothing to gather
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int hg = wave & 1;          // head group: heads 64 hg .. 64 hg + 63
+    const int kh = wave >> 1;         // key half: keys 32 kh .. 32 kh + 31 of a tile
     const int half = lane >> 5;
     const int col = lane & 31;
-    // this wave gathers key rows 8w .. 8w+7 of every tile; lane l < 8 holds
-    // the index of row 8w + l
-    const int my_slot = kSlotsPerWave * wave + (lane & 7);
+    // this wave gathers rows 16 w .. 16 w + 15 of every tile; lane l < 16
+    // holds the index of row 16 w + l
+    const int my_slot = kRowsPerWave * wave + (lane & 15);
     const uint4* __restrict__ q4 = static_cast<const uint4*>(a.q);
     const char* __restrict__ kbytes = static_cast<const char*>(a.k);
-    float* const stage = reinterpret_cast<float*>(kbuf[3]);
+    float* const stage = reinterpret_cast<float*>(kbuf[1]);
     const uint32_t kbuf_lds = lds_addr(kbuf);
-    const uint32_t ring_lds = lds_addr(kring);
+    const uint32_t ibuf_lds = lds_addr(ibuf);
     const uint32_t lse_lds = lds_addr(lsebuf);
+    const uint32_t dummy_lds = lds_addr(dummy);
     const uint32_t voff16 = (uint32_t)lane << 4;
     const uint32_t voff4 = (uint32_t)lane << 2;
 
-    // ---- state of the current row (c*) and of the prefetched next row (n*)
     int64_t it = 0;
     int64_t rc = row_of(a, 0, blockIdx.x);   // num_wg <= R, so rc < R
     RowInfo ric = decode_row<TND>(a, rc);
-    uint4 qa[kChunks / 2];
-    int32_t nk0, nk1, nk2;                  // next row: index of key row my_slot, tiles 0..2
+    uint4 qa0[kChunks / 2], qa1[kChunks / 2];
+    float l2[32];
     int64_t rn = a.R, rln = rc;             // next row, and the row its loads read
     RowInfo rin = ric;
+    int ib = 0;                             // ibuf slot of the current row
 
-    auto idx_rsrc = [&](int64_t r) { return rsrc(a.idx + r * a.K, (uint32_t)a.K * 4u); };
-    auto idx_desc = [&](int64_t r) { return raw_desc(a.idx + r * a.K, (uint32_t)a.K * 4u); };
     auto k_desc = [&](const RowInfo& ri) {
         const int64_t rows = a.rows_k - ri.kbase;
         const int64_t bytes = rows * 1024;
         return raw_desc(kbytes + ri.kbase * 1024,
                         bytes > 0xffffffffll ? 0xffffffffu : (uint32_t)(bytes < 0 ? 0 : bytes));
     };
-    // Q and lse of a row pass through LDS: loaded as whole 1 KB head rows
-    // (a load of Q straight into the MFMA operand layout would touch 32
-    // head rows per instruction, several times slower through the address
-    // unit), then read back per lane in the operand layout.
-    // Q of row r, heads [h0, h1), into the K buffers (head h -> buffer
-    // h / 32, row h % 32); heads past G read as zero
+    // row r's index list into ibuf[slot] (kIdxOps loads; entries past K read
+    // as zero)
+    auto load_idx_row = [&](int64_t r, int slot) {
+        const i32x4_t id = raw_desc(a.idx + r * a.K, (uint32_t)a.K * 4u);
+#pragma unroll
+        for (int i = 0; i < kIdxOps; ++i) {
+            const int c = kIdxOps * wave + i;  // 256-byte piece of the list
+            dma_dword(id, ibuf_lds + (uint32_t)(slot * kVcap * 4 + c * 256), c * 256, voff4);
+        }
+    };
+    // Q and lse pass through LDS as whole rows (a load straight into the MFMA
+    // operand layout touches 32 head rows per instruction and is several
+    // times slower through the address unit). Q of row r, heads [h0, h1),
+    // into the K buffers: head h -> buffer h / 64, row h % 64.
     auto stage_q = [&](int64_t r, int h0, int h1) {
         const i32x4_t qd = raw_desc(q4 + r * a.G * kChunks, (uint32_t)a.G * 1024u);
         for (int h = h0 + wave; h < h1; h += HT)
-            dma_row(qd, kbuf_lds + (uint32_t)((h >> 5) * kBufBytes + (h & 31) * kRowBytes),
+            dma_row(qd, kbuf_lds + (uint32_t)((h >> 6) * kWideBufBytes + (h & 63) * kRowBytes),
                     h * 1024, voff16);
     };
-    // lse of row r: heads 32w .. 32w+31 into lsebuf[w][0 .. 31]
     auto stage_lse = [&](int64_t r) {
         const i32x4_t ld = raw_desc(a.lse + r * a.G, (uint32_t)a.G * 4u);
-        dma_dword(ld, lse_lds + (uint32_t)(wave * 256), wave * 32 * 4, voff4);
+        if (wave < 2)  // 2 x 64 heads
+            dma_dword(ld, lse_lds + (uint32_t)(wave * 256), wave * 256, voff4);
     };
-    // this wave's Q (MFMA A operands: lane (m, half) holds head 32w + m,
-    // elements 16s + 8 half .. +8 for k-step s) and lse (log2 units; padded
-    // heads get +inf) from LDS
-    float l2[16];
+    // this wave's Q (A operands of block j: lane (m, half) holds head
+    // 64 hg + 32 j + m, elements 16s + 8 half .. +8 of k-step s) and its lse
+    // in log2 units (padded heads +inf), from LDS
     auto read_q_lse = [&]() {
-        const uint4* row = kbuf[wave] + col * kPitch + half;
+        const uint4* r0 = kbuf[hg] + col * kPitch + half;
+        const uint4* r1 = kbuf[hg] + (32 + col) * kPitch + half;
 #pragma unroll
-        for (int s = 0; s < kChunks / 2; ++s) qa[s] = row[2 * s];
+        for (int s = 0; s < kChunks / 2; ++s) {
+            qa0[s] = r0[2 * s];
+            qa1[s] = r1[2 * s];
+        }
 #pragma unroll
-        for (int e = 0; e < 16; ++e) {
-            const int hl = 8 * (e >> 2) + 4 * half + (e & 3);
-            l2[e] = wave * 32 + hl < a.G ? lsebuf[wave][hl] * kLog2e : __builtin_inff();
+        for (int e = 0; e < 32; ++e) {
+            const int h = 64 * hg + 32 * (e >> 4) + 8 * ((e & 15) >> 2) + 4 * half + (e & 3);
+            l2[e] = h < a.G ? lsebuf[h] * kLog2e : __builtin_inff();
         }
     };
-    // the next row of this workgroup, decoded, and the gather indices of its
-    // tiles 0..2 (kPrefetchOps loads; the decode's scalar loads are waited
-    // for here, so that later LDS waits can count)
+    // the next row of this workgroup, decoded (its scalar loads waited for
+    // here, so that later LDS waits can count), and its index list
     auto prefetch_next = [&]() {
         rn = (it + 1) * a.num_wg < a.R ? row_of(a, it + 1, blockIdx.x) : a.R;
         rln = rn < a.R ? rn : rc;  // the last row loads itself again (unused)
         rin = decode_row<TND>(a, rln);
         waitcnt_vm_lgkm0<63>();
-        const __amdgpu_buffer_rsrc_t ridx = idx_rsrc(rln);
-        nk0 = __builtin_amdgcn_raw_buffer_load_b32(ridx, (uint32_t)(0 * kTile + my_slot) * 4u, 0, 0);
-        nk1 = __builtin_amdgcn_raw_buffer_load_b32(ridx, (uint32_t)(1 * kTile + my_slot) * 4u, 0, 0);
-        nk2 = __builtin_amdgcn_raw_buffer_load_b32(ridx, (uint32_t)(2 * kTile + my_slot) * 4u, 0, 0);
+        load_idx_row(rln, ib ^ 1);
     };
-    auto ntiles_of = [](const RowInfo& ri) { return (ri.n + kTile - 1) / kTile; };
+    auto ntiles_of = [](const RowInfo& ri) { return (ri.n + kWideKeys - 1) / kWideKeys; };
     // byte offset of the key row of slot my_slot of `tile` holding raw index
     // j: j's row if the entry is used, else row 0 (loaded, never read)
     auto row_off = [&](const RowInfo& ri, int tile, int32_t j) -> int32_t {
-        return (tile * kTile + my_slot < ri.n && (uint32_t)j < (uint32_t)ri.vis) ? (j << 10) : 0;
+        return (tile * kWideKeys + my_slot < ri.n && (uint32_t)j < (uint32_t)ri.vis) ? (j << 10)
+                                                                                       : 0;
     };
-    // a row's first three gathers and the index rows of its tiles 3..5
-    auto start_row = [&](const RowInfo& ri, int64_t r) {
+    // a row's first tile into buffer 0 (its index list is in ibuf[slot])
+    auto start_row = [&](const RowInfo& ri, int slot) {
+        if (ntiles_of(ri) == 0) return;
         const i32x4_t kd = k_desc(ri);
-        const int nt = ntiles_of(ri);
-        const int32_t o0 = row_off(ri, 0, nk0), o1 = row_off(ri, 1, nk1), o2 = row_off(ri, 2, nk2);
-        const uint32_t m0w = kbuf_lds + (uint32_t)(kSlotsPerWave * wave * kRowBytes);
+        const int32_t o = row_off(ri, 0, ibuf[slot][my_slot]);
+        int32_t so[kRowsPerWave];
 #pragma unroll
-        for (int k = 0; k < 3; ++k) {
-            if (nt > k) {
-                const int32_t o = k == 0 ? o0 : (k == 1 ? o1 : o2);
-                int32_t so[kSlotsPerWave];
-#pragma unroll
-                for (int i = 0; i < kSlotsPerWave; ++i) {
-                    so[i] = __builtin_amdgcn_readlane(o, i);
-                    pin_s(so[i]);
-                }
-#pragma unroll
-                for (int i = 0; i < kSlotsPerWave; ++i)
-                    dma_row(kd, m0w + (uint32_t)(k * kBufBytes + i * kRowBytes), so[i], voff16);
-            }
+        for (int i = 0; i < kRowsPerWave; ++i) {
+            so[i] = __builtin_amdgcn_readlane(o, i);
+            pin_s(so[i]);
         }
-        const i32x4_t id = idx_desc(r);
-        dma_dword(id, ring_lds + 3u * 256u, 3 * kTile * 4, voff4);
-        dma_dword(id, ring_lds + 0u * 256u, 4 * kTile * 4, voff4);
-        dma_dword(id, ring_lds + 1u * 256u, 5 * kTile * 4, voff4);
+        int32_t m0 = (int32_t)(kbuf_lds + (uint32_t)(kRowsPerWave * wave * kRowBytes));
+        pin_s(m0);
+#pragma unroll
+        for (int i = 0; i < kRowsPerWave; ++i) {
+            dma_row(kd, (uint32_t)m0, so[i], voff16);
+            m0 += kRowBytes;
+            pin_s(m0);
+        }
     };
 
-    // ---- first row: operands, then tiles 0..2 in flight
-    {
-        stage_q(rc, 0, HT * 32);
-        stage_lse(rc);
-        barrier_after_vmcnt(0);
-        read_q_lse();
-        lds_barrier();
-        const __amdgpu_buffer_rsrc_t ridx = idx_rsrc(rc);
-        nk0 = __builtin_amdgcn_raw_buffer_load_b32(ridx, (uint32_t)(0 * kTile + my_slot) * 4u, 0, 0);
-        nk1 = __builtin_amdgcn_raw_buffer_load_b32(ridx, (uint32_t)(1 * kTile + my_slot) * 4u, 0, 0);
-        nk2 = __builtin_amdgcn_raw_buffer_load_b32(ridx, (uint32_t)(2 * kTile + my_slot) * 4u, 0, 0);
-        start_row(ric, rc);
-    }
+    // ---- first row: operands and index list, then tile 0 in flight
+    load_idx_row(rc, 0);
+    stage_q(rc, 0, HT * 32);
+    stage_lse(rc);
+    barrier_after_vmcnt(0);
+    read_q_lse();
+    lds_barrier();
+    start_row(ric, 0);
 
     for (; it * a.num_wg < a.R && rc < a.R; ++it) {
         const int ntiles = ntiles_of(ric);
-        // the tile after whose MFMAs the next row is prefetched
-        const int pf = ntiles > 3 ? 2 : ntiles - 1;
-        auto extra = [&](int u) -> int { return u == pf ? kPrefetchOps : 0; };
+        // the tile after whose MFMAs the next row's index list is loaded
+        const int pf = ntiles > 2 ? 1 : ntiles - 1;
         float* __restrict__ orow = a.out + rc * a.W;
-        const __amdgpu_buffer_rsrc_t ridx = idx_rsrc(rc);
-        const i32x4_t idesc = idx_desc(rc);
         const i32x4_t kdesc = k_desc(ric);
         const int64_t seg0 = ric.col0;
         const int64_t seg1 = ric.col0 + (ntiles > 0 ? ric.vis : 0);
+        const int32_t* __restrict__ irow = ibuf[ib];
 
         if (ntiles == 0) prefetch_next();
 
-        f32x16_t acc_prev = {};
-        // One tile: barrier; index row of tile+3 from the ring, of tile+6
-        // into it; tile-2's head-tile sums (read now, added over steps
-        // 1..7, stored at 8); the gather of tile+3 spread over the MFMAs of
-        // this tile; tile-1's epilogue.
-        auto body = [&](auto gtag, int tile) {
-            constexpr bool kGather = decltype(gtag)::value;
-            // Loads issued after the gather of this tile (in tile-3; vector
-            // memory returns in order): index row and gather of tiles -2 and
-            // -1, and the prefetch if it came after. Tile 0 waits for
-            // everything (the previous row's stores and this row's Q
-            // included); tiles 1 and 2 were gathered before that wait.
-            int later = 63;
-            if (tile == 0) {
-                later = 0;
-            } else if (tile >= 3) {
-                later = extra(tile - 3) + 2 + 8 * (tile + 1 < ntiles) + 8 * (tile + 2 < ntiles) +
-                        extra(tile - 2) + extra(tile - 1);
-                later = later > 63 ? 63 : later;
-            }
+        f32x16_t prev0 = {}, prev1 = {};
+        auto body = [&](int tile) {
+            const bool gather = tile + 1 < ntiles;
+            // Loads issued after the gather of this tile (in tile-1; vector
+            // memory returns in order): the next row's index list if it came
+            // after. Tile 0 waits for everything (the previous row's stores
+            // included).
+            const int later = tile == 0 ? 0 : (tile - 1 == pf ? kIdxOps : 0);
             barrier_after_vmcnt(later);
-            const int32_t key = kring[(tile + 3) & 3][my_slot];
-            dma_dword(idesc, ring_lds + (uint32_t)(((tile + 2) & 3) * 256), (tile + 6) * kTile * 4,
-                      voff4);
-            const int slot = (wave * kSlotsPerWave + lane) & (kTile - 1);
+            const int32_t key = gather ? irow[(tile + 1) * kWideKeys + my_slot] : 0;
+            const int32_t rows_off = row_off(ric, tile + 1, key);
+            const int slot = (kRowsPerWave * wave + lane) & (kWideKeys - 1);
             const int pb = tile & 1;  // parity of tile - 2
-            float parts[2 * HT];
+            float parts[4];
 #pragma unroll
-            for (int w = 0; w < 2 * HT; ++w) parts[w] = red[pb][w][slot];
-            const int32_t rows_off = row_off(ric, tile + 3, key);
-            const uint32_t m0_rows = kbuf_lds + (uint32_t)(((tile + 3) & 3) * kBufBytes +
-                                                           kSlotsPerWave * wave * kRowBytes);
+            for (int p = 0; p < 4; ++p) parts[p] = red[pb][p][slot];
+            const uint32_t m0_rows =
+                gather ? kbuf_lds + (uint32_t)(((tile + 1) & 1) * kWideBufBytes +
+                                               kRowsPerWave * wave * kRowBytes)
+                       : dummy_lds;
+            const uint32_t m0_step = gather ? (uint32_t)kRowBytes : 0u;
             float tot = 0.0f;
             float sum_prev;
-            const f32x16_t acc = qk_tile_seq<BF16, kGather>(
-                kbuf[tile & 3], qa, col, half, acc_prev, l2, a.c_scale, &sum_prev, kdesc, m0_rows,
-                rows_off, voff16, [&](int s) {
-                    if (s == 1) {
+            f32x16_t acc0, acc1;
+            qk_tile_wide<BF16>(
+                kbuf[tile & 1] + 32 * kh * kPitch, qa0, qa1, col, half, prev0, prev1, l2,
+                a.c_scale, &sum_prev, kdesc, m0_rows, m0_step, rows_off, voff16,
+                [&](int s) {
+                    if (s == 2) {
                         tot = parts[0] + parts[1];
                         pin(tot);
-                    } else if (s >= 2 && s < 2 * HT) {
-                        tot += parts[s];
+                    } else if (s == 3) {
+                        tot += parts[2];
                         pin(tot);
-                    } else if (s == 2 * HT) {
-                        const bool mine = lane < kSlotsPerWave && tile >= 2;
-                        vals[mine ? (tile - 2) * kTile + slot : kVcap + lane] = tot * a.inv_g;
+                    } else if (s == 4) {
+                        tot += parts[3];
+                        pin(tot);
+                    } else if (s == 5) {
+                        const bool mine = lane < kRowsPerWave && tile >= 2;
+                        vals[mine ? (tile - 2) * kWideKeys + slot : kVcap + lane] = tot * a.inv_g;
                     }
-                });
-            red[(tile - 1) & 1][2 * wave + half][col] = sum_prev;  // tile 0: unused slot
-            acc_prev = acc;
+                },
+                acc0, acc1);
+            red[(tile - 1) & 1][2 * hg + half][32 * kh + col] = sum_prev;  // tile 0: unused
+            prev0 = acc0;
+            prev1 = acc1;
         };
-        using G1 = std::integral_constant<bool, true>;
-        using G0 = std::integral_constant<bool, false>;
         for (int tile = 0; tile < ntiles; ++tile) {
-            if (tile + 3 < ntiles) body(G1{}, tile); else body(G0{}, tile);
+            body(tile);
             if (tile == pf) prefetch_next();
         }
         if (ntiles > 0)
-            red[(ntiles - 1) & 1][2 * wave + half][col] = head_sum(acc_prev, l2, a.c_scale);
+            red[(ntiles - 1) & 1][2 * hg + half][32 * kh + col] =
+                head_sum(prev0, l2, a.c_scale) + head_sum(prev1, l2 + 16, a.c_scale);
 
-        // indices for this row's assembly
-        int32_t jre[kPerThread];
-#pragma unroll
-        for (int i = 0; i < kPerThread; ++i)
-            jre[i] = __builtin_amdgcn_raw_buffer_load_b32(ridx, (uint32_t)(tid + i * NT) * 4u, 0, 0);
         // all MFMAs done and every gather of this row has landed: K buffers
         // are free; partial sums visible
         lds_barrier();
         auto reduce = [&](int tile) {
-            const int slot = (wave * kSlotsPerWave + lane) & (kTile - 1);
+            const int slot = (kRowsPerWave * wave + lane) & (kWideKeys - 1);
             const int pb = tile & 1;
-            float tot = red[pb][0][slot];
-#pragma unroll
-            for (int w = 1; w < 2 * HT; ++w) tot += red[pb][w][slot];
-            const bool mine = lane < kSlotsPerWave;
-            vals[mine ? tile * kTile + slot : kVcap + lane] = tot * a.inv_g;
+            const float tot = red[pb][0][slot] + red[pb][1][slot] + red[pb][2][slot] +
+                              red[pb][3][slot];
+            const bool mine = lane < kRowsPerWave;
+            vals[mine ? tile * kWideKeys + slot : kVcap + lane] = tot * a.inv_g;
         };
         if (ntiles >= 2) reduce(ntiles - 2);
         if (ntiles >= 1) reduce(ntiles - 1);
 
-        // the next row's Q (heads 0..95, into K buffers 0..2) and lse land
-        // while this row is assembled in buffer 3
+        // the next row's Q (heads 0..63, into buffer 0) and lse land while
+        // this row is assembled in buffer 1
         const bool more = rn < a.R;
         if (more) {
-            stage_q(rln, 0, 3 * 32);
+            stage_q(rln, 0, 64);
             stage_lse(rln);
         }
 
         // assemble columns [seg0, seg1) of this row in LDS and write them once
-        // (the next tile 0 barrier frees the stage for the next row's tile 3)
         for (int64_t c0 = seg0; c0 < seg1; c0 += kStage - 4) {
             const int64_t len = (seg1 - c0 < kStage - 4) ? seg1 - c0 : kStage - 4;
             const int m0 = (int)((rc * a.W + c0) & 3);
@@ -872,7 +860,7 @@ __global__ __launch_bounds__(256, 1) void smla_pipe_kernel(KernelArgs a) {
 #pragma unroll
             for (int i = 0; i < kPerThread; ++i) {
                 const int t = tid + i * NT;
-                const int32_t j = jre[i];
+                const int32_t j = irow[t];
                 if (t < ric.n && (uint32_t)j < (uint32_t)ric.vis) {
                     const int64_t c = ric.col0 + j - c0;
                     if (c >= 0 && c < len) stage[c + m0] = vals[t];
@@ -892,43 +880,38 @@ __global__ __launch_bounds__(256, 1) void smla_pipe_kernel(KernelArgs a) {
                 }
             }
         }
-#pragma unroll
-        for (int i = 0; i < kPerThread; ++i) consume(jre[i]);
 
-        // the rest of the next row's Q into buffer 3 once the stage is free;
-        // every wave reads its own heads back, then the K buffers take the
-        // next row's first three tiles (ring slots: the index rows still in
-        // flight into them land before these, in order)
+        // the rest of the next row's Q into buffer 1 once the stage is free;
+        // every wave reads its heads back, then buffer 0 takes the next
+        // row's first tile
         if (more) {
             lds_barrier();
-            stage_q(rln, 3 * 32, HT * 32);
+            stage_q(rln, 64, HT * 32);
             barrier_after_vmcnt(0);
             read_q_lse();
             lds_barrier();
-            start_row(rin, rn);
+            start_row(rin, ib ^ 1);
         }
-        consume(nk0);
-        consume(nk1);
-        consume(nk2);
         zero_span(orow, 0, seg0, tid, NT);
         zero_span(orow, seg1, a.W, tid, NT);
 
         // the next row becomes current
         rc = rn;
         ric = rin;
+        ib ^= 1;
     }
 }
 
 template <bool BF16, bool TND>
-hipError_t launch_pipe_t(const KernelArgs& a, hipStream_t stream) {
-    hipLaunchKernelGGL((smla_pipe_kernel<BF16, TND>), dim3(a.num_wg), dim3(256), 0, stream, a);
+hipError_t launch_wide_t(const KernelArgs& a, hipStream_t stream) {
+    hipLaunchKernelGGL((smla_wide_kernel<BF16, TND>), dim3(a.num_wg), dim3(256), 0, stream, a);
     return hipGetLastError();
 }
 
 template <bool BF16, bool TND>
-hipError_t occupancy_pipe_t(int* out) {
+hipError_t occupancy_wide_t(int* out) {
     return hipOccupancyMaxActiveBlocksPerMultiprocessor(
-        out, reinterpret_cast<const void*>(&smla_pipe_kernel<BF16, TND>), 256, 0);
+        out, reinterpret_cast<const void*>(&smla_wide_kernel<BF16, TND>), 256, 0);
 }
 
 template <int HT, bool BF16, bool TND>
@@ -973,16 +956,16 @@ bool uses_pipe(int ht, int64_t topk) { return ht == 4 && topk <= kVcap; }
 
 hipError_t launch(const KernelArgs& a, int ht, bool bf16, bool tnd, hipStream_t stream) {
     if (uses_pipe(ht, a.K)) {
-        if (bf16) return tnd ? launch_pipe_t<true, true>(a, stream) : launch_pipe_t<true, false>(a, stream);
-        return tnd ? launch_pipe_t<false, true>(a, stream) : launch_pipe_t<false, false>(a, stream);
+        if (bf16) return tnd ? launch_wide_t<true, true>(a, stream) : launch_wide_t<true, false>(a, stream);
+        return tnd ? launch_wide_t<false, true>(a, stream) : launch_wide_t<false, false>(a, stream);
     }
     SMLA_DISPATCH(launch_t, a, stream);
 }
 
 hipError_t resident_per_cu(int ht, bool bf16, bool tnd, int64_t topk, int* out) {
     if (uses_pipe(ht, topk)) {
-        if (bf16) return tnd ? occupancy_pipe_t<true, true>(out) : occupancy_pipe_t<true, false>(out);
-        return tnd ? occupancy_pipe_t<false, true>(out) : occupancy_pipe_t<false, false>(out);
+        if (bf16) return tnd ? occupancy_wide_t<true, true>(out) : occupancy_wide_t<true, false>(out);
+        return tnd ? occupancy_wide_t<false, true>(out) : occupancy_wide_t<false, false>(out);
     }
     SMLA_DISPATCH(occupancy_t, out);
 }

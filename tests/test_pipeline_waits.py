@@ -1,23 +1,23 @@
 """Host-side model of the pipelined kernel's vector-memory wait counts.
 
-Each tile barrier of smla_pipe_kernel waits with vmcnt(later): at most
+Each tile barrier of smla_wide_kernel waits with vmcnt(later): at most
 `later` of the wave's own vector-memory instructions may still be in flight.
 Vector memory completes in issue order, so the wait covers every instruction
 issued more than `later` instructions before it. This test replays one
 wave's issue order over rows of random tile counts, in the kernel's order:
 
-  * row start (end of the previous row): gathers of tiles 0..2 (8 loads each
-    while the tile exists), index rows of tiles 3..5 (1 each);
-  * tile t: barrier; index row of tile t+6 (1); gather of tile t+3 (8, while
-    it exists); after tile pf = (ntiles > 3 ? 2 : ntiles-1) the next row's
-    indices of tiles 0..2 (3);
-  * row end: stores and loads that the next row's tile-0 wait (vmcnt(0))
-    covers.
+  * row start (end of the previous row): the row's Q in two halves (16 loads
+    each), its lse (1), stores of the previous row, then a wait for
+    everything, then the gather of tile 0 (16 loads);
+  * tile t: barrier; the gather of tile t+1 (16 loads, into a dummy row
+    when there is no tile t+1); after tile pf = (ntiles > 2 ? 1 : ntiles-1)
+    the next row's index list (8 loads);
+  * row end: stores, which the next row's tile-0 wait (vmcnt(0)) covers.
 
 It checks that the kernel's formula for `later` covers, at every barrier,
-the gather of the tile and the index row the tile reads, and that every
-value the formula produces has a case in the kernel's wait switch (anything
-else would fall back to waiting for everything: correct but slow).
+the gather of the tile, and that every value the formula produces has a
+case in the kernel's wait switch (anything else would fall back to waiting
+for everything: correct but slow).
 """
 
 import os
@@ -26,7 +26,8 @@ import re
 
 KERNEL = os.path.join(os.path.dirname(__file__), os.pardir, "sparse_mla_attention_02_amd",
                       "csrc", "smla_kernels.hip")
-PREFETCH = 3
+ROWS_PER_WAVE = 16   # gathered rows per wave and tile
+IDX_OPS = 8          # loads of one index list per wave
 
 
 def switch_values():
@@ -37,18 +38,14 @@ def switch_values():
 
 
 def later_of(tile, nt, pf):
-    """The kernel's formula (smla_pipe_kernel, body)."""
-    extra = lambda u: PREFETCH if u == pf else 0
+    """The kernel's formula (smla_wide_kernel, body)."""
     if tile == 0:
         return 0
-    if tile < 3:
-        return 63
-    later = (extra(tile - 3) + 2 + 8 * (tile + 1 < nt) + 8 * (tile + 2 < nt) +
-             extra(tile - 2) + extra(tile - 1))
-    return min(later, 63)
+    return IDX_OPS if tile - 1 == pf else 0
 
 
-def replay(rows, switch, rng):
+def replay(rows, switch, rng, formula=None):
+    formula = formula or later_of
     stream, done = [], 0
 
     def issue(tag, n=1):
@@ -58,40 +55,38 @@ def replay(rows, switch, rng):
         nonlocal done
         done = max(done, len(stream) - n)
 
-    def start_row(r, nt):
-        for k in range(min(nt, 3)):
-            issue(("gather", r, k), 8)
-        for k in (3, 4, 5):
-            issue(("index", r, k))
+    def row_start(r, nt):
+        issue(("q", r), 16)
+        issue(("lse", r))
+        issue(("stores", r - 1), rng.randint(0, 12))
+        issue(("q", r), 16)
+        wait(0)
+        if nt > 0:
+            issue(("gather", r, 0), ROWS_PER_WAVE)
 
-    issue(("indices", 0), PREFETCH)
-    start_row(0, rows[0])
+    issue(("index list", 0), IDX_OPS)
+    row_start(0, rows[0])
     for r, nt in enumerate(rows):
-        pf = 2 if nt > 3 else nt - 1
+        pf = 1 if nt > 2 else nt - 1
         if nt == 0:
-            issue(("indices", r + 1), PREFETCH)
+            issue(("index list", r + 1), IDX_OPS)
         for t in range(nt):
-            later = later_of(t, nt, pf)
+            later = formula(t, nt, pf)
             wait(later if later in switch else 0)
-            need = {("gather", r, t), ("index", r, t + 3)}
             for i, tag in enumerate(stream):
-                assert not (tag in need and i >= done), (rows, r, t, tag)
-            issue(("index", r, t + 6))
-            if t + 3 < nt:
-                issue(("gather", r, t + 3), 8)
+                assert not (tag == ("gather", r, t) and i >= done), (rows, r, t)
+            issue(("gather", r, t + 1) if t + 1 < nt else ("dummy", r), ROWS_PER_WAVE)
             if t == pf:
-                issue(("indices", r + 1), PREFETCH)
-        issue(("row end", r), rng.randint(0, 40))
+                issue(("index list", r + 1), IDX_OPS)
         if r + 1 < len(rows):
-            start_row(r + 1, rows[r + 1])
-        issue(("stores", r), rng.randint(0, 12))
+            row_start(r + 1, rows[r + 1])
 
 
 def test_switch_has_every_count_the_formula_produces():
     switch = switch_values()
     produced = set()
-    for nt in range(0, 70):
-        pf = 2 if nt > 3 else nt - 1
+    for nt in range(0, 40):
+        pf = 1 if nt > 2 else nt - 1
         for t in range(nt):
             produced.add(later_of(t, nt, pf))
     assert produced - {0} <= switch, sorted(produced - switch)
@@ -101,27 +96,21 @@ def test_waits_cover_each_tiles_loads():
     switch = switch_values()
     rng = random.Random(7)
     for _ in range(3000):
-        rows = [rng.choice([0, 1, 2, 3, 4, 5, 6, 7, 9, 17, 64])
-                for _ in range(rng.randint(1, 5))]
+        rows = [rng.choice([0, 1, 2, 3, 4, 5, 9, 17, 32]) for _ in range(rng.randint(1, 5))]
         replay(rows, switch, rng)
 
 
 def test_model_catches_a_too_lenient_wait():
-    # a planted mistake in the formula (one load too few counted as issued
-    # after the gather) must be caught by the replay
-    global later_of
-    good = later_of
-    try:
-        later_of = lambda t, nt, pf: good(t, nt, pf) + (1 if t >= 3 else 0)
-        switch = set(range(64))
-        rng = random.Random(3)
-        caught = False
-        for _ in range(200):
-            try:
-                replay([rng.choice([8, 17, 64])], switch, rng)
-            except AssertionError:
-                caught = True
-                break
-        assert caught
-    finally:
-        later_of = good
+    # a planted mistake in the formula (the index list counted after the
+    # gather one tile too late) must be caught by the replay
+    def wrong(t, nt, pf):
+        return 0 if t == 0 else (IDX_OPS if t - 2 == pf else 0)
+    rng = random.Random(3)
+    caught = False
+    for _ in range(200):
+        try:
+            replay([rng.choice([5, 9, 17, 32])], set(range(64)), rng, formula=wrong)
+        except AssertionError:
+            caught = True
+            break
+    assert caught
