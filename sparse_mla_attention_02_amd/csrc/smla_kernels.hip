@@ -487,8 +487,9 @@ __device__ __forceinline__ void waitcnt_vm_lgkm0() {
 // into LDS still in flight stay in flight.
 __device__ __forceinline__ void barrier_after_vmcnt(int n) {
     switch (n) {
-        // the counts the pipelined kernel produces; anything else waits for all
+        // the counts in use; anything else waits for all
         case 8: waitcnt_vm_lgkm0<8>(); break;
+        case 16: waitcnt_vm_lgkm0<16>(); break;
         default: waitcnt_vm_lgkm0<0>(); break;
     }
     asm volatile("s_barrier" ::: "memory");
@@ -556,8 +557,13 @@ constexpr int kRowBytes = kPitch * 16;          // one key row in LDS
 // 64 (w & 1) .. +63 and keys 32 (w >> 1) .. +31 of each tile. Two tiles live
 // in LDS; the gather of tile t+1 (16 rows per wave, loaded straight into
 // LDS) is spread over the first half of the MFMAs of tile t. The row's index
-// list sits in LDS (double-buffered: the next row's list is loaded during
-// this row), so the tile loop reads no other global memory.
+// list sits in LDS, so the tile loop reads no other global memory.
+//
+// Output: a row is zero-filled before its first tile barrier (which waits
+// for every memory operation of the wave, so the zeros reach L2 before any
+// wave goes on); each tile's values are then stored straight to their
+// columns by the wave that finishes them, two tiles later. A row's end only
+// loads the next row's Q, lse and index list.
 
 constexpr int kWideKeys = 64;                      // keys per tile
 constexpr int kWideBufBytes = kWideKeys * kRowBytes;
@@ -627,13 +633,11 @@ template <bool BF16, bool TND>
 __global__ __launch_bounds__(256, 1) void smla_wide_kernel(KernelArgs a) {
     constexpr int HT = 4;
     constexpr int NT = 256;
-    constexpr int kPerThread = kVcap / NT;
     constexpr int kRowsPerWave = kWideKeys / HT;      // gathered rows per wave and tile
     constexpr int kIdxOps = kVcap / 64 / HT;          // loads of one index list per wave
     __shared__ uint4 kbuf[2][kWideKeys * kPitch];     // tile t in buffer t % 2
     __shared__ int32_t ibuf[2][kVcap];                // index lists: this row, next row
     __shared__ float red[2][4][kWideKeys];            // partial sums, last two tiles
-    __shared__ float vals[kVcap + 64];                // the row's values by entry; then a sink
     __shared__ float lsebuf[HT * 32];                 // the next row's lse
     __shared__ uint4 dummy[64];                       // loads of a tile with nothing to gather
 
@@ -649,7 +653,6 @@ __global__ __launch_bounds__(256, 1) void smla_wide_kernel(KernelArgs a) {
     const int my_slot = kRowsPerWave * wave + (lane & 15);
     const uint4* __restrict__ q4 = static_cast<const uint4*>(a.q);
     const char* __restrict__ kbytes = static_cast<const char*>(a.k);
-    float* const stage = reinterpret_cast<float*>(kbuf[1]);
     const uint32_t kbuf_lds = lds_addr(kbuf);
     const uint32_t ibuf_lds = lds_addr(ibuf);
     const uint32_t lse_lds = lds_addr(lsebuf);
@@ -715,13 +718,12 @@ __global__ __launch_bounds__(256, 1) void smla_wide_kernel(KernelArgs a) {
         }
     };
     // the next row of this workgroup, decoded (its scalar loads waited for
-    // here, so that later LDS waits can count), and its index list
-    auto prefetch_next = [&]() {
+    // here, so that later LDS waits can count)
+    auto decode_next = [&]() {
         rn = (it + 1) * a.num_wg < a.R ? row_of(a, it + 1, blockIdx.x) : a.R;
-        rln = rn < a.R ? rn : rc;  // the last row loads itself again (unused)
+        rln = rn < a.R ? rn : rc;
         rin = decode_row<TND>(a, rln);
         waitcnt_vm_lgkm0<63>();
-        load_idx_row(rln, ib ^ 1);
     };
     auto ntiles_of = [](const RowInfo& ri) { return (ri.n + kWideKeys - 1) / kWideKeys; };
     // byte offset of the key row of slot my_slot of `tile` holding raw index
@@ -751,10 +753,12 @@ __global__ __launch_bounds__(256, 1) void smla_wide_kernel(KernelArgs a) {
         }
     };
 
-    // ---- first row: operands and index list, then tile 0 in flight
+    // ---- first row: operands, index list and zeroed output, then tile 0 in
+    // flight
     load_idx_row(rc, 0);
     stage_q(rc, 0, HT * 32);
     stage_lse(rc);
+    zero_span(a.out + rc * a.W, 0, a.W, tid, NT);
     barrier_after_vmcnt(0);
     read_q_lse();
     lds_barrier();
@@ -762,32 +766,32 @@ __global__ __launch_bounds__(256, 1) void smla_wide_kernel(KernelArgs a) {
 
     for (; it * a.num_wg < a.R && rc < a.R; ++it) {
         const int ntiles = ntiles_of(ric);
-        // the tile after whose MFMAs the next row's index list is loaded
-        const int pf = ntiles > 2 ? 1 : ntiles - 1;
         float* __restrict__ orow = a.out + rc * a.W;
         const i32x4_t kdesc = k_desc(ric);
-        const int64_t seg0 = ric.col0;
-        const int64_t seg1 = ric.col0 + (ntiles > 0 ? ric.vis : 0);
         const int32_t* __restrict__ irow = ibuf[ib];
-
-        if (ntiles == 0) prefetch_next();
+        // Finish entry `e` = tile*64 + slot (slot 16 w + lane for lanes < 16):
+        // the sum of its four partial sums over G, stored to its column if
+        // the entry is used.
+        const int slot = (kRowsPerWave * wave + lane) & (kWideKeys - 1);
+        auto store_value = [&](int tile, float tot, int32_t j) {
+            const int e = tile * kWideKeys + slot;
+            if (lane < kRowsPerWave && tile >= 0 && e < ric.n && (uint32_t)j < (uint32_t)ric.vis)
+                orow[ric.col0 + j] = tot * a.inv_g;
+        };
 
         f32x16_t prev0 = {}, prev1 = {};
         auto body = [&](int tile) {
             const bool gather = tile + 1 < ntiles;
-            // Loads issued after the gather of this tile (in tile-1; vector
-            // memory returns in order): the next row's index list if it came
-            // after. Tile 0 waits for everything (the previous row's stores
-            // included).
-            const int later = tile == 0 ? 0 : (tile - 1 == pf ? kIdxOps : 0);
-            barrier_after_vmcnt(later);
+            // The gather of this tile (issued in tile-1, or at the row start)
+            // is the last vector-memory work of the wave: wait for all of it.
+            barrier_after_vmcnt(0);
             const int32_t key = gather ? irow[(tile + 1) * kWideKeys + my_slot] : 0;
             const int32_t rows_off = row_off(ric, tile + 1, key);
-            const int slot = (kRowsPerWave * wave + lane) & (kWideKeys - 1);
             const int pb = tile & 1;  // parity of tile - 2
             float parts[4];
 #pragma unroll
             for (int p = 0; p < 4; ++p) parts[p] = red[pb][p][slot];
+            const int32_t jv = tile >= 2 ? irow[(tile - 2) * kWideKeys + slot] : -1;
             const uint32_t m0_rows =
                 gather ? kbuf_lds + (uint32_t)(((tile + 1) & 1) * kWideBufBytes +
                                                kRowsPerWave * wave * kRowBytes)
@@ -810,8 +814,7 @@ __global__ __launch_bounds__(256, 1) void smla_wide_kernel(KernelArgs a) {
                         tot += parts[3];
                         pin(tot);
                     } else if (s == 5) {
-                        const bool mine = lane < kRowsPerWave && tile >= 2;
-                        vals[mine ? (tile - 2) * kWideKeys + slot : kVcap + lane] = tot * a.inv_g;
+                        store_value(tile - 2, tot, jv);
                     }
                 },
                 acc0, acc1);
@@ -819,10 +822,7 @@ __global__ __launch_bounds__(256, 1) void smla_wide_kernel(KernelArgs a) {
             prev0 = acc0;
             prev1 = acc1;
         };
-        for (int tile = 0; tile < ntiles; ++tile) {
-            body(tile);
-            if (tile == pf) prefetch_next();
-        }
+        for (int tile = 0; tile < ntiles; ++tile) body(tile);
         if (ntiles > 0)
             red[(ntiles - 1) & 1][2 * hg + half][32 * kh + col] =
                 head_sum(prev0, l2, a.c_scale) + head_sum(prev1, l2 + 16, a.c_scale);
@@ -830,70 +830,29 @@ __global__ __launch_bounds__(256, 1) void smla_wide_kernel(KernelArgs a) {
         // all MFMAs done and every gather of this row has landed: K buffers
         // are free; partial sums visible
         lds_barrier();
-        auto reduce = [&](int tile) {
-            const int slot = (kRowsPerWave * wave + lane) & (kWideKeys - 1);
+        auto finish = [&](int tile) {
             const int pb = tile & 1;
             const float tot = red[pb][0][slot] + red[pb][1][slot] + red[pb][2][slot] +
                               red[pb][3][slot];
-            const bool mine = lane < kRowsPerWave;
-            vals[mine ? tile * kWideKeys + slot : kVcap + lane] = tot * a.inv_g;
+            store_value(tile, tot, irow[tile * kWideKeys + slot]);
         };
-        if (ntiles >= 2) reduce(ntiles - 2);
-        if (ntiles >= 1) reduce(ntiles - 1);
+        if (ntiles >= 2) finish(ntiles - 2);
+        if (ntiles >= 1) finish(ntiles - 1);
 
-        // the next row's Q (heads 0..63, into buffer 0) and lse land while
-        // this row is assembled in buffer 1
-        const bool more = rn < a.R;
-        if (more) {
-            stage_q(rln, 0, 64);
+        // the next row: Q into the K buffers, lse, index list and zeroed
+        // output; every wave reads its heads back, then buffer 0 takes the
+        // next row's first tile
+        decode_next();
+        if (rn < a.R) {
+            stage_q(rln, 0, HT * 32);
             stage_lse(rln);
-        }
-
-        // assemble columns [seg0, seg1) of this row in LDS and write them once
-        for (int64_t c0 = seg0; c0 < seg1; c0 += kStage - 4) {
-            const int64_t len = (seg1 - c0 < kStage - 4) ? seg1 - c0 : kStage - 4;
-            const int m0 = (int)((rc * a.W + c0) & 3);
-            lds_barrier();  // values complete; previous chunk written out
-            for (int i = tid; i < (len + m0 + 3) >> 2; i += NT)
-                reinterpret_cast<f32x4_t*>(stage)[i] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-            lds_barrier();
-#pragma unroll
-            for (int i = 0; i < kPerThread; ++i) {
-                const int t = tid + i * NT;
-                const int32_t j = irow[t];
-                if (t < ric.n && (uint32_t)j < (uint32_t)ric.vis) {
-                    const int64_t c = ric.col0 + j - c0;
-                    if (c >= 0 && c < len) stage[c + m0] = vals[t];
-                }
-            }
-            lds_barrier();
-            const int ngroups = (int)((len + m0 + 3) >> 2);
-            for (int qg = tid; qg < ngroups; qg += NT) {
-                const int64_t cb = c0 - m0 + 4 * (int64_t)qg;
-                if (cb >= c0 && cb + 4 <= c0 + len) {
-                    const f32x4_t v = reinterpret_cast<const f32x4_t*>(stage)[qg];
-                    __builtin_nontemporal_store(v, reinterpret_cast<f32x4_t*>(orow + cb));
-                } else {
-#pragma unroll
-                    for (int e = 0; e < 4; ++e)
-                        if (cb + e >= c0 && cb + e < c0 + len) orow[cb + e] = stage[4 * qg + e];
-                }
-            }
-        }
-
-        // the rest of the next row's Q into buffer 1 once the stage is free;
-        // every wave reads its heads back, then buffer 0 takes the next
-        // row's first tile
-        if (more) {
-            lds_barrier();
-            stage_q(rln, 64, HT * 32);
+            load_idx_row(rln, ib ^ 1);
+            zero_span(a.out + rn * a.W, 0, a.W, tid, NT);
             barrier_after_vmcnt(0);
             read_q_lse();
             lds_barrier();
             start_row(rin, ib ^ 1);
         }
-        zero_span(orow, 0, seg0, tid, NT);
-        zero_span(orow, seg1, a.W, tid, NT);
 
         // the next row becomes current
         rc = rn;

@@ -6,13 +6,12 @@ Vector memory completes in issue order, so the wait covers every instruction
 issued more than `later` instructions before it. This test replays one
 wave's issue order over rows of random tile counts, in the kernel's order:
 
-  * row start (end of the previous row): the row's Q in two halves (16 loads
-    each), its lse (1), stores of the previous row, then a wait for
-    everything, then the gather of tile 0 (16 loads);
-  * tile t: barrier; the gather of tile t+1 (16 loads, into a dummy row
-    when there is no tile t+1); after tile pf = (ntiles > 2 ? 1 : ntiles-1)
-    the next row's index list (8 loads);
-  * row end: stores, which the next row's tile-0 wait (vmcnt(0)) covers.
+  * row start (end of the previous row): the previous row's last value
+    stores, the row's Q (32 loads), lse (1), index list (8), the zero-fill
+    of its output, then a wait for everything, then the gather of tile 0
+    (16 loads);
+  * tile t: barrier; the value stores of tile t-2 (1); the gather of tile
+    t+1 (16 loads, into a dummy row when there is no tile t+1).
 
 It checks that the kernel's formula for `later` covers, at every barrier,
 the gather of the tile, and that every value the formula produces has a
@@ -38,10 +37,9 @@ def switch_values():
 
 
 def later_of(tile, nt, pf):
-    """The kernel's formula (smla_wide_kernel, body)."""
-    if tile == 0:
-        return 0
-    return IDX_OPS if tile - 1 == pf else 0
+    """The kernel's count (smla_wide_kernel, body): the gather of a tile is
+    the last vector-memory work before its barrier."""
+    return 0
 
 
 def replay(rows, switch, rng, formula=None):
@@ -56,28 +54,26 @@ def replay(rows, switch, rng, formula=None):
         done = max(done, len(stream) - n)
 
     def row_start(r, nt):
-        issue(("q", r), 16)
+        issue(("stores", r - 1), 2)
+        issue(("q", r), 32)
         issue(("lse", r))
-        issue(("stores", r - 1), rng.randint(0, 12))
-        issue(("q", r), 16)
+        issue(("index list", r), IDX_OPS)
+        issue(("zero fill", r), rng.randint(4, 12))
         wait(0)
         if nt > 0:
             issue(("gather", r, 0), ROWS_PER_WAVE)
 
-    issue(("index list", 0), IDX_OPS)
     row_start(0, rows[0])
     for r, nt in enumerate(rows):
         pf = 1 if nt > 2 else nt - 1
-        if nt == 0:
-            issue(("index list", r + 1), IDX_OPS)
         for t in range(nt):
             later = formula(t, nt, pf)
             wait(later if later in switch else 0)
             for i, tag in enumerate(stream):
-                assert not (tag == ("gather", r, t) and i >= done), (rows, r, t)
+                assert not (tag in (("gather", r, t), ("zero fill", r)) and i >= done), (rows, r, t)
+            if t >= 2:
+                issue(("stores", r))
             issue(("gather", r, t + 1) if t + 1 < nt else ("dummy", r), ROWS_PER_WAVE)
-            if t == pf:
-                issue(("index list", r + 1), IDX_OPS)
         if r + 1 < len(rows):
             row_start(r + 1, rows[r + 1])
 
@@ -101,10 +97,10 @@ def test_waits_cover_each_tiles_loads():
 
 
 def test_model_catches_a_too_lenient_wait():
-    # a planted mistake in the formula (the index list counted after the
-    # gather one tile too late) must be caught by the replay
+    # a planted mistake (a wait that lets the last 16 loads stay in flight)
+    # must be caught by the replay
     def wrong(t, nt, pf):
-        return 0 if t == 0 else (IDX_OPS if t - 2 == pf else 0)
+        return 0 if t == 0 else 16
     rng = random.Random(3)
     caught = False
     for _ in range(200):
