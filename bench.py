@@ -113,8 +113,11 @@ def cpu_baseline(p, target_s):
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=200)
+    ap.add_argument("--prewarm-seconds", type=float, default=0.5,
+                    help="untimed steps run for this long before the warmup steps: an idle "
+                         "GPU takes on the order of 100 ms of load to reach its working clock")
     ap.add_argument("--workload", default="dsv32")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -122,6 +125,8 @@ def main():
                     help="only run a plain 256 MiB device-to-device copy 5 times (the "
                          "known-size reference for the HBM byte counters)")
     args = ap.parse_args()
+    if args.steps < 1 or args.warmup < 0 or args.prewarm_seconds < 0:
+        ap.error("--steps must be >= 1, --warmup and --prewarm-seconds >= 0")
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
     rank = int(os.environ.get("RANK", "0"))
@@ -186,9 +191,16 @@ def main():
             after.record(stream)
         return md
 
-    log(f"warmup {args.warmup} steps")
+    t_pre = time.perf_counter()
+    n_pre = 0
+    while time.perf_counter() - t_pre < args.prewarm_seconds:
+        for _ in range(10):
+            step()
+        n_pre += 10
+        torch.cuda.synchronize()
+    log(f"prewarm {n_pre} steps; warmup {args.warmup} steps")
     for _ in range(args.warmup):
-        md = step()
+        step()
     torch.cuda.synchronize()
 
     # timed region: K steps, each kernel bracketed by events on its stream
@@ -198,7 +210,7 @@ def main():
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(args.steps):
-        step(ev[i][0], ev[i][1])
+        md = step(ev[i][0], ev[i][1])
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     kernel_ms = [a.elapsed_time(b) for a, b in ev]
@@ -228,7 +240,8 @@ def main():
     line = {
         "metric": "QK TFLOP/s + HBM GB/s, sparse softmax-L1Norm N1=128 topk=2048 D=512",
         "value": round(tflops, 2), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
-        "warmup": args.warmup, "ms_per_step": round(ms_step, 4), "higher_is_better": True,
+        "warmup": args.warmup, "prewarm_steps": n_pre, "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True,
         "scaling": "weak", "vs_baseline": None, "dtype": p.dtype, "data": "synthetic",
         "hbm_gbps": round(gbps, 1), "hbm_frac": round(gbps / PEAK_HBM_GBPS, 4),
         "config": {"workload": p.name, "layout": p.layout, "batch": p.batch,

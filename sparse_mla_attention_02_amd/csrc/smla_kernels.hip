@@ -488,8 +488,7 @@ __device__ __forceinline__ void waitcnt_vm_lgkm0() {
 __device__ __forceinline__ void barrier_after_vmcnt(int n) {
     switch (n) {
         // the counts in use; anything else waits for all
-        case 8: waitcnt_vm_lgkm0<8>(); break;
-        case 16: waitcnt_vm_lgkm0<16>(); break;
+        case 1: waitcnt_vm_lgkm0<1>(); break;
         default: waitcnt_vm_lgkm0<0>(); break;
     }
     asm volatile("s_barrier" ::: "memory");
@@ -533,6 +532,27 @@ __device__ __forceinline__ void dma_row(i32x4_t desc, uint32_t m0, int32_t soff,
         : "s"(m0), "v"(voff), "s"(desc), "s"(soff)
         : "memory", "m0");
 }
+// The same with the non-temporal hint, for data read once (Q rows, index
+// lists): the key rows, which are gathered again and again, keep their
+// place in L2.
+__device__ __forceinline__ void dma_row_nt(i32x4_t desc, uint32_t m0, int32_t soff, uint32_t voff) {
+    asm volatile(
+        "s_mov_b32 m0, %0\n\t"
+        "s_nop 0\n\t"
+        "buffer_load_dwordx4 %1, %2, %3 offen nt lds"
+        :
+        : "s"(m0), "v"(voff), "s"(desc), "s"(soff)
+        : "memory", "m0");
+}
+__device__ __forceinline__ void dma_dword_nt(i32x4_t desc, uint32_t m0, int32_t soff, uint32_t voff) {
+    asm volatile(
+        "s_mov_b32 m0, %0\n\t"
+        "s_nop 0\n\t"
+        "buffer_load_dword %1, %2, %3 offen nt lds"
+        :
+        : "s"(m0), "v"(voff), "s"(desc), "s"(soff)
+        : "memory", "m0");
+}
 // Lane i moves 4 bytes at byte offset voff + soff to LDS address m0 + 4 i.
 __device__ __forceinline__ void dma_dword(i32x4_t desc, uint32_t m0, int32_t soff, uint32_t voff) {
     asm volatile(
@@ -559,11 +579,15 @@ constexpr int kRowBytes = kPitch * 16;          // one key row in LDS
 // LDS) is spread over the first half of the MFMAs of tile t. The row's index
 // list sits in LDS, so the tile loop reads no other global memory.
 //
-// Output: a row is zero-filled before its first tile barrier (which waits
-// for every memory operation of the wave, so the zeros reach L2 before any
-// wave goes on); each tile's values are then stored straight to their
-// columns by the wave that finishes them, two tiles later. A row's end only
-// loads the next row's Q, lse and index list.
+// Output: a row is zero-filled (at the end of the previous row) before the
+// barrier of its first tile, which waits for every memory operation of the
+// wave, so the zeros reach L2 before any wave goes on; each tile's values are
+// then stored straight to their columns by the wave that finishes them, two
+// tiles later, after the gather loads of that step sequence.
+//
+// Accumulators alternate between two register sets from tile to tile, so
+// the epilogue of tile t reads its scores where the MFMAs of tile t left
+// them while the MFMAs of tile t+1 fill the other set.
 
 constexpr int kWideKeys = 64;                      // keys per tile
 constexpr int kWideBufBytes = kWideKeys * kRowBytes;
@@ -575,14 +599,17 @@ constexpr int kWideBufBytes = kWideKeys * kRowBytes;
 // the load of gathered row s-1 of tile t+1 (its row offset read one step
 // earlier) to LDS address m0_rows + (s-1) m0_step (a step of 0 sends a tile
 // that has nothing to gather to one dummy row); `mid(s)` is the caller's
-// spread-out work.
-template <bool BF16, typename Mid>
+// spread-out work. Before step 0, after the LDS reads of the first kLead
+// operands, `pre()` issues the caller's own LDS reads (so that the first
+// MFMA waits only for its operand); `offs()`, called in step 0, gives each
+// lane's byte offset of the row it gathers (lanes 0..15 used).
+template <bool BF16, typename Pre, typename Offs, typename Mid>
 __device__ __forceinline__ void qk_tile_wide(const uint4* __restrict__ src, const uint4* qa0,
                                              const uint4* qa1, int col, int half,
                                              const f32x16_t& prev0, const f32x16_t& prev1,
                                              const float* l2, float c, float* prev_sum,
                                              i32x4_t kdesc, uint32_t m0_rows, uint32_t m0_step,
-                                             int32_t rows_off, uint32_t voff, Mid mid,
+                                             Pre pre, Offs offs, uint32_t voff, Mid mid,
                                              f32x16_t& acc0, f32x16_t& acc1) {
     constexpr int kSteps = kChunks / 2;
     constexpr int kLead = 8;
@@ -590,10 +617,14 @@ __device__ __forceinline__ void qk_tile_wide(const uint4* __restrict__ src, cons
     uint4 b[kSteps];
 #pragma unroll
     for (int s = 0; s < kLead; ++s) b[s] = row[2 * s];
+    __builtin_amdgcn_sched_barrier(0);
+    pre();
+    __builtin_amdgcn_sched_barrier(0);
     acc0 = f32x16_t{};
     acc1 = f32x16_t{};
     float sum = 0.0f, t = 0.0f, ex = 0.0f;
     int32_t soff = 0;
+    int32_t rows_off = 0;
     int32_t m0 = (int32_t)m0_rows;
     pin_s(m0);
 #pragma unroll
@@ -617,6 +648,7 @@ __device__ __forceinline__ void qk_tile_wide(const uint4* __restrict__ src, cons
             m0 += (int32_t)m0_step;
             pin_s(m0);
         }
+        if (s == 0) rows_off = offs();
         if (s < 16) {
             soff = __builtin_amdgcn_readlane(rows_off, s);
             pin_s(soff);
@@ -682,7 +714,7 @@ __global__ __launch_bounds__(256, 1) void smla_wide_kernel(KernelArgs a) {
 #pragma unroll
         for (int i = 0; i < kIdxOps; ++i) {
             const int c = kIdxOps * wave + i;  // 256-byte piece of the list
-            dma_dword(id, ibuf_lds + (uint32_t)(slot * kVcap * 4 + c * 256), c * 256, voff4);
+            dma_dword_nt(id, ibuf_lds + (uint32_t)(slot * kVcap * 4 + c * 256), c * 256, voff4);
         }
     };
     // Q and lse pass through LDS as whole rows (a load straight into the MFMA
@@ -692,7 +724,7 @@ __global__ __launch_bounds__(256, 1) void smla_wide_kernel(KernelArgs a) {
     auto stage_q = [&](int64_t r, int h0, int h1) {
         const i32x4_t qd = raw_desc(q4 + r * a.G * kChunks, (uint32_t)a.G * 1024u);
         for (int h = h0 + wave; h < h1; h += HT)
-            dma_row(qd, kbuf_lds + (uint32_t)((h >> 6) * kWideBufBytes + (h & 63) * kRowBytes),
+            dma_row_nt(qd, kbuf_lds + (uint32_t)((h >> 6) * kWideBufBytes + (h & 63) * kRowBytes),
                     h * 1024, voff16);
     };
     auto stage_lse = [&](int64_t r) {
@@ -718,12 +750,15 @@ __global__ __launch_bounds__(256, 1) void smla_wide_kernel(KernelArgs a) {
         }
     };
     // the next row of this workgroup, decoded (its scalar loads waited for
-    // here, so that later LDS waits can count)
-    auto decode_next = [&]() {
+    // here, so that later LDS waits can count), its output zero-filled and
+    // its index list loaded
+    auto prepare_next = [&]() {
         rn = (it + 1) * a.num_wg < a.R ? row_of(a, it + 1, blockIdx.x) : a.R;
-        rln = rn < a.R ? rn : rc;
+        rln = rn < a.R ? rn : rc;  // the last row loads itself again (unused)
         rin = decode_row<TND>(a, rln);
         waitcnt_vm_lgkm0<63>();
+        if (rn < a.R) zero_span(a.out + rn * a.W, 0, a.W, tid, NT);
+        load_idx_row(rln, ib ^ 1);
     };
     auto ntiles_of = [](const RowInfo& ri) { return (ri.n + kWideKeys - 1) / kWideKeys; };
     // byte offset of the key row of slot my_slot of `tile` holding raw index
@@ -766,32 +801,50 @@ __global__ __launch_bounds__(256, 1) void smla_wide_kernel(KernelArgs a) {
 
     for (; it * a.num_wg < a.R && rc < a.R; ++it) {
         const int ntiles = ntiles_of(ric);
-        float* __restrict__ orow = a.out + rc * a.W;
         const i32x4_t kdesc = k_desc(ric);
         const int32_t* __restrict__ irow = ibuf[ib];
         // Finish entry `e` = tile*64 + slot (slot 16 w + lane for lanes < 16):
         // the sum of its four partial sums over G, stored to its column if
-        // the entry is used.
+        // the entry is used. The store is one buffer store per call whatever
+        // the lanes hold (lanes with nothing to store give an offset past
+        // the row, which the buffer range check drops), so the wave's
+        // memory-operation count is known.
         const int slot = (kRowsPerWave * wave + lane) & (kWideKeys - 1);
+        const int64_t obytes = a.W * 4;
+        const __amdgpu_buffer_rsrc_t orsrc = __builtin_amdgcn_make_buffer_rsrc(
+            a.out + rc * a.W, (short)0, obytes < 0x7ffffff0ll ? (int)obytes : 0x7ffffff0,
+            0x00020000);
         auto store_value = [&](int tile, float tot, int32_t j) {
             const int e = tile * kWideKeys + slot;
-            if (lane < kRowsPerWave && tile >= 0 && e < ric.n && (uint32_t)j < (uint32_t)ric.vis)
-                orow[ric.col0 + j] = tot * a.inv_g;
+            const bool used =
+                lane < kRowsPerWave && tile >= 0 && e < ric.n && (uint32_t)j < (uint32_t)ric.vis;
+            // (the builtin's data operand is an integer: pass the bits)
+            __builtin_amdgcn_raw_buffer_store_b32(
+                __builtin_bit_cast(uint32_t, tot * a.inv_g), orsrc,
+                used ? (int)((uint32_t)(ric.col0 + j) * 4u) : 0x7ffffff0, 0, 0);
         };
 
-        f32x16_t prev0 = {}, prev1 = {};
-        auto body = [&](int tile) {
+        f32x16_t xa0, xa1, xb0 = {}, xb1 = {};
+        // memory operations this wave issued after the gather of the tile
+        // about to start: the previous tile's value store (none before the
+        // row's first tile)
+        int later = 0;
+        auto body = [&](int tile, const f32x16_t& prev0, const f32x16_t& prev1, f32x16_t& acc0,
+                        f32x16_t& acc1) {
             const bool gather = tile + 1 < ntiles;
-            // The gather of this tile (issued in tile-1, or at the row start)
-            // is the last vector-memory work of the wave: wait for all of it.
-            barrier_after_vmcnt(0);
-            const int32_t key = gather ? irow[(tile + 1) * kWideKeys + my_slot] : 0;
-            const int32_t rows_off = row_off(ric, tile + 1, key);
-            const int pb = tile & 1;  // parity of tile - 2
+            // wait for the gather of this tile (issued in tile-1, or at the
+            // row start) and everything before it
+            barrier_after_vmcnt(later);
+            int32_t key = 0, jv = -1;
             float parts[4];
+            const int pb = tile & 1;  // parity of tile - 2
+            auto pre = [&]() {
+                key = irow[((tile + 1) & 31) * kWideKeys + my_slot];
 #pragma unroll
-            for (int p = 0; p < 4; ++p) parts[p] = red[pb][p][slot];
-            const int32_t jv = tile >= 2 ? irow[(tile - 2) * kWideKeys + slot] : -1;
+                for (int p = 0; p < 4; ++p) parts[p] = red[pb][p][slot];
+                jv = irow[((tile - 2) & 31) * kWideKeys + slot];
+            };
+            auto offs = [&]() -> int32_t { return row_off(ric, tile + 1, gather ? key : 0); };
             const uint32_t m0_rows =
                 gather ? kbuf_lds + (uint32_t)(((tile + 1) & 1) * kWideBufBytes +
                                                kRowsPerWave * wave * kRowBytes)
@@ -799,10 +852,9 @@ __global__ __launch_bounds__(256, 1) void smla_wide_kernel(KernelArgs a) {
             const uint32_t m0_step = gather ? (uint32_t)kRowBytes : 0u;
             float tot = 0.0f;
             float sum_prev;
-            f32x16_t acc0, acc1;
             qk_tile_wide<BF16>(
                 kbuf[tile & 1] + 32 * kh * kPitch, qa0, qa1, col, half, prev0, prev1, l2,
-                a.c_scale, &sum_prev, kdesc, m0_rows, m0_step, rows_off, voff16,
+                a.c_scale, &sum_prev, kdesc, m0_rows, m0_step, pre, offs, voff16,
                 [&](int s) {
                     if (s == 2) {
                         tot = parts[0] + parts[1];
@@ -813,16 +865,21 @@ __global__ __launch_bounds__(256, 1) void smla_wide_kernel(KernelArgs a) {
                     } else if (s == 4) {
                         tot += parts[3];
                         pin(tot);
-                    } else if (s == 5) {
-                        store_value(tile - 2, tot, jv);
+                    } else if (s == 20) {
+                        store_value(tile - 2, tot, tile >= 2 ? jv : -1);
                     }
                 },
                 acc0, acc1);
             red[(tile - 1) & 1][2 * hg + half][32 * kh + col] = sum_prev;  // tile 0: unused
-            prev0 = acc0;
-            prev1 = acc1;
         };
-        for (int tile = 0; tile < ntiles; ++tile) body(tile);
+        for (int tile = 0; tile < ntiles; tile += 2) {
+            body(tile, xb0, xb1, xa0, xa1);
+            later = 1;
+            if (tile + 1 >= ntiles) break;
+            body(tile + 1, xa0, xa1, xb0, xb1);
+        }
+        const f32x16_t& prev0 = (ntiles & 1) ? xa0 : xb0;
+        const f32x16_t& prev1 = (ntiles & 1) ? xa1 : xb1;
         if (ntiles > 0)
             red[(ntiles - 1) & 1][2 * hg + half][32 * kh + col] =
                 head_sum(prev0, l2, a.c_scale) + head_sum(prev1, l2 + 16, a.c_scale);
@@ -839,15 +896,13 @@ __global__ __launch_bounds__(256, 1) void smla_wide_kernel(KernelArgs a) {
         if (ntiles >= 2) finish(ntiles - 2);
         if (ntiles >= 1) finish(ntiles - 1);
 
-        // the next row: Q into the K buffers, lse, index list and zeroed
-        // output; every wave reads its heads back, then buffer 0 takes the
-        // next row's first tile
-        decode_next();
+        // the next row: index list and zeroed output, then Q into the K
+        // buffers and lse; every wave reads its heads back, then buffer 0
+        // takes the next row's first tile
+        prepare_next();
         if (rn < a.R) {
             stage_q(rln, 0, HT * 32);
             stage_lse(rln);
-            load_idx_row(rln, ib ^ 1);
-            zero_span(a.out + rn * a.W, 0, a.W, tid, NT);
             barrier_after_vmcnt(0);
             read_q_lse();
             lds_barrier();
@@ -859,6 +914,9 @@ __global__ __launch_bounds__(256, 1) void smla_wide_kernel(KernelArgs a) {
         ric = rin;
         ib ^= 1;
     }
+    // loads into LDS (the last tile's dummy loads) must land before the
+    // workgroup's LDS is released
+    waitcnt_vm_lgkm0<0>();
 }
 
 template <bool BF16, bool TND>

@@ -6,17 +6,20 @@ Vector memory completes in issue order, so the wait covers every instruction
 issued more than `later` instructions before it. This test replays one
 wave's issue order over rows of random tile counts, in the kernel's order:
 
-  * row start (end of the previous row): the previous row's last value
-    stores, the row's Q (32 loads), lse (1), index list (8), the zero-fill
-    of its output, then a wait for everything, then the gather of tile 0
-    (16 loads);
-  * tile t: barrier; the value stores of tile t-2 (1); the gather of tile
-    t+1 (16 loads, into a dummy row when there is no tile t+1).
+  * first row: its index list (8 loads), Q (32), lse (1), the zero-fill of
+    its output, a wait for everything, then the gather of tile 0 (16);
+  * tile t: barrier; the gather of tile t+1 (16 loads, into a dummy row
+    when there is no tile t+1); one value store (always issued: lanes with
+    nothing to store point past the row);
+  * row end: the value stores of the last two tiles, the zero-fill of the
+    next row's output, its index list (8), Q (32) and lse (1), a wait for
+    everything, then the gather of its tile 0.
 
-It checks that the kernel's formula for `later` covers, at every barrier,
-the gather of the tile, and that every value the formula produces has a
-case in the kernel's wait switch (anything else would fall back to waiting
-for everything: correct but slow).
+It checks that the kernel's count `later` covers, at every barrier, the
+gather of the tile and the zero-fill of the row, that the index list of a
+row has landed before its first tile reads it, and that every value the
+count takes has a case in the kernel's wait switch (anything else would fall
+back to waiting for everything: correct but slow).
 """
 
 import os
@@ -36,10 +39,10 @@ def switch_values():
     return {int(v) for v in re.findall(r"case (\d+): waitcnt_vm_lgkm0", body)}
 
 
-def later_of(tile, nt, pf):
-    """The kernel's count (smla_wide_kernel, body): the gather of a tile is
-    the last vector-memory work before its barrier."""
-    return 0
+def later_of(t, nt):
+    """The kernel's count after tile t (smla_wide_kernel, tile loop): the
+    value store of tile t."""
+    return 1
 
 
 def replay(rows, switch, rng, formula=None):
@@ -53,38 +56,44 @@ def replay(rows, switch, rng, formula=None):
         nonlocal done
         done = max(done, len(stream) - n)
 
-    def row_start(r, nt):
-        issue(("stores", r - 1), 2)
-        issue(("q", r), 32)
-        issue(("lse", r))
-        issue(("index list", r), IDX_OPS)
-        issue(("zero fill", r), rng.randint(4, 12))
-        wait(0)
-        if nt > 0:
-            issue(("gather", r, 0), ROWS_PER_WAVE)
+    def landed(tag):
+        return all(i < done for i, x in enumerate(stream) if x == tag)
 
-    row_start(0, rows[0])
+    issue(("index list", 0), IDX_OPS)
+    issue(("q", 0), 32)
+    issue(("lse", 0))
+    issue(("zero fill", 0), rng.randint(0, 12))
+    wait(0)
+    if rows[0] > 0:
+        issue(("gather", 0, 0), ROWS_PER_WAVE)
     for r, nt in enumerate(rows):
-        pf = 1 if nt > 2 else nt - 1
+        more = r + 1 < len(rows)
+        assert landed(("index list", r)) and landed(("zero fill", r)), (rows, r)
+        later = 0
         for t in range(nt):
-            later = formula(t, nt, pf)
             wait(later if later in switch else 0)
-            for i, tag in enumerate(stream):
-                assert not (tag in (("gather", r, t), ("zero fill", r)) and i >= done), (rows, r, t)
-            if t >= 2:
-                issue(("stores", r))
+            assert landed(("gather", r, t)) and landed(("zero fill", r)), (rows, r, t)
             issue(("gather", r, t + 1) if t + 1 < nt else ("dummy", r), ROWS_PER_WAVE)
-        if r + 1 < len(rows):
-            row_start(r + 1, rows[r + 1])
+            issue(("store", r))
+            later = formula(t, nt)
+        issue(("store", r), min(nt, 2))
+        if more:
+            issue(("zero fill", r + 1), rng.randint(0, 12))
+        issue(("index list", r + 1), IDX_OPS)
+        if more:
+            issue(("q", r + 1), 32)
+            issue(("lse", r + 1))
+            wait(0)
+            if rows[r + 1] > 0:
+                issue(("gather", r + 1, 0), ROWS_PER_WAVE)
 
 
 def test_switch_has_every_count_the_formula_produces():
     switch = switch_values()
     produced = set()
-    for nt in range(0, 40):
-        pf = 1 if nt > 2 else nt - 1
+    for nt in range(0, 70):
         for t in range(nt):
-            produced.add(later_of(t, nt, pf))
+            produced.add(later_of(t, nt))
     assert produced - {0} <= switch, sorted(produced - switch)
 
 
@@ -92,20 +101,20 @@ def test_waits_cover_each_tiles_loads():
     switch = switch_values()
     rng = random.Random(7)
     for _ in range(3000):
-        rows = [rng.choice([0, 1, 2, 3, 4, 5, 9, 17, 32]) for _ in range(rng.randint(1, 5))]
+        rows = [rng.choice([0, 1, 2, 3, 4, 5, 6, 9, 17, 19, 32]) for _ in range(rng.randint(1, 5))]
         replay(rows, switch, rng)
 
 
 def test_model_catches_a_too_lenient_wait():
-    # a planted mistake (a wait that lets the last 16 loads stay in flight)
-    # must be caught by the replay
-    def wrong(t, nt, pf):
-        return 0 if t == 0 else 16
+    # a planted mistake (a wait that lets the last 16 operations stay in
+    # flight: the gather of the tile) must be caught by the replay
+    def wrong(t, nt):
+        return 17
     rng = random.Random(3)
     caught = False
     for _ in range(200):
         try:
-            replay([rng.choice([5, 9, 17, 32])], set(range(64)), rng, formula=wrong)
+            replay([rng.choice([5, 9, 17, 32]), 4], set(range(64)), rng, formula=wrong)
         except AssertionError:
             caught = True
             break
