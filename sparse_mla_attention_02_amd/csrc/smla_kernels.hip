@@ -488,7 +488,7 @@ __device__ __forceinline__ void waitcnt_vm_lgkm0() {
 __device__ __forceinline__ void barrier_after_vmcnt(int n) {
     switch (n) {
         // the counts in use; anything else waits for all
-        case 1: waitcnt_vm_lgkm0<1>(); break;
+        case 7: waitcnt_vm_lgkm0<7>(); break;
         default: waitcnt_vm_lgkm0<0>(); break;
     }
     asm volatile("s_barrier" ::: "memory");
@@ -506,7 +506,13 @@ __device__ __forceinline__ void consume(int32_t v) { asm volatile("" ::"v"(v)); 
 // Keeps a value's computation at this point of the instruction stream (pure
 // arithmetic is otherwise free to move to its first use).
 __device__ __forceinline__ void pin(float& v) { asm volatile("" : "+v"(v)); }
-__device__ __forceinline__ void pin_s(int32_t& v) { asm volatile("" : "+s"(v)); }
+// The same for a wave-uniform value kept in a scalar register (the
+// readfirstlane costs nothing where the compiler already knows the value is
+// uniform, and makes it legal where it cannot prove it).
+__device__ __forceinline__ void pin_s(int32_t& v) {
+    v = __builtin_amdgcn_readfirstlane(v);
+    asm volatile("" : "+s"(v));
+}
 
 // Buffer descriptor as four dwords (base, range in bytes, gfx9 untyped
 // format); offsets at or past `bytes` read as zero.
@@ -592,47 +598,55 @@ constexpr int kRowBytes = kPitch * 16;          // one key row in LDS
 constexpr int kWideKeys = 64;                      // keys per tile
 constexpr int kWideBufBytes = kWideKeys * kRowBytes;
 
-// One 64-key tile of one wave: step s issues the two MFMAs of k-step s (one
-// shared B operand), the LDS read of the operand of step s + kLead, one
-// element of the previous tile's epilogue in three independent pieces (FMA
-// of element s, exp of element s-1, sum of element s-2), and for s = 1..16
-// the load of gathered row s-1 of tile t+1 (its row offset read one step
-// earlier) to LDS address m0_rows + (s-1) m0_step (a step of 0 sends a tile
-// that has nothing to gather to one dummy row); `mid(s)` is the caller's
-// spread-out work. Before step 0, after the LDS reads of the first kLead
-// operands, `pre()` issues the caller's own LDS reads (so that the first
-// MFMA waits only for its operand); `offs()`, called in step 0, gives each
-// lane's byte offset of the row it gathers (lanes 0..15 used).
-template <bool BF16, typename Pre, typename Offs, typename Mid>
-__device__ __forceinline__ void qk_tile_wide(const uint4* __restrict__ src, const uint4* qa0,
-                                             const uint4* qa1, int col, int half,
-                                             const f32x16_t& prev0, const f32x16_t& prev1,
-                                             const float* l2, float c, float* prev_sum,
-                                             i32x4_t kdesc, uint32_t m0_rows, uint32_t m0_step,
-                                             Pre pre, Offs offs, uint32_t voff, Mid mid,
-                                             f32x16_t& acc0, f32x16_t& acc1) {
+// One 64-key tile t of one wave, 32 steps. Step s issues the two MFMAs of
+// k-step s (one shared B operand, from an 8-deep ring of operand registers),
+// the LDS read of the operand 8 steps ahead, one element of the previous
+// tile's epilogue in three independent pieces (FMA of element s, exp of
+// element s-1, sum of element s-2), and the gather loads of this wave's 16
+// rows of later tiles: rows 7..15 of tile t+1 at steps 1..9 (from `offa`,
+// to LDS address m0a + (r-7) stepa) and rows 0..6 of tile t+2 at steps
+// 25..31 (offsets from `offs_b(key_b())`: the key read in step 12, the
+// offsets formed in step 20, so that no step waits for an LDS read issued
+// just before it; returned in `offb` for the next tile; to m0b + r stepb). A step of 0 sends loads of a tile
+// that does not exist to one dummy row. Each row offset is read into a
+// scalar register one step before its load.
+//
+// The workgroup barrier sits after the MFMAs of step kBar = 24: by then every
+// wave has read its last operand of tile t (step 31's, read in step 23) and
+// waited for its own loads of tile t+1 (the last issued in step 9), so after
+// it the operand reads run on into tile t+1 (`nxt`) and the loads of tile
+// t+2 may overwrite tile t's buffer. Tile boundaries then need no barrier and
+// the MFMA stream does not drain between tiles. `mid(s)` is the caller's
+// spread-out work, called at the end of step s.
+constexpr int kBarStep = 24;
+template <bool BF16, typename Key, typename Offs, typename Mid>
+__device__ __forceinline__ void wide_tile(const uint4* __restrict__ cur,
+                                          const uint4* __restrict__ nxt, uint4 (&ring)[8],
+                                          const uint4* qa0, const uint4* qa1,
+                                          const f32x16_t& prev0, const f32x16_t& prev1,
+                                          const float* l2, float c, float* prev_sum,
+                                          i32x4_t kdesc, uint32_t m0a, uint32_t stepa,
+                                          int32_t offa, uint32_t m0b, uint32_t stepb,
+                                          Key key_b, Offs offs_b, int32_t& offb, uint32_t voff,
+                                          Mid mid,
+                                          f32x16_t& acc0, f32x16_t& acc1) {
     constexpr int kSteps = kChunks / 2;
     constexpr int kLead = 8;
-    const uint4* row = src + col * kPitch + half;
-    uint4 b[kSteps];
-#pragma unroll
-    for (int s = 0; s < kLead; ++s) b[s] = row[2 * s];
-    __builtin_amdgcn_sched_barrier(0);
-    pre();
-    __builtin_amdgcn_sched_barrier(0);
     acc0 = f32x16_t{};
     acc1 = f32x16_t{};
     float sum = 0.0f, t = 0.0f, ex = 0.0f;
-    int32_t soff = 0;
-    int32_t rows_off = 0;
-    int32_t m0 = (int32_t)m0_rows;
-    pin_s(m0);
+    int32_t soff = 0, soa = 0, kb = 0;
+    int32_t ma = (int32_t)m0a, mb = (int32_t)m0b;
+    pin_s(ma);
+    pin_s(mb);
 #pragma unroll
     for (int s = 0; s < kSteps; ++s) {
         __builtin_amdgcn_sched_barrier(0);
-        acc0 = mfma_32x32x16<BF16>(qa0[s], b[s], acc0);
-        acc1 = mfma_32x32x16<BF16>(qa1[s], b[s], acc1);
-        if (s + kLead < kSteps) b[s + kLead] = row[2 * (s + kLead)];
+        acc0 = mfma_32x32x16<BF16>(qa0[s], ring[s & 7], acc0);
+        acc1 = mfma_32x32x16<BF16>(qa1[s], ring[s & 7], acc1);
+        if (s == kBarStep) barrier_after_vmcnt(0);
+        ring[(s + kLead) & 7] =
+            s + kLead < kSteps ? cur[2 * (s + kLead)] : nxt[2 * (s + kLead - kSteps)];
         if (s >= 2) {
             sum += ex;
             pin(sum);
@@ -641,16 +655,32 @@ __device__ __forceinline__ void qk_tile_wide(const uint4* __restrict__ src, cons
             ex = __builtin_amdgcn_exp2f(t);
             pin(ex);
         }
-        t = __builtin_fmaf(s < 16 ? prev0[s] : prev1[s - 16], c, -l2[s]);
+        // the previous tile's score, read from the accumulator register where
+        // its MFMAs left it (left to the compiler, the whole accumulator set is
+        // copied out before the first MFMA of the tile, which then waits for
+        // the last MFMA of the previous tile to drain); the last write to it
+        // is at least a step and the tail of the previous tile away
+        float pv;
+        asm volatile("v_accvgpr_read_b32 %0, %1" : "=v"(pv) : "a"(s < 16 ? prev0[s] : prev1[s - 16]));
+        t = __builtin_fmaf(pv, c, -l2[s]);
         pin(t);
-        if (s >= 1 && s <= 16) {
-            dma_row(kdesc, (uint32_t)m0, soff, voff);
-            m0 += (int32_t)m0_step;
-            pin_s(m0);
+        if (s >= 1 && s <= 9) {  // stream A: row s + 6 of tile t+1
+            dma_row(kdesc, (uint32_t)ma, soa, voff);
+            ma += (int32_t)stepa;
+            pin_s(ma);
         }
-        if (s == 0) rows_off = offs();
-        if (s < 16) {
-            soff = __builtin_amdgcn_readlane(rows_off, s);
+        if (s >= 25) {  // stream B: row s - 25 of tile t+2
+            dma_row(kdesc, (uint32_t)mb, soff, voff);
+            mb += (int32_t)stepb;
+            pin_s(mb);
+        }
+        if (s == 12) kb = key_b();
+        if (s == 20) offb = offs_b(kb);
+        if (s <= 8) {
+            soa = __builtin_amdgcn_readlane(offa, s + 7);
+            pin_s(soa);
+        } else if (s >= 24 && s <= 30) {
+            soff = __builtin_amdgcn_readlane(offb, s - 24);
             pin_s(soff);
         }
         mid(s);
@@ -670,6 +700,7 @@ __global__ __launch_bounds__(256, 1) void smla_wide_kernel(KernelArgs a) {
     __shared__ uint4 kbuf[2][kWideKeys * kPitch];     // tile t in buffer t % 2
     __shared__ int32_t ibuf[2][kVcap];                // index lists: this row, next row
     __shared__ float red[2][4][kWideKeys];            // partial sums, last two tiles
+    __shared__ float redl[4][kWideKeys];              // partial sums of a row's last tile
     __shared__ float lsebuf[HT * 32];                 // the next row's lse
     __shared__ uint4 dummy[64];                       // loads of a tile with nothing to gather
 
@@ -745,8 +776,12 @@ __global__ __launch_bounds__(256, 1) void smla_wide_kernel(KernelArgs a) {
         }
 #pragma unroll
         for (int e = 0; e < 32; ++e) {
+            // (the read is unconditional, h < 128 always, and the padding
+            // heads take +inf by a select: a conditional read compiles to a
+            // branch per element)
             const int h = 64 * hg + 32 * (e >> 4) + 8 * ((e & 15) >> 2) + 4 * half + (e & 3);
-            l2[e] = h < a.G ? lsebuf[h] * kLog2e : __builtin_inff();
+            const float v = lsebuf[h];
+            l2[e] = h < a.G ? v * kLog2e : __builtin_inff();
         }
     };
     // the next row of this workgroup, decoded (its scalar loads waited for
@@ -767,15 +802,21 @@ __global__ __launch_bounds__(256, 1) void smla_wide_kernel(KernelArgs a) {
         return (tile * kWideKeys + my_slot < ri.n && (uint32_t)j < (uint32_t)ri.vis) ? (j << 10)
                                                                                        : 0;
     };
-    // a row's first tile into buffer 0 (its index list is in ibuf[slot])
-    auto start_row = [&](const RowInfo& ri, int slot) {
-        if (ntiles_of(ri) == 0) return;
+    // A row's start: tile 0 (16 rows) into buffer 0 and rows 0..6 of tile 1
+    // into buffer 1 (to the dummy row when there is no tile 1), 23 loads in
+    // all for a row with tiles; returns each lane's row offset in tile 1 for
+    // the loads of its rows 7..15 in tile 0.
+    auto start_row = [&](const RowInfo& ri, int slot) -> int32_t {
+        const int nt = __builtin_amdgcn_readfirstlane(ntiles_of(ri));  // uniform
+        if (nt == 0) return 0;
         const i32x4_t kd = k_desc(ri);
-        const int32_t o = row_off(ri, 0, ibuf[slot][my_slot]);
+        const int32_t* il = ibuf[slot];
+        const int32_t o0 = row_off(ri, 0, il[my_slot]);
+        const int32_t o1 = row_off(ri, 1, nt > 1 ? il[kWideKeys + my_slot] : 0);
         int32_t so[kRowsPerWave];
 #pragma unroll
         for (int i = 0; i < kRowsPerWave; ++i) {
-            so[i] = __builtin_amdgcn_readlane(o, i);
+            so[i] = __builtin_amdgcn_readlane(o0, i);
             pin_s(so[i]);
         }
         int32_t m0 = (int32_t)(kbuf_lds + (uint32_t)(kRowsPerWave * wave * kRowBytes));
@@ -786,6 +827,23 @@ __global__ __launch_bounds__(256, 1) void smla_wide_kernel(KernelArgs a) {
             m0 += kRowBytes;
             pin_s(m0);
         }
+#pragma unroll
+        for (int i = 0; i < 7; ++i) {
+            so[i] = __builtin_amdgcn_readlane(o1, i);
+            pin_s(so[i]);
+        }
+        const int32_t step1 = nt > 1 ? kRowBytes : 0;
+        m0 = __builtin_amdgcn_readfirstlane(
+            (int32_t)(nt > 1 ? kbuf_lds + (uint32_t)(kWideBufBytes + kRowsPerWave * wave * kRowBytes)
+                             : dummy_lds));
+        pin_s(m0);
+#pragma unroll
+        for (int i = 0; i < 7; ++i) {
+            dma_row(kd, (uint32_t)m0, so[i], voff16);
+            m0 += step1;
+            pin_s(m0);
+        }
+        return o1;
     };
 
     // ---- first row: operands, index list and zeroed output, then tile 0 in
@@ -797,18 +855,20 @@ __global__ __launch_bounds__(256, 1) void smla_wide_kernel(KernelArgs a) {
     barrier_after_vmcnt(0);
     read_q_lse();
     lds_barrier();
-    start_row(ric, 0);
+    int32_t offa = start_row(ric, 0);
+    uint4 ring[8];
 
     for (; it * a.num_wg < a.R && rc < a.R; ++it) {
-        const int ntiles = ntiles_of(ric);
+        // (uniform, but the compiler cannot always see it: say so, so that
+        // the LDS addresses derived from it stay in scalar registers)
+        const int ntiles = __builtin_amdgcn_readfirstlane(ntiles_of(ric));
         const i32x4_t kdesc = k_desc(ric);
         const int32_t* __restrict__ irow = ibuf[ib];
         // Finish entry `e` = tile*64 + slot (slot 16 w + lane for lanes < 16):
         // the sum of its four partial sums over G, stored to its column if
         // the entry is used. The store is one buffer store per call whatever
         // the lanes hold (lanes with nothing to store give an offset past
-        // the row, which the buffer range check drops), so the wave's
-        // memory-operation count is known.
+        // the row, which the buffer range check drops).
         const int slot = (kRowsPerWave * wave + lane) & (kWideKeys - 1);
         const int64_t obytes = a.W * 4;
         const __amdgpu_buffer_rsrc_t orsrc = __builtin_amdgcn_make_buffer_rsrc(
@@ -824,77 +884,87 @@ __global__ __launch_bounds__(256, 1) void smla_wide_kernel(KernelArgs a) {
                 used ? (int)((uint32_t)(ric.col0 + j) * 4u) : 0x7ffffff0, 0, 0);
         };
 
+        // tile 0 has landed (tile 1's first rows may still be in flight);
+        // the operands of its first 8 steps into the ring
+        barrier_after_vmcnt(7);
+        {
+            const uint4* r0 = kbuf[0] + (32 * kh + col) * kPitch + half;
+#pragma unroll
+            for (int i = 0; i < 8; ++i) ring[i] = r0[2 * i];
+        }
         f32x16_t xa0, xa1, xb0 = {}, xb1 = {};
-        // memory operations this wave issued after the gather of the tile
-        // about to start: the previous tile's value store (none before the
-        // row's first tile)
-        int later = 0;
         auto body = [&](int tile, const f32x16_t& prev0, const f32x16_t& prev1, f32x16_t& acc0,
                         f32x16_t& acc1) {
-            const bool gather = tile + 1 < ntiles;
-            // wait for the gather of this tile (issued in tile-1, or at the
-            // row start) and everything before it
-            barrier_after_vmcnt(later);
-            int32_t key = 0, jv = -1;
-            float parts[4];
-            const int pb = tile & 1;  // parity of tile - 2
-            auto pre = [&]() {
-                key = irow[((tile + 1) & 31) * kWideKeys + my_slot];
-#pragma unroll
-                for (int p = 0; p < 4; ++p) parts[p] = red[pb][p][slot];
-                jv = irow[((tile - 2) & 31) * kWideKeys + slot];
+            const bool has1 = tile + 1 < ntiles, has2 = tile + 2 < ntiles;
+            const uint4* cur = kbuf[tile & 1] + (32 * kh + col) * kPitch + half;
+            const uint4* nxt = kbuf[(tile + 1) & 1] + (32 * kh + col) * kPitch + half;
+            const uint32_t m0a = __builtin_amdgcn_readfirstlane(
+                has1 ? kbuf_lds + (uint32_t)(((tile + 1) & 1) * kWideBufBytes +
+                                             (kRowsPerWave * wave + 7) * kRowBytes)
+                     : dummy_lds);
+            const uint32_t m0b = __builtin_amdgcn_readfirstlane(
+                has2 ? kbuf_lds + (uint32_t)((tile & 1) * kWideBufBytes +
+                                             kRowsPerWave * wave * kRowBytes)
+                     : dummy_lds);
+            int32_t jv = -1, offb = 0;
+            float parts[4], tot = 0.0f, sum_prev;
+            auto key_b = [&]() -> int32_t { return irow[((tile + 2) & 31) * kWideKeys + my_slot]; };
+            auto offs_b = [&](int32_t key) -> int32_t {
+                return row_off(ric, tile + 2, has2 ? key : 0);
             };
-            auto offs = [&]() -> int32_t { return row_off(ric, tile + 1, gather ? key : 0); };
-            const uint32_t m0_rows =
-                gather ? kbuf_lds + (uint32_t)(((tile + 1) & 1) * kWideBufBytes +
-                                               kRowsPerWave * wave * kRowBytes)
-                       : dummy_lds;
-            const uint32_t m0_step = gather ? (uint32_t)kRowBytes : 0u;
-            float tot = 0.0f;
-            float sum_prev;
-            qk_tile_wide<BF16>(
-                kbuf[tile & 1] + 32 * kh * kPitch, qa0, qa1, col, half, prev0, prev1, l2,
-                a.c_scale, &sum_prev, kdesc, m0_rows, m0_step, pre, offs, voff16,
+            wide_tile<BF16>(
+                cur, nxt, ring, qa0, qa1, prev0, prev1, l2, a.c_scale, &sum_prev, kdesc, m0a,
+                has1 ? (uint32_t)kRowBytes : 0u, offa, m0b, has2 ? (uint32_t)kRowBytes : 0u,
+                key_b, offs_b, offb, voff16,
                 [&](int s) {
-                    if (s == 2) {
+                    // (each LDS read is used a few steps after it is issued)
+                    if (s == 20) {
+                        jv = irow[((tile - 2) & 31) * kWideKeys + slot];
+                    } else if (s == kBarStep + 2) {
+                        // tile-2's partial sums, written at the end of tile-1
+                        // and visible after the barrier
+#pragma unroll
+                        for (int p = 0; p < 4; ++p) parts[p] = red[tile & 1][p][slot];
+                    } else if (s == kBarStep + 4) {
                         tot = parts[0] + parts[1];
                         pin(tot);
-                    } else if (s == 3) {
+                    } else if (s == kBarStep + 5) {
                         tot += parts[2];
                         pin(tot);
-                    } else if (s == 4) {
+                    } else if (s == kBarStep + 6) {
                         tot += parts[3];
                         pin(tot);
-                    } else if (s == 20) {
+                    } else if (s == kBarStep + 7) {
                         store_value(tile - 2, tot, tile >= 2 ? jv : -1);
                     }
                 },
                 acc0, acc1);
+            offa = offb;
             red[(tile - 1) & 1][2 * hg + half][32 * kh + col] = sum_prev;  // tile 0: unused
         };
         for (int tile = 0; tile < ntiles; tile += 2) {
             body(tile, xb0, xb1, xa0, xa1);
-            later = 1;
             if (tile + 1 >= ntiles) break;
             body(tile + 1, xa0, xa1, xb0, xb1);
         }
         const f32x16_t& prev0 = (ntiles & 1) ? xa0 : xb0;
         const f32x16_t& prev1 = (ntiles & 1) ? xa1 : xb1;
+        // (the last tile's sums go to their own buffer: other waves may still
+        // be reading red[(ntiles - 1) & 1] in the last tile)
         if (ntiles > 0)
-            red[(ntiles - 1) & 1][2 * hg + half][32 * kh + col] =
+            redl[2 * hg + half][32 * kh + col] =
                 head_sum(prev0, l2, a.c_scale) + head_sum(prev1, l2 + 16, a.c_scale);
 
-        // all MFMAs done and every gather of this row has landed: K buffers
-        // are free; partial sums visible
+        // all MFMAs done, every operand read done and every gather of this
+        // row landed (only loads to the dummy row may be in flight): K
+        // buffers are free; partial sums visible
         lds_barrier();
-        auto finish = [&](int tile) {
-            const int pb = tile & 1;
-            const float tot = red[pb][0][slot] + red[pb][1][slot] + red[pb][2][slot] +
-                              red[pb][3][slot];
+        auto finish = [&](const float (*pr)[kWideKeys], int tile) {
+            const float tot = pr[0][slot] + pr[1][slot] + pr[2][slot] + pr[3][slot];
             store_value(tile, tot, irow[tile * kWideKeys + slot]);
         };
-        if (ntiles >= 2) finish(ntiles - 2);
-        if (ntiles >= 1) finish(ntiles - 1);
+        if (ntiles >= 2) finish(red[ntiles & 1], ntiles - 2);
+        if (ntiles >= 1) finish(redl, ntiles - 1);
 
         // the next row: index list and zeroed output, then Q into the K
         // buffers and lse; every wave reads its heads back, then buffer 0
@@ -906,7 +976,7 @@ __global__ __launch_bounds__(256, 1) void smla_wide_kernel(KernelArgs a) {
             barrier_after_vmcnt(0);
             read_q_lse();
             lds_barrier();
-            start_row(rin, ib ^ 1);
+            offa = start_row(rin, ib ^ 1);
         }
 
         // the next row becomes current

@@ -1,25 +1,29 @@
 """Host-side model of the pipelined kernel's vector-memory wait counts.
 
-Each tile barrier of smla_wide_kernel waits with vmcnt(later): at most
-`later` of the wave's own vector-memory instructions may still be in flight.
-Vector memory completes in issue order, so the wait covers every instruction
-issued more than `later` instructions before it. This test replays one
-wave's issue order over rows of random tile counts, in the kernel's order:
+smla_wide_kernel waits with vmcnt(n): at most n of the wave's own
+vector-memory instructions may still be in flight. Vector memory completes
+in issue order, so the wait covers every instruction issued more than n
+instructions before it. This test replays one wave's issue order over rows
+of random tile counts, in the kernel's order:
 
   * first row: its index list (8 loads), Q (32), lse (1), the zero-fill of
-    its output, a wait for everything, then the gather of tile 0 (16);
-  * tile t: barrier; the gather of tile t+1 (16 loads, into a dummy row
-    when there is no tile t+1); one value store (always issued: lanes with
-    nothing to store point past the row);
+    its output, a wait for everything;
+  * row start: the gather of tile 0 (16 loads) and of rows 0..6 of tile 1
+    (7 loads, to a dummy row when there is no tile 1), then a wait that
+    leaves the last 7 in flight, and the barrier;
+  * tile t, steps 1..9: rows 7..15 of tile t+1 (stream A); step 24: a wait
+    for everything and the barrier (after which the operands of tile t+1
+    are read); steps 25..31: rows 0..6 of tile t+2 (stream B), then the
+    value store of the step sequence;
   * row end: the value stores of the last two tiles, the zero-fill of the
     next row's output, its index list (8), Q (32) and lse (1), a wait for
-    everything, then the gather of its tile 0.
+    everything, then the next row's start.
 
-It checks that the kernel's count `later` covers, at every barrier, the
-gather of the tile and the zero-fill of the row, that the index list of a
-row has landed before its first tile reads it, and that every value the
-count takes has a case in the kernel's wait switch (anything else would fall
-back to waiting for everything: correct but slow).
+It checks that each wait covers the loads of the tile whose operands are read
+after it, the zero-fill of the row before its first value store and the
+index list before its first read, and that every count the kernel uses has a
+case in the kernel's wait switch (anything else would fall back to waiting
+for everything: correct but slow).
 """
 
 import os
@@ -28,8 +32,9 @@ import re
 
 KERNEL = os.path.join(os.path.dirname(__file__), os.pardir, "sparse_mla_attention_02_amd",
                       "csrc", "smla_kernels.hip")
-ROWS_PER_WAVE = 16   # gathered rows per wave and tile
 IDX_OPS = 8          # loads of one index list per wave
+ROW_START_LATER = 7  # tile 1's first rows, left in flight at a row start
+BAR_STEP = 24
 
 
 def switch_values():
@@ -39,14 +44,7 @@ def switch_values():
     return {int(v) for v in re.findall(r"case (\d+): waitcnt_vm_lgkm0", body)}
 
 
-def later_of(t, nt):
-    """The kernel's count after tile t (smla_wide_kernel, tile loop): the
-    value store of tile t."""
-    return 1
-
-
-def replay(rows, switch, rng, formula=None):
-    formula = formula or later_of
+def replay(rows, switch, rng, row_start_later=ROW_START_LATER, bar_later=0):
     stream, done = [], 0
 
     def issue(tag, n=1):
@@ -54,28 +52,38 @@ def replay(rows, switch, rng, formula=None):
 
     def wait(n):
         nonlocal done
+        assert n == 0 or n in switch, n
         done = max(done, len(stream) - n)
 
     def landed(tag):
         return all(i < done for i, x in enumerate(stream) if x == tag)
+
+    def gather(r, t, lo, hi, nt):
+        issue(("gather", r, t) if t < nt else ("dummy", r), hi - lo)
+
+    def row_start(r):
+        nt = rows[r]
+        if nt > 0:
+            gather(r, 0, 0, 16, nt)
+            gather(r, 1, 0, 7, nt)
+        wait(row_start_later)
+        assert landed(("gather", r, 0)), (rows, r)
 
     issue(("index list", 0), IDX_OPS)
     issue(("q", 0), 32)
     issue(("lse", 0))
     issue(("zero fill", 0), rng.randint(0, 12))
     wait(0)
-    if rows[0] > 0:
-        issue(("gather", 0, 0), ROWS_PER_WAVE)
+    row_start(0)
     for r, nt in enumerate(rows):
         more = r + 1 < len(rows)
         assert landed(("index list", r)) and landed(("zero fill", r)), (rows, r)
-        later = 0
         for t in range(nt):
-            wait(later if later in switch else 0)
-            assert landed(("gather", r, t)) and landed(("zero fill", r)), (rows, r, t)
-            issue(("gather", r, t + 1) if t + 1 < nt else ("dummy", r), ROWS_PER_WAVE)
-            issue(("store", r))
-            later = formula(t, nt)
+            gather(r, t + 1, 7, 16, nt)                  # steps 1..9
+            wait(bar_later)                              # step 24
+            assert landed(("gather", r, t + 1)), (rows, r, t)
+            gather(r, t + 2, 0, 7, nt)                   # steps 25..31
+            issue(("store", r))                          # step 31
         issue(("store", r), min(nt, 2))
         if more:
             issue(("zero fill", r + 1), rng.randint(0, 12))
@@ -84,17 +92,11 @@ def replay(rows, switch, rng, formula=None):
             issue(("q", r + 1), 32)
             issue(("lse", r + 1))
             wait(0)
-            if rows[r + 1] > 0:
-                issue(("gather", r + 1, 0), ROWS_PER_WAVE)
+            row_start(r + 1)
 
 
-def test_switch_has_every_count_the_formula_produces():
-    switch = switch_values()
-    produced = set()
-    for nt in range(0, 70):
-        for t in range(nt):
-            produced.add(later_of(t, nt))
-    assert produced - {0} <= switch, sorted(produced - switch)
+def test_switch_has_every_count_the_kernel_uses():
+    assert {ROW_START_LATER} <= switch_values()
 
 
 def test_waits_cover_each_tiles_loads():
@@ -106,16 +108,17 @@ def test_waits_cover_each_tiles_loads():
 
 
 def test_model_catches_a_too_lenient_wait():
-    # a planted mistake (a wait that lets the last 16 operations stay in
-    # flight: the gather of the tile) must be caught by the replay
-    def wrong(t, nt):
-        return 17
+    # planted mistakes must be caught: a row start that leaves tile 0's last
+    # row in flight, and a tile barrier that leaves stream A's last row in
+    # flight
     rng = random.Random(3)
-    caught = False
-    for _ in range(200):
-        try:
-            replay([rng.choice([5, 9, 17, 32]), 4], set(range(64)), rng, formula=wrong)
-        except AssertionError:
-            caught = True
-            break
-    assert caught
+    everything = set(range(64))
+    for kwargs in ({"row_start_later": 8}, {"bar_later": 1}):
+        caught = False
+        for _ in range(50):
+            try:
+                replay([rng.choice([3, 5, 9, 17, 32]), 4], everything, rng, **kwargs)
+            except AssertionError:
+                caught = True
+                break
+        assert caught, kwargs
