@@ -522,6 +522,12 @@ __device__ __forceinline__ i32x4_t raw_desc(const void* base, uint32_t bytes) {
     return i32x4_t{(int32_t)(uint32_t)p, (int32_t)((uint32_t)(p >> 32) & 0xffffu), (int32_t)bytes,
                    0x00020000};
 }
+// A descriptor chosen by a wave-uniform condition, kept in scalar registers
+// (the inline-asm loads take it as an "s" operand).
+__device__ __forceinline__ i32x4_t uniform_desc(i32x4_t d) {
+    return i32x4_t{__builtin_amdgcn_readfirstlane(d[0]), __builtin_amdgcn_readfirstlane(d[1]),
+                   __builtin_amdgcn_readfirstlane(d[2]), __builtin_amdgcn_readfirstlane(d[3])};
+}
 __device__ __forceinline__ uint32_t lds_addr(const void* p) {
     return (uint32_t)(uintptr_t)(__attribute__((address_space(3))) const void*)p;
 }
@@ -607,9 +613,11 @@ constexpr int kWideBufBytes = kWideKeys * kRowBytes;
 // to LDS address m0a + (r-7) stepa) and rows 0..6 of tile t+2 at steps
 // 25..31 (offsets from `offs_b(key_b())`: the key read in step 12, the
 // offsets formed in step 20, so that no step waits for an LDS read issued
-// just before it; returned in `offb` for the next tile; to m0b + r stepb). A step of 0 sends loads of a tile
-// that does not exist to one dummy row. Each row offset is read into a
-// scalar register one step before its load.
+// just before it; returned in `offb` for the next tile; to m0b + r
+// stepb). Each stream has its own buffer descriptor: a stream whose tile
+// does not exist loads rows of the next query row's Q into the free buffer
+// instead, or (a step of 0) sends its loads to one dummy row. Each row
+// offset is read into a scalar register one step before its load.
 //
 // The workgroup barrier sits after the MFMAs of step kBar = 24: by then every
 // wave has read its last operand of tile t (step 31's, read in step 23) and
@@ -625,7 +633,8 @@ __device__ __forceinline__ void wide_tile(const uint4* __restrict__ cur,
                                           const uint4* qa0, const uint4* qa1,
                                           const f32x16_t& prev0, const f32x16_t& prev1,
                                           const float* l2, float c, float* prev_sum,
-                                          i32x4_t kdesc, uint32_t m0a, uint32_t stepa,
+                                          i32x4_t desc_a, i32x4_t desc_b, uint32_t m0a,
+                                          uint32_t stepa,
                                           int32_t offa, uint32_t m0b, uint32_t stepb,
                                           Key key_b, Offs offs_b, int32_t& offb, uint32_t voff,
                                           Mid mid,
@@ -644,6 +653,9 @@ __device__ __forceinline__ void wide_tile(const uint4* __restrict__ cur,
         __builtin_amdgcn_sched_barrier(0);
         acc0 = mfma_32x32x16<BF16>(qa0[s], ring[s & 7], acc0);
         acc1 = mfma_32x32x16<BF16>(qa1[s], ring[s & 7], acc1);
+        // keeps the MFMAs in their step (as pure operations they may
+        // otherwise be sunk towards the far uses of the accumulators)
+        asm volatile("" ::"a"(acc0), "a"(acc1));
         if (s == kBarStep) barrier_after_vmcnt(0);
         ring[(s + kLead) & 7] =
             s + kLead < kSteps ? cur[2 * (s + kLead)] : nxt[2 * (s + kLead - kSteps)];
@@ -665,12 +677,12 @@ __device__ __forceinline__ void wide_tile(const uint4* __restrict__ cur,
         t = __builtin_fmaf(pv, c, -l2[s]);
         pin(t);
         if (s >= 1 && s <= 9) {  // stream A: row s + 6 of tile t+1
-            dma_row(kdesc, (uint32_t)ma, soa, voff);
+            dma_row(desc_a, (uint32_t)ma, soa, voff);
             ma += (int32_t)stepa;
             pin_s(ma);
         }
         if (s >= 25) {  // stream B: row s - 25 of tile t+2
-            dma_row(kdesc, (uint32_t)mb, soff, voff);
+            dma_row(desc_b, (uint32_t)mb, soff, voff);
             mb += (int32_t)stepb;
             pin_s(mb);
         }
@@ -787,13 +799,29 @@ __global__ __launch_bounds__(256, 1) void smla_wide_kernel(KernelArgs a) {
     // the next row of this workgroup, decoded (its scalar loads waited for
     // here, so that later LDS waits can count), its output zero-filled and
     // its index list loaded
-    auto prepare_next = [&]() {
+    auto decode_next = [&]() {
         rn = (it + 1) * a.num_wg < a.R ? row_of(a, it + 1, blockIdx.x) : a.R;
         rln = rn < a.R ? rn : rc;  // the last row loads itself again (unused)
         rin = decode_row<TND>(a, rln);
         waitcnt_vm_lgkm0<63>();
+    };
+    auto prepare_next = [&]() {
         if (rn < a.R) zero_span(a.out + rn * a.W, 0, a.W, tid, NT);
         load_idx_row(rln, ib ^ 1);
+    };
+    // Q of row r, heads 64 buf + 16 w + i for i in [i0, i1), into rows
+    // 16 w + i of K buffer buf (the layout in which the last tiles of a row
+    // stage the next row's Q in the buffers they free)
+    auto stage_q_rows = [&](int64_t r, int buf, int i0, int i1) {
+        const i32x4_t qd = raw_desc(q4 + r * a.G * kChunks, (uint32_t)a.G * 1024u);
+        for (int i = i0; i < i1; ++i) {
+            // (uniform; said so for the scalar operands of the load)
+            const uint32_t m0 = __builtin_amdgcn_readfirstlane(
+                kbuf_lds + (uint32_t)(buf * kWideBufBytes + (kRowsPerWave * wave + i) * kRowBytes));
+            const int32_t so =
+                __builtin_amdgcn_readfirstlane((64 * buf + kRowsPerWave * wave + i) * 1024);
+            dma_row_nt(qd, m0, so, voff16);
+        }
     };
     auto ntiles_of = [](const RowInfo& ri) { return (ri.n + kWideKeys - 1) / kWideKeys; };
     // byte offset of the key row of slot my_slot of `tile` holding raw index
@@ -863,6 +891,15 @@ __global__ __launch_bounds__(256, 1) void smla_wide_kernel(KernelArgs a) {
         // the LDS addresses derived from it stay in scalar registers)
         const int ntiles = __builtin_amdgcn_readfirstlane(ntiles_of(ric));
         const i32x4_t kdesc = k_desc(ric);
+        // the next row, decoded now: the last tiles of this row load its Q
+        decode_next();
+        const bool more = rn < a.R;
+        const i32x4_t qdesc = raw_desc(q4 + rln * a.G * kChunks, (uint32_t)a.G * 1024u);
+        // each lane's byte offset in Q of the head that rows 16 w + lane of
+        // K buffer buf take when it holds the next row's Q
+        auto q_off = [&](int buf) -> int32_t {
+            return (64 * buf + kRowsPerWave * wave + (lane & 15)) * 1024;
+        };
         const int32_t* __restrict__ irow = ibuf[ib];
         // Finish entry `e` = tile*64 + slot (slot 16 w + lane for lanes < 16):
         // the sum of its four partial sums over G, stored to its column if
@@ -896,25 +933,30 @@ __global__ __launch_bounds__(256, 1) void smla_wide_kernel(KernelArgs a) {
         auto body = [&](int tile, const f32x16_t& prev0, const f32x16_t& prev1, f32x16_t& acc0,
                         f32x16_t& acc1) {
             const bool has1 = tile + 1 < ntiles, has2 = tile + 2 < ntiles;
+            // streams whose tile does not exist take the next row's Q (stream
+            // A only from tile 1 on: tile 0's offsets come from the row start)
+            const bool qa = !has1 && more && tile >= 1, qb = !has2 && more;
             const uint4* cur = kbuf[tile & 1] + (32 * kh + col) * kPitch + half;
             const uint4* nxt = kbuf[(tile + 1) & 1] + (32 * kh + col) * kPitch + half;
             const uint32_t m0a = __builtin_amdgcn_readfirstlane(
-                has1 ? kbuf_lds + (uint32_t)(((tile + 1) & 1) * kWideBufBytes +
-                                             (kRowsPerWave * wave + 7) * kRowBytes)
-                     : dummy_lds);
+                has1 || qa ? kbuf_lds + (uint32_t)(((tile + 1) & 1) * kWideBufBytes +
+                                                   (kRowsPerWave * wave + 7) * kRowBytes)
+                           : dummy_lds);
             const uint32_t m0b = __builtin_amdgcn_readfirstlane(
-                has2 ? kbuf_lds + (uint32_t)((tile & 1) * kWideBufBytes +
-                                             kRowsPerWave * wave * kRowBytes)
-                     : dummy_lds);
+                has2 || qb ? kbuf_lds + (uint32_t)((tile & 1) * kWideBufBytes +
+                                                   kRowsPerWave * wave * kRowBytes)
+                           : dummy_lds);
             int32_t jv = -1, offb = 0;
             float parts[4], tot = 0.0f, sum_prev;
             auto key_b = [&]() -> int32_t { return irow[((tile + 2) & 31) * kWideKeys + my_slot]; };
             auto offs_b = [&](int32_t key) -> int32_t {
-                return row_off(ric, tile + 2, has2 ? key : 0);
+                return has2 ? row_off(ric, tile + 2, key) : (qb ? q_off(tile & 1) : 0);
             };
             wide_tile<BF16>(
-                cur, nxt, ring, qa0, qa1, prev0, prev1, l2, a.c_scale, &sum_prev, kdesc, m0a,
-                has1 ? (uint32_t)kRowBytes : 0u, offa, m0b, has2 ? (uint32_t)kRowBytes : 0u,
+                cur, nxt, ring, qa0, qa1, prev0, prev1, l2, a.c_scale, &sum_prev,
+                uniform_desc(has1 ? kdesc : qdesc), uniform_desc(has2 ? kdesc : qdesc), m0a,
+                has1 || qa ? (uint32_t)kRowBytes : 0u, offa, m0b,
+                has2 || qb ? (uint32_t)kRowBytes : 0u,
                 key_b, offs_b, offb, voff16,
                 [&](int s) {
                     // (each LDS read is used a few steps after it is issued)
@@ -966,12 +1008,18 @@ __global__ __launch_bounds__(256, 1) void smla_wide_kernel(KernelArgs a) {
         if (ntiles >= 2) finish(red[ntiles & 1], ntiles - 2);
         if (ntiles >= 1) finish(redl, ntiles - 1);
 
-        // the next row: index list and zeroed output, then Q into the K
-        // buffers and lse; every wave reads its heads back, then buffer 0
-        // takes the next row's first tile
+        // the next row: index list and zeroed output, then the rows of its Q
+        // the last tiles did not load (see the streams in the tile loop) and
+        // its lse; every wave reads its heads back, then buffer 0 takes the
+        // next row's first tile
         prepare_next();
-        if (rn < a.R) {
-            stage_q(rln, 0, HT * 32);
+        if (more) {
+            if (ntiles >= 2) {
+                stage_q_rows(rln, (ntiles - 1) & 1, 7, kRowsPerWave);
+            } else {
+                stage_q_rows(rln, 0, ntiles == 1 ? 7 : 0, kRowsPerWave);
+                stage_q_rows(rln, 1, 0, kRowsPerWave);
+            }
             stage_lse(rln);
             barrier_after_vmcnt(0);
             read_q_lse();
