@@ -86,6 +86,29 @@ __device__ __forceinline__ void zero_span(float* __restrict__ row, int64_t c0, i
     if (tid < c1 - t0) row[t0 + tid] = 0.0f;
 }
 
+// Writes row[0, w) from LDS (src[c] holds column c) with 16-byte
+// non-temporal stores where the row is 16-byte aligned, single floats for
+// the unaligned head and tail.
+__device__ __forceinline__ void write_row(float* __restrict__ row, const float* src, int64_t w,
+                                          int tid, int nt) {
+    const int64_t head = ((16 - (reinterpret_cast<uintptr_t>(row) & 15)) & 15) >> 2;
+    const int64_t h = head < w ? head : w;
+    if (tid < h) row[tid] = src[tid];
+    const int64_t n4 = (w - h) >> 2;
+    f32x4_t* o4 = reinterpret_cast<f32x4_t*>(row + h);
+    if (h == 0) {
+        const f32x4_t* s4 = reinterpret_cast<const f32x4_t*>(src);
+        for (int64_t i = tid; i < n4; i += nt) __builtin_nontemporal_store(s4[i], o4 + i);
+    } else {
+        for (int64_t i = tid; i < n4; i += nt) {
+            const float* p = src + h + 4 * i;
+            __builtin_nontemporal_store(f32x4_t{p[0], p[1], p[2], p[3]}, o4 + i);
+        }
+    }
+    const int64_t t0 = h + 4 * n4;
+    if (tid < w - t0) row[t0 + tid] = src[t0 + tid];
+}
+
 // Read-only int32 data at a wave-uniform address: the constant address
 // space lets the compiler use scalar loads (waited with lgkmcnt, so they do
 // not queue behind the vector loads in flight).
@@ -602,6 +625,7 @@ constexpr int kRowBytes = kPitch * 16;          // one key row in LDS
 // them while the MFMAs of tile t+1 fill the other set.
 
 constexpr int kWideKeys = 64;                      // keys per tile
+constexpr int kRowCap = 4096;                      // widest output row assembled in LDS
 constexpr int kWideBufBytes = kWideKeys * kRowBytes;
 
 // One 64-key tile t of one wave, 32 steps. Step s issues the two MFMAs of
@@ -703,14 +727,20 @@ __device__ __forceinline__ void wide_tile(const uint4* __restrict__ cur,
     *prev_sum = sum + ex;
 }
 
-template <bool BF16, bool TND>
+// ROWBUF (output rows of at most kRowCap columns): each row is assembled in
+// LDS (zeroed at the row start, values written as they are finished) and
+// written out once with 16-byte stores at the row end; the index list is then
+// single-buffered to make room. Otherwise rows are zero-filled in memory and
+// the values stored straight to their columns.
+template <bool BF16, bool TND, bool ROWBUF>
 __global__ __launch_bounds__(256, 1) void smla_wide_kernel(KernelArgs a) {
     constexpr int HT = 4;
     constexpr int NT = 256;
     constexpr int kRowsPerWave = kWideKeys / HT;      // gathered rows per wave and tile
     constexpr int kIdxOps = kVcap / 64 / HT;          // loads of one index list per wave
     __shared__ uint4 kbuf[2][kWideKeys * kPitch];     // tile t in buffer t % 2
-    __shared__ int32_t ibuf[2][kVcap];                // index lists: this row, next row
+    __shared__ int32_t ibuf[ROWBUF ? 1 : 2][kVcap];   // index lists: this row (, next row)
+    __shared__ __attribute__((aligned(16))) float rowbuf[ROWBUF ? kRowCap + 64 : 4];  // row, sinks
     __shared__ float red[2][4][kWideKeys];            // partial sums, last two tiles
     __shared__ float redl[4][kWideKeys];              // partial sums of a row's last tile
     __shared__ float lsebuf[HT * 32];                 // the next row's lse
@@ -806,8 +836,8 @@ __global__ __launch_bounds__(256, 1) void smla_wide_kernel(KernelArgs a) {
         waitcnt_vm_lgkm0<63>();
     };
     auto prepare_next = [&]() {
-        if (rn < a.R) zero_span(a.out + rn * a.W, 0, a.W, tid, NT);
-        load_idx_row(rln, ib ^ 1);
+        if (!ROWBUF && rn < a.R) zero_span(a.out + rn * a.W, 0, a.W, tid, NT);
+        load_idx_row(rln, ROWBUF ? 0 : ib ^ 1);
     };
     // Q of row r, heads 64 buf + 16 w + i for i in [i0, i1), into rows
     // 16 w + i of K buffer buf (the layout in which the last tiles of a row
@@ -879,7 +909,7 @@ __global__ __launch_bounds__(256, 1) void smla_wide_kernel(KernelArgs a) {
     load_idx_row(rc, 0);
     stage_q(rc, 0, HT * 32);
     stage_lse(rc);
-    zero_span(a.out + rc * a.W, 0, a.W, tid, NT);
+    if (!ROWBUF) zero_span(a.out + rc * a.W, 0, a.W, tid, NT);
     barrier_after_vmcnt(0);
     read_q_lse();
     lds_barrier();
@@ -915,12 +945,21 @@ __global__ __launch_bounds__(256, 1) void smla_wide_kernel(KernelArgs a) {
             const int e = tile * kWideKeys + slot;
             const bool used =
                 lane < kRowsPerWave && tile >= 0 && e < ric.n && (uint32_t)j < (uint32_t)ric.vis;
-            // (the builtin's data operand is an integer: pass the bits)
-            __builtin_amdgcn_raw_buffer_store_b32(
-                __builtin_bit_cast(uint32_t, tot * a.inv_g), orsrc,
-                used ? (int)((uint32_t)(ric.col0 + j) * 4u) : 0x7ffffff0, 0, 0);
+            if (ROWBUF) {
+                // (col0 + j < W <= kRowCap; other lanes write their own sink)
+                rowbuf[used ? (int)(ric.col0 + j) : kRowCap + lane] = tot * a.inv_g;
+            } else {
+                // (the builtin's data operand is an integer: pass the bits)
+                __builtin_amdgcn_raw_buffer_store_b32(
+                    __builtin_bit_cast(uint32_t, tot * a.inv_g), orsrc,
+                    used ? (int)((uint32_t)(ric.col0 + j) * 4u) : 0x7ffffff0, 0, 0);
+            }
         };
 
+        if (ROWBUF) {  // zeroed before the barrier, so before any value lands
+            for (int i = tid; i < (int)((a.W + 3) >> 2); i += NT)
+                reinterpret_cast<f32x4_t*>(rowbuf)[i] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+        }
         // tile 0 has landed (tile 1's first rows may still be in flight);
         // the operands of its first 8 steps into the ring
         barrier_after_vmcnt(7);
@@ -1007,6 +1046,12 @@ __global__ __launch_bounds__(256, 1) void smla_wide_kernel(KernelArgs a) {
         };
         if (ntiles >= 2) finish(red[ntiles & 1], ntiles - 2);
         if (ntiles >= 1) finish(redl, ntiles - 1);
+        if (ROWBUF) {
+            // every value is in the row buffer and every read of the index
+            // list is done: write the row out (16-byte stores where aligned)
+            lds_barrier();
+            write_row(a.out + rc * a.W, rowbuf, a.W, tid, NT);
+        }
 
         // the next row: index list and zeroed output, then the rows of its Q
         // the last tiles did not load (see the streams in the tile loop) and
@@ -1024,13 +1069,13 @@ __global__ __launch_bounds__(256, 1) void smla_wide_kernel(KernelArgs a) {
             barrier_after_vmcnt(0);
             read_q_lse();
             lds_barrier();
-            offa = start_row(rin, ib ^ 1);
+            offa = start_row(rin, ROWBUF ? 0 : ib ^ 1);
         }
 
         // the next row becomes current
         rc = rn;
         ric = rin;
-        ib ^= 1;
+        if (!ROWBUF) ib ^= 1;
     }
     // loads into LDS (the last tile's dummy loads) must land before the
     // workgroup's LDS is released
@@ -1039,14 +1084,19 @@ __global__ __launch_bounds__(256, 1) void smla_wide_kernel(KernelArgs a) {
 
 template <bool BF16, bool TND>
 hipError_t launch_wide_t(const KernelArgs& a, hipStream_t stream) {
-    hipLaunchKernelGGL((smla_wide_kernel<BF16, TND>), dim3(a.num_wg), dim3(256), 0, stream, a);
+    if (a.W <= kRowCap)
+        hipLaunchKernelGGL((smla_wide_kernel<BF16, TND, true>), dim3(a.num_wg), dim3(256), 0,
+                           stream, a);
+    else
+        hipLaunchKernelGGL((smla_wide_kernel<BF16, TND, false>), dim3(a.num_wg), dim3(256), 0,
+                           stream, a);
     return hipGetLastError();
 }
 
 template <bool BF16, bool TND>
 hipError_t occupancy_wide_t(int* out) {
     return hipOccupancyMaxActiveBlocksPerMultiprocessor(
-        out, reinterpret_cast<const void*>(&smla_wide_kernel<BF16, TND>), 256, 0);
+        out, reinterpret_cast<const void*>(&smla_wide_kernel<BF16, TND, true>), 256, 0);
 }
 
 template <int HT, bool BF16, bool TND>

@@ -152,6 +152,13 @@ def medium_cases():
     cs.append(("g96_no_topk_length", C.gen("tiny", heads_q=96, batch=1, seqlen_q=80,
                                             seqlen_k=500, topk=100, mask_mode=3,
                                             with_topk_length=False, seed=48)))
+    # rows wider than the 4096 columns the pipelined kernel assembles in LDS
+    # (it then zero-fills and stores values directly)
+    cs.append(("g128_w5000_direct", C.gen("tiny", heads_q=128, batch=1, seqlen_q=40,
+                                           seqlen_k=5000, topk=300, mask_mode=3, seed=50)))
+    cs.append(("tnd_g80_w5200_direct", C.gen("tnd_varlen", heads_q=80, topk=200,
+                                              seqlens_q=(30, 20), seqlens_k=(3000, 2200),
+                                              seed=51)))
     return cs
 
 

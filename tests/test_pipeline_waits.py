@@ -16,8 +16,12 @@ of random tile counts, in the kernel's order:
     are read); steps 25..31: rows 0..6 of tile t+2 (stream B), then the
     value store of the step sequence;
   * row end: the value stores of the last two tiles, the zero-fill of the
-    next row's output, its index list (8), Q (32) and lse (1), a wait for
-    everything, then the next row's start.
+    next row's output, its index list (8), the rest of its Q and lse (1), a
+    wait for everything, then the next row's start.
+
+With rows assembled in LDS (output rows of at most 4096 columns) the values
+go to LDS instead: no store in the tile loop and no zero-fill; the row end
+writes the whole row out before loading the next row's index list.
 
 It checks that each wait covers the loads of the tile whose operands are read
 after it, the zero-fill of the row before its first value store and the
@@ -44,7 +48,7 @@ def switch_values():
     return {int(v) for v in re.findall(r"case (\d+): waitcnt_vm_lgkm0", body)}
 
 
-def replay(rows, switch, rng, row_start_later=ROW_START_LATER, bar_later=0):
+def replay(rows, switch, rng, row_start_later=ROW_START_LATER, bar_later=0, rowbuf=False):
     stream, done = [], 0
 
     def issue(tag, n=1):
@@ -72,21 +76,27 @@ def replay(rows, switch, rng, row_start_later=ROW_START_LATER, bar_later=0):
     issue(("index list", 0), IDX_OPS)
     issue(("q", 0), 32)
     issue(("lse", 0))
-    issue(("zero fill", 0), rng.randint(0, 12))
+    if not rowbuf:
+        issue(("zero fill", 0), rng.randint(0, 12))
     wait(0)
     row_start(0)
     for r, nt in enumerate(rows):
         more = r + 1 < len(rows)
-        assert landed(("index list", r)) and landed(("zero fill", r)), (rows, r)
+        assert landed(("index list", r)), (rows, r)
+        assert rowbuf or landed(("zero fill", r)), (rows, r)
         for t in range(nt):
             gather(r, t + 1, 7, 16, nt)                  # steps 1..9
             wait(bar_later)                              # step 24
             assert landed(("gather", r, t + 1)), (rows, r, t)
             gather(r, t + 2, 0, 7, nt)                   # steps 25..31
-            issue(("store", r))                          # step 31
-        issue(("store", r), min(nt, 2))
-        if more:
-            issue(("zero fill", r + 1), rng.randint(0, 12))
+            if not rowbuf:
+                issue(("store", r))                      # step 31
+        if rowbuf:
+            issue(("row", r), rng.randint(1, 4))
+        else:
+            issue(("store", r), min(nt, 2))
+            if more:
+                issue(("zero fill", r + 1), rng.randint(0, 12))
         issue(("index list", r + 1), IDX_OPS)
         if more:
             issue(("q", r + 1), 32)
@@ -104,7 +114,7 @@ def test_waits_cover_each_tiles_loads():
     rng = random.Random(7)
     for _ in range(3000):
         rows = [rng.choice([0, 1, 2, 3, 4, 5, 6, 9, 17, 19, 32]) for _ in range(rng.randint(1, 5))]
-        replay(rows, switch, rng)
+        replay(rows, switch, rng, rowbuf=rng.random() < 0.5)
 
 
 def test_model_catches_a_too_lenient_wait():
