@@ -139,7 +139,8 @@ class _Args:
             qf = qf[torch.from_numpy(self.rows)]
         self.q = np.ascontiguousarray(qf.float().numpy())
         self.k = np.ascontiguousarray(p.k.reshape(-1, D).float().numpy())
-        self.idx = _c32(p.sparse_indices.reshape(R, p.topk))
+        # None: the dense case (every key of the row's sequence)
+        self.idx = None if p.sparse_indices is None else _c32(p.sparse_indices.reshape(R, p.topk))
         self.tlen = _c32(None if p.topk_length is None else p.topk_length.reshape(R))
         self.cu_q = _c32(p.cu_seqlens_q)
         self.cu_k = _c32(p.cu_seqlens_k)

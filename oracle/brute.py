@@ -12,7 +12,9 @@ heads under those masks. Everything is float64.
 
 The readings it takes are the same as the C oracle's (local TND indices,
 entries past ``topk_length`` / out of range / -1 ignored, compressed causal
-rule, natural-base exp, repeated indices counted twice).
+rule, natural-base exp, repeated indices counted twice). Without
+sparse_indices (the dense case, stage 1 selecting the whole K) the
+selection-count matrix is all ones.
 """
 
 from __future__ import annotations
@@ -50,6 +52,9 @@ def _pieces(p, b, qs, ks):
     else:
         vis = np.ones((s1, s2), dtype=bool)
 
+    if p.sparse_indices is None:
+        # dense: every key of the sequence is selected once
+        return S, np.ones((s1, s2), dtype=np.float64) * vis
     idx = p.sparse_indices.reshape(R, K)[qs].astype(np.int64)
     if p.topk_length is None:
         # selectBlockCount without topk_length: K, or (mask 3) no more than

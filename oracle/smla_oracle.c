@@ -9,6 +9,8 @@
  * ops-transformer, pnsm.cn),
  *   - section 三阶段计算公式 (three-stage formula):
  *       stage 1  selectedKv = Gather(K, sparseIndices[i]), i < selectBlockCount
+ *                in the sparse case, else selectedKv = K (the dense case,
+ *                no sparse_indices: every key of the row's batch/sequence)
  *       stage 2  P = SimpleSoftmax(Mask(Q selectedKv^T * scale), softmaxLse)
  *       stage 3  softmaxL1Norm = ReduceSum(P, dimG) / G,   G = N1 / N2
  *   - section 参数说明 (parameters) for layouts, cu_seqlens, topk_length,
@@ -31,7 +33,10 @@
  *   - SimpleSoftmax with the forward lse is exp(s - lse) in the natural base,
  *     the scale applied to Q.K^T before the lse is subtracted;
  *   - every output element not hit by a used entry is 0 (rows with no used
- *     entry are all 0); repeated indices accumulate.
+ *     entry are all 0); repeated indices accumulate;
+ *   - dense case (idx == NULL): the row's entries are its sequence's keys in
+ *     order, entry t being key t (n = S2_b); topk_length does not apply;
+ *     mask and output columns are those of the sparse case.
  *
  * The forward softmax_lse itself (oracle_lse) is not part of the operation:
  * it is the log-sum-exp over the same used entries that the forward pass
@@ -61,7 +66,7 @@ typedef struct {
 
 typedef struct {
     const float* k;          /* (B*S2 | T2, D) */
-    const int32_t* idx;      /* (R, K) */
+    const int32_t* idx;      /* (R, K), or NULL: the dense case */
     const int32_t* topk_len; /* (R) or NULL */
     const int32_t* cu_q;     /* (B+1) for TND */
     const int32_t* cu_k;
@@ -103,6 +108,7 @@ static int visible(const problem* p, const row_info* ri, int64_t j) {
 
 /* number of leading entries of row r that are looked at */
 static int64_t selected_count(const problem* p, const row_info* ri, int64_t r) {
+    if (!p->idx) return ri->s2; /* dense: selectedKv = K */
     if (!p->topk_len) {
         if (p->mask_mode == 0) return p->K;
         int64_t nvis = 0;  /* keys of the row's sequence it can see */
@@ -117,7 +123,7 @@ static int64_t selected_count(const problem* p, const row_info* ri, int64_t r) {
 
 /* key index of entry t if the entry is used, else -1 */
 static int64_t used_key(const problem* p, const row_info* ri, int64_t r, int64_t t) {
-    int64_t j = p->idx[r * p->K + t];
+    int64_t j = p->idx ? p->idx[r * p->K + t] : t;
     if (j < 0 || j >= ri->s2) return -1;
     if (!visible(p, ri, j)) return -1;
     return j;

@@ -46,7 +46,7 @@ def clone(p):
     c = copy.copy(p)
     c.q = p.q.clone()
     c.k = p.k.clone()
-    c.sparse_indices = p.sparse_indices.copy()
+    c.sparse_indices = None if p.sparse_indices is None else p.sparse_indices.copy()
     c.topk_length = None if p.topk_length is None else p.topk_length.copy()
     c.softmax_lse = None if p.softmax_lse is None else p.softmax_lse.copy()
     return c
@@ -100,8 +100,11 @@ def inject_edges(p, seed=0, invisible=True, out_of_range=True, shorten=True):
 
 
 def full_selection(p):
-    """Copy of p whose every row lists every key of its sequence, in order."""
+    """Copy of p whose every row lists every key of its sequence, in order
+    (a dense problem is returned as it is: it already selects every key)."""
     c = clone(p)
+    if c.sparse_indices is None:
+        return c
     s2max = max(k1 - k0 for (_, _, _, k0, k1) in seq_bounds(c))
     R = c.rows
     idx = np.full((R, s2max), -1, dtype=np.int32)
@@ -141,6 +144,14 @@ def tiny_cases():
     cs.append(("fp16_sigma", gen("tiny", heads_q=5, dtype="fp16", sigma=0.5, seed=19)))
     cs.append(("uniform2", gen("tiny", heads_q=4, dist="uniform2", seed=20)))
     edged = [(n + "+edges", inject_edges(p, seed=i)) for i, (n, p) in enumerate(cs)]
+    # the dense case (no sparse_indices: every key of the sequence)
+    cs.append(("dense_bsnd_mask0", gen("tiny", heads_q=3, batch=2, seqlen_q=4, seqlen_k=7,
+                                        topk=0, mask_mode=0, seed=21)))
+    cs.append(("dense_bsnd_causal", gen("tiny", heads_q=4, batch=1, seqlen_q=9,
+                                         seqlen_k=6, topk=0, mask_mode=3, seed=22)))
+    cs.append(("dense_tnd_cmp4", gen("tnd_varlen", heads_q=2, topk=0, cmp_ratio=4,
+                                      cmp_residual=(2, 0, 1), seqlens_q=(6, 1, 9),
+                                      seqlens_k=(3, 2, 4), seed=23)))
     return cs + edged
 
 

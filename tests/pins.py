@@ -62,7 +62,9 @@ def entry_counts(p):
         res = 0 if p.cmp_residual_k is None else int(p.cmp_residual_k[b])
         vis = library_visibility(q1 - q0, k1 - k0, p.cmp_ratio, res, p.mask_mode)
         for r in range(q0, q1):
-            if tl is not None:
+            if p.sparse_indices is None:  # dense: every key of the sequence
+                n[r] = k1 - k0
+            elif tl is not None:
                 n[r] = min(max(int(tl[r]), 0), K)
             else:
                 n[r] = K if p.mask_mode == 0 else min(K, int(vis[r - q0].sum()))
@@ -73,7 +75,8 @@ def used_entries(p):
     """Per row: (first k row, first output column, local key ids of the used
     entries in entry order)."""
     R, K = p.rows, p.topk
-    idx = p.sparse_indices.reshape(R, K)
+    dense = p.sparse_indices is None
+    idx = None if dense else p.sparse_indices.reshape(R, K)
     tl = None if p.topk_length is None else p.topk_length.reshape(R)
     out = [None] * R
     for (b, q0, q1, k0, k1) in C.seq_bounds(p):
@@ -81,6 +84,9 @@ def used_entries(p):
         res = 0 if p.cmp_residual_k is None else int(p.cmp_residual_k[b])
         vis = library_visibility(q1 - q0, s2, p.cmp_ratio, res, p.mask_mode)
         for r in range(q0, q1):
+            if dense:  # every key of the sequence, in order
+                out[r] = (k0, C.out_col0(p, b), [j for j in range(s2) if vis[r - q0, j]])
+                continue
             if tl is not None:
                 n = min(max(int(tl[r]), 0), K)
             else:  # mask 3: no more entries than visible keys
@@ -234,14 +240,16 @@ def pin_permutation(orc, problems):
         orc.fill_lse(a)
         o = orc.l1norm(a)
         rng = np.random.Generator(np.random.PCG64(200 + i))
-        # entry order within each row's first n entries
-        b = C.clone(a)
-        R, K = b.rows, b.topk
-        idx = b.sparse_indices.reshape(R, K)
-        for r, n in enumerate(entry_counts(b)):
-            idx[r, :n] = idx[r, :n][rng.permutation(n)]
-        ob = orc.l1norm(b)
-        np.testing.assert_array_equal(o, ob, err_msg=name)
+        # entry order within each row's first n entries (a dense problem has
+        # no index list to permute)
+        if a.sparse_indices is not None:
+            b = C.clone(a)
+            R, K = b.rows, b.topk
+            idx = b.sparse_indices.reshape(R, K)
+            for r, n in enumerate(entry_counts(b)):
+                idx[r, :n] = idx[r, :n][rng.permutation(n)]
+            ob = orc.l1norm(b)
+            np.testing.assert_array_equal(o, ob, err_msg=name)
         # joint head permutation of q and lse
         c = C.clone(a)
         perm = torch.from_numpy(rng.permutation(c.groups))

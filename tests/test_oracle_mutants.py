@@ -33,6 +33,7 @@ MUTANTS = {
     "ignore_cmp_ratio": ("int64_t r = p->cmp_ratio;", "int64_t r = 1;"),
     "ignore_topk_length": ("if (!p->topk_len) {", "if (1) {"),
     "no_visible_cap": ("return nvis < p->K ? nvis : p->K;", "return p->K;"),
+    "dense_drops_last_key": ("if (!p->idx) return ri->s2;", "if (!p->idx) return ri->s2 - 1;"),
     "lse_no_max_shift": ("lse = m + log(sum);", "lse = log(sum);"),
     "no_mask": ("if (p->mask_mode == 0) return 1;", "return 1;"),
     "s1_for_s2": ("ri->i + 1 + ri->s2 * r + res - ri->s1",

@@ -22,6 +22,8 @@ Recipe (stated once, used by every caller):
   ``i + S2_b*r + res - S1_b``; compressed key ``j`` covers original positions
   ``[j*r, (j+1)*r - 1]``; the prefix is every key whose last position is not
   after the query.
+* dense workloads (``topk=0``) draw no sparse_indices and no topk_length:
+  every key of a row's sequence is an entry (the page's dense case).
 * softmax_lse is NOT drawn here for parity work: tests take it from the
   oracle. ``lse_standin`` gives a cheap stand-in with the same shape and a
   realistic magnitude for timing runs, where the values do not change the
@@ -65,7 +67,7 @@ class Problem:
     dtype: str                  # "bf16" or "fp16"
     q: torch.Tensor             # (B,S1,N1,D) or (T1,N1,D), CPU
     k: torch.Tensor             # (B,S2,N2,D) or (T2,N2,D), CPU
-    sparse_indices: np.ndarray  # int32 (B,S1,N2,K) or (T1,N2,K)
+    sparse_indices: Optional[np.ndarray]  # int32 (B,S1,N2,K) or (T1,N2,K); None: dense
     topk_length: Optional[np.ndarray]      # int32 (B,S1,N2) or (T1,N2)
     cu_seqlens_q: Optional[np.ndarray]     # int32 (B+1,) for TND
     cu_seqlens_k: Optional[np.ndarray]
@@ -73,6 +75,7 @@ class Problem:
     max_seqlen_q: int
     max_seqlen_k: int
     softmax_lse: Optional[np.ndarray] = None  # float32 (B,N2,S1,G) or (N2,T1,G)
+    row_entries: Optional[np.ndarray] = None  # int64 (R,): keys drawn, or (dense) visible
 
     @property
     def groups(self) -> int:
@@ -99,8 +102,8 @@ class Problem:
         return (self.heads_k, self.seqlen_q, self.groups)
 
     def valid_pairs(self) -> int:
-        """Sum over rows of topk_length (the number of drawn keys)."""
-        return int(self.topk_length.astype(np.int64).sum())
+        """Sum over rows of the keys drawn (sparse) or visible (dense)."""
+        return int(self.row_entries.sum())
 
 
 @dataclasses.dataclass(frozen=True)
@@ -147,6 +150,14 @@ SPECS = {
                                 dtype="fp16", mask_mode=3, seqlens_q=(16,),
                                 seqlens_k=(2048,), cmp_ratio=128, cmp_residual=(0,),
                                 dist="uniform2", seed=6),
+    # Dense variant (no sparse_indices, every key of the sequence): the page's
+    # example itself, and a causal 2048x2048 BSND shape to measure.
+    "page_example_dense": Spec("page_example_dense", "TND", heads_q=128, topk=0,
+                               dtype="fp16", mask_mode=3, seqlens_q=(16,),
+                               seqlens_k=(2048,), cmp_ratio=128, cmp_residual=(0,),
+                               dist="uniform2", seed=6),
+    "dense_causal": Spec("dense_causal", "BSND", heads_q=128, topk=0, dtype="bf16",
+                         mask_mode=3, batch=1, seqlen_q=2048, seqlen_k=2048, seed=7),
 }
 
 
@@ -212,6 +223,7 @@ def generate(spec: Spec | str, seed: Optional[int] = None, **overrides) -> Probl
     k = torch.from_numpy(k32).to(tdt)
     del q32, k32
 
+    dense = K == 0
     idx = np.full((T1, K), -1, dtype=np.int32)
     tlen = np.zeros((T1,), dtype=np.int32)
     row = 0
@@ -220,11 +232,12 @@ def generate(spec: Spec | str, seed: Optional[int] = None, **overrides) -> Probl
         rb = res[b] if res is not None else 0
         for i in range(s1):
             L = visible_prefix(i, s1, s2, spec.mask_mode, r, rb)
-            n = min(K, L)
-            if n > 0:
+            n = L if dense else min(K, L)
+            if n > 0 and not dense:
                 idx[row, :n] = rng.choice(L, n, replace=False)
             tlen[row] = n
             row += 1
+    entries = tlen.astype(np.int64)
 
     scale = spec.softmax_scale if spec.softmax_scale is not None else 1.0 / math.sqrt(D)
     if spec.layout == "BSND":
@@ -246,10 +259,11 @@ def generate(spec: Spec | str, seed: Optional[int] = None, **overrides) -> Probl
         name=spec.name, layout=spec.layout, batch=B, seqlen_q=sq, seqlen_k=sk,
         heads_q=N1, heads_k=N2, head_dim=D, topk=K, mask_mode=spec.mask_mode,
         cmp_ratio=r, softmax_scale=scale, dtype=spec.dtype, q=q, k=k,
-        sparse_indices=idx, topk_length=tlen if spec.with_topk_length else None,
+        sparse_indices=None if dense else idx,
+        topk_length=tlen if spec.with_topk_length and not dense else None,
         cu_seqlens_q=cu_q, cu_seqlens_k=cu_k,
         cmp_residual_k=np.asarray(res, dtype=np.int32) if res is not None else None,
-        max_seqlen_q=mq, max_seqlen_k=mk,
+        max_seqlen_q=mq, max_seqlen_k=mk, row_entries=entries,
     )
 
 
@@ -261,8 +275,7 @@ def lse_standin(p: Problem) -> np.ndarray:
     k). The values only keep exp(s - lse) in a realistic range; they do not
     make rows sum to one. Rows with no drawn key get -inf.
     """
-    n = p.topk_length.reshape(-1).astype(np.float64) if p.topk_length is not None \
-        else np.full(p.rows, float(p.topk))
+    n = p.row_entries.astype(np.float64)
     v = p.head_dim * p.softmax_scale ** 2
     base = np.where(n > 0, np.log(np.maximum(n, 1.0)) + 0.5 * v, -np.inf)
     lse = np.repeat(base[:, None], p.groups, axis=1).astype(np.float32)
