@@ -47,8 +47,8 @@ enum {
     SMLA_SUCCESS = 0,
     SMLA_ERR_PARAM_NULLPTR = 161001,
     SMLA_ERR_PARAM_INVALID = 161002,
-    SMLA_ERR_UNSUPPORTED = 161101, /* valid on the page, not built here (dense
-                                      path without sparse_indices, seqused_q/k) */
+    SMLA_ERR_UNSUPPORTED = 161101, /* valid on the page, not built here
+                                      (seqused_q/k) */
     SMLA_ERR_RUNTIME = 561001      /* a HIP runtime call failed */
 };
 
@@ -76,8 +76,9 @@ enum { SMLA_MASK_NONE = 0, SMLA_MASK_RIGHT_DOWN_CAUSAL = 3 };
  *   [20] head tiles per row (kernel variant), [21] device, [22] CU count,
  *   [23] resident workgroups per CU,
  *   [24] kernel: 0 = general (one wave per 32-head tile, two workgroups
- *        per CU), 1 = pipelined (65..128 heads and topk <= 2048: one
- *        4-wave workgroup per CU, 64 heads per wave, 64-key tiles);
+ *        per CU), 1 = pipelined (65..128 heads with topk <= 2048 or the
+ *        dense case: one 4-wave workgroup per CU, 64 heads per wave,
+ *        64-key tiles);
  *        [25..63] zero.
  */
 #define SMLA_META_MAGIC 0x534D4C41
@@ -98,9 +99,13 @@ enum { SMLA_MASK_NONE = 0, SMLA_MASK_RIGHT_DOWN_CAUSAL = 3 };
  *   batch_size     B (> 0): batches for BSND, sequences for TND (the
  *                  length of cu_seqlens_q minus one)
  *   max_seqlen_q, max_seqlen_k  S1, S2: required > 0 for BSND (the padded
- *                  per-batch lengths); for TND 0 means "from cu_seqlens"
- *   topk           K, number of indices per row; must be >= 1 (0 = dense,
- *                  not supported)
+ *                  per-batch lengths); for TND 0 means "from cu_seqlens",
+ *                  and a non-zero max_seqlen_k must cover the longest k
+ *                  sequence
+ *   topk           K, number of indices per row, >= 0; 0 = the dense case
+ *                  (no sparse_indices: every key of the row's batch or
+ *                  sequence is an entry; stage 1 of the page's formula
+ *                  selects the whole K)
  *   layout_q, layout_k  SMLA_LAYOUT_*, must be equal
  *   mask_mode      0 or 3; cmp_ratio in [1,128]
  *   device         HIP device ordinal whose CU count sizes the grid
@@ -110,7 +115,7 @@ enum { SMLA_MASK_NONE = 0, SMLA_MASK_RIGHT_DOWN_CAUSAL = 3 };
  *
  * Errors: SMLA_ERR_PARAM_NULLPTR (metadata_host NULL, TND without
  * cu_seqlens), SMLA_ERR_PARAM_INVALID (out-of-range value, layout mismatch,
- * inconsistent cu_seqlens), SMLA_ERR_UNSUPPORTED (seqused_*, topk == 0),
+ * inconsistent cu_seqlens), SMLA_ERR_UNSUPPORTED (seqused_*),
  * SMLA_ERR_RUNTIME (device query failed; only when core_budget == 0).
  */
 smla_status_t smla_l1norm_metadata(
@@ -131,9 +136,11 @@ smla_status_t smla_l1norm_metadata(
  *   q              (B,S1,N1,D) | (T1,N1,D), dtype `dtype`
  *   k              (B,S2,N2,D) | (T2,N2,D), same dtype as q
  *   softmax_lse    fp32 (B,N2,S1,G) | (N2,T1,G), natural-log forward lse
- *   sparse_indices int32 (B,S1,N2,K) | (T1,N2,K); required (NULL selects
- *                  the page's dense path, which returns SMLA_ERR_UNSUPPORTED).
- *                  Entries index the keys of the row's own batch/sequence
+ *   sparse_indices int32 (B,S1,N2,K) | (T1,N2,K), or NULL for the dense
+ *                  case (then topk must be 0 and topk_length is ignored:
+ *                  entry t of a row is key t of its batch/sequence, every
+ *                  key in order). Entries index the keys of the row's own
+ *                  batch/sequence
  *                  (0-based, local to a TND sequence); an entry is used iff
  *                  its position is < the row's entry count (topk_length
  *                  below), it lies in [0, S2_b) and
@@ -146,8 +153,9 @@ smla_status_t smla_l1norm_metadata(
  *                  mask_mode == 3 and cmp_ratio != 1, else may be NULL (0)
  *   topk_length    int32 (B,S1,N2) | (T1,N2): entries per row to look at
  *                  (selectBlockCount), clamped to [0,K]; required when
- *                  mask_mode == 0; when NULL (mask_mode 3) a row looks at its
- *                  first min(K, keys visible to it) entries
+ *                  mask_mode == 0 with sparse_indices; when NULL (mask_mode
+ *                  3) a row looks at its first min(K, keys visible to it)
+ *                  entries
  *   metadata_host  int32[64] from smla_l1norm_metadata for the same shapes
  *   dtype          SMLA_DTYPE_FP16 or SMLA_DTYPE_BF16
  *   batch_size, seqlen_q, seqlen_k  B,S1,S2 (BSND) | B,T1,T2 (TND)
@@ -168,7 +176,7 @@ smla_status_t smla_l1norm_metadata(
  * is NULL (as on the page) or a value/shape is out of range or does not
  * match the metadata; SMLA_ERR_PARAM_NULLPTR when a conditionally required
  * pointer is NULL (metadata, cu_seqlens for TND, cmp_residual_k,
- * topk_length); SMLA_ERR_UNSUPPORTED for the dense path or seqused_*;
+ * topk_length); SMLA_ERR_UNSUPPORTED for seqused_*;
  * SMLA_ERR_RUNTIME if the launch fails. An empty q (R == 0) or an empty
  * output (S2/T2 == 0) returns SMLA_SUCCESS once the attributes are checked,
  * before any pointer or the metadata is looked at, and launches nothing.

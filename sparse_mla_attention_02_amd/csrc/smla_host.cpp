@@ -151,9 +151,8 @@ smla_status_t smla_l1norm_metadata(
     if (st != SMLA_SUCCESS) return st;
     if (seqused_q_host || seqused_k_host)
         return fail(SMLA_ERR_UNSUPPORTED, "seqused_q / seqused_k are not supported");
-    if (topk == 0)
-        return fail(SMLA_ERR_UNSUPPORTED, "topk == 0 (dense path) is not supported");
-    if (topk < 0) return fail(SMLA_ERR_PARAM_INVALID, "topk must be >= 1");
+    // topk == 0: the dense case (no sparse_indices)
+    if (topk < 0) return fail(SMLA_ERR_PARAM_INVALID, "topk must be >= 0");
     if (core_budget < 0) return fail(SMLA_ERR_PARAM_INVALID, "core_budget must be >= 0");
 
     int64_t B = batch_size, R = 0, rows_k = 0, mq = max_seqlen_q, mk = max_seqlen_k;
@@ -178,6 +177,9 @@ smla_status_t smla_l1norm_metadata(
             return fail(SMLA_ERR_PARAM_INVALID, "max_seqlen_q/k must be >= 0");
         if (mq == 0) mq = mxq;
         if (mk == 0) mk = mxk;
+        if (mk < mxk)
+            return fail(SMLA_ERR_PARAM_INVALID,
+                        "max_seqlen_k is smaller than the longest cu_seqlens_k sequence");
         R = tq;
         rows_k = tk;
     }
@@ -265,10 +267,14 @@ smla_status_t smla_softmax_l1norm(
     if (!q || !k || !softmax_lse || !softmax_l1_norm)
         return fail(SMLA_ERR_PARAM_INVALID,
                     "q, k, softmax_lse and softmax_l1_norm are required");
-    if (!sparse_indices)
-        return fail(SMLA_ERR_UNSUPPORTED,
-                    "the dense path (no sparse_indices) is not supported");
-    if (topk < 1) return fail(SMLA_ERR_PARAM_INVALID, "topk must be >= 1 with sparse_indices");
+    // no sparse_indices: the dense case, every key of the row's batch or
+    // sequence (stage 1 of the page's formula selects the whole K); topk
+    // is then 0 and topk_length does not apply
+    const bool dense = !sparse_indices;
+    if (dense && topk != 0)
+        return fail(SMLA_ERR_PARAM_INVALID, "topk must be 0 without sparse_indices");
+    if (!dense && topk < 1)
+        return fail(SMLA_ERR_PARAM_INVALID, "topk must be >= 1 with sparse_indices");
     if (!metadata_host)
         return fail(SMLA_ERR_PARAM_NULLPTR,
                     "metadata is required (from smla_l1norm_metadata)");
@@ -277,7 +283,7 @@ smla_status_t smla_softmax_l1norm(
     if (mask_mode == SMLA_MASK_RIGHT_DOWN_CAUSAL && cmp_ratio != 1 && !cmp_residual_k)
         return fail(SMLA_ERR_PARAM_NULLPTR,
                     "cmp_residual_k is required when mask_mode == 3 and cmp_ratio != 1");
-    if (mask_mode == SMLA_MASK_NONE && !topk_length)
+    if (!dense && mask_mode == SMLA_MASK_NONE && !topk_length)
         return fail(SMLA_ERR_PARAM_NULLPTR,
                     "topk_length is required when mask_mode == 0 with sparse_indices");
     if (R > INT32_MAX || rows_k > INT32_MAX || topk > INT32_MAX)
@@ -301,7 +307,7 @@ smla_status_t smla_softmax_l1norm(
     a.k = k;
     a.lse = softmax_lse;
     a.idx = sparse_indices;
-    a.topk_len = topk_length;
+    a.topk_len = dense ? nullptr : topk_length;
     a.cu_q = cu_seqlens_q;
     a.cu_k = cu_seqlens_k;
     a.cmp_res = cmp_residual_k;
@@ -313,7 +319,10 @@ smla_status_t smla_softmax_l1norm(
     a.S1 = tnd ? 0 : (int32_t)seqlen_q;
     a.S2 = tnd ? 0 : (int32_t)seqlen_k;
     a.G = (int32_t)(num_heads_q / num_heads_k);
-    a.K = (int32_t)topk;
+    // dense: entries per row at most the longest key sequence (S2, or the
+    // maximum of cu_seqlens_k as the metadata call resolved it)
+    a.K = dense ? (tnd ? m[13] : (int32_t)seqlen_k) : (int32_t)topk;
+    a.dense = dense ? 1 : 0;
     a.mask_mode = (int32_t)mask_mode;
     a.cmp_ratio = (int32_t)cmp_ratio;
     const float scale32 = (float)softmax_scale;  // the attribute is FLOAT32

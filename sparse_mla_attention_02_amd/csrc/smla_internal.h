@@ -11,7 +11,7 @@ struct KernelArgs {
     const void* q;            // (R, G, 512) bf16/fp16, N2 == 1 so N1 == G
     const void* k;            // (rows_k, 512) bf16/fp16
     const float* lse;         // (R, G) fp32
-    const int32_t* idx;       // (R, K) int32
+    const int32_t* idx;       // (R, K) int32; NULL when dense
     const int32_t* topk_len;  // (R) or nullptr
     const int32_t* cu_q;      // (B+1) for TND
     const int32_t* cu_k;      // (B+1) for TND
@@ -30,6 +30,7 @@ struct KernelArgs {
     float inv_g;              // 1 / G
     int32_t num_wg;           // workgroups launched (metadata field 4)
     int32_t snake;            // row order: 1 = snake, 0 = plain strided
+    int32_t dense;            // 1: no sparse_indices, entry t of a row is key t (idx NULL)
 };
 
 // Head tiles of 32 heads each that one row needs: 1, 2 or 4.

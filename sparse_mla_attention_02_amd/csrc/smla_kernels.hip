@@ -173,9 +173,13 @@ __device__ __forceinline__ RowInfo decode_row(const KernelArgs& a, int64_t r) {
         }
     }
     // entries to look at (selectBlockCount): topk_length clamped to [0, K];
-    // without it K, or under the causal mask no more than the visible keys
+    // without it K, or under the causal mask no more than the visible keys.
+    // Dense (no sparse_indices): the row's keys in order, so the visible ones
+    // are its leading entries
     int32_t n = a.K;
-    if (a.topk_len) {
+    if (a.dense) {
+        n = vis < a.K ? (int32_t)vis : a.K;
+    } else if (a.topk_len) {
         n = uload(a.topk_len, r);
         n = n < 0 ? 0 : (n > a.K ? a.K : n);
     } else if (a.mask_mode == 3 && vis < n) {
@@ -332,11 +336,14 @@ __global__ __launch_bounds__(64 * HT, 2) void smla_l1norm_kernel(KernelArgs a) {
         const int64_t seg0 = ri.col0;
         const int64_t seg1 = ri.col0 + (ntiles > 0 ? ri.vis : 0);
 
-        // raw index of slot `col` of a tile (any value; checked where used)
-        const __amdgpu_buffer_rsrc_t ridx = rsrc(irow, (uint32_t)a.K * 4u);
+        // raw index of slot `col` of a tile (any value; checked where used);
+        // dense: the entry itself (the descriptor then has no range, so the
+        // load reads nothing)
+        const __amdgpu_buffer_rsrc_t ridx = rsrc(irow, a.dense ? 0u : (uint32_t)a.K * 4u);
         auto tile_idx = [&](int tile) -> int32_t {
-            return __builtin_amdgcn_raw_buffer_load_b32(ridx, (uint32_t)(tile * kTile + col) * 4u,
-                                                        0, 0);
+            const int32_t e = tile * kTile + col;
+            const int32_t j = __builtin_amdgcn_raw_buffer_load_b32(ridx, (uint32_t)e * 4u, 0, 0);
+            return a.dense ? e : j;
         };
         // is slot kk of a tile, holding raw index j, a used entry?
         auto used = [&](int tile, int kk, int32_t j) -> bool {
@@ -433,9 +440,11 @@ __global__ __launch_bounds__(64 * HT, 2) void smla_l1norm_kernel(KernelArgs a) {
         int32_t jre[kPerThread];
         if (staged) {
 #pragma unroll
-            for (int i = 0; i < kPerThread; ++i)
-                jre[i] = __builtin_amdgcn_raw_buffer_load_b32(ridx, (uint32_t)(tid + i * NT) * 4u,
-                                                              0, 0);
+            for (int i = 0; i < kPerThread; ++i) {
+                const int32_t j = __builtin_amdgcn_raw_buffer_load_b32(
+                    ridx, (uint32_t)(tid + i * NT) * 4u, 0, 0);
+                jre[i] = a.dense ? tid + i * NT : j;
+            }
         }
         // unconditional (a clamped row when this is the last one), so the new
         // operands take over the registers of the old ones
@@ -783,6 +792,7 @@ __global__ __launch_bounds__(256, 1) void smla_wide_kernel(KernelArgs a) {
     // row r's index list into ibuf[slot] (kIdxOps loads; entries past K read
     // as zero)
     auto load_idx_row = [&](int64_t r, int slot) {
+        if (a.dense) return;  // no index list: entry t is key t
         const i32x4_t id = raw_desc(a.idx + r * a.K, (uint32_t)a.K * 4u);
 #pragma unroll
         for (int i = 0; i < kIdxOps; ++i) {
@@ -869,8 +879,9 @@ __global__ __launch_bounds__(256, 1) void smla_wide_kernel(KernelArgs a) {
         if (nt == 0) return 0;
         const i32x4_t kd = k_desc(ri);
         const int32_t* il = ibuf[slot];
-        const int32_t o0 = row_off(ri, 0, il[my_slot]);
-        const int32_t o1 = row_off(ri, 1, nt > 1 ? il[kWideKeys + my_slot] : 0);
+        const int32_t o0 = row_off(ri, 0, a.dense ? my_slot : il[my_slot]);
+        const int32_t o1 =
+            row_off(ri, 1, nt > 1 ? (a.dense ? kWideKeys + my_slot : il[kWideKeys + my_slot]) : 0);
         int32_t so[kRowsPerWave];
 #pragma unroll
         for (int i = 0; i < kRowsPerWave; ++i) {
@@ -987,7 +998,10 @@ __global__ __launch_bounds__(256, 1) void smla_wide_kernel(KernelArgs a) {
                            : dummy_lds);
             int32_t jv = -1, offb = 0;
             float parts[4], tot = 0.0f, sum_prev;
-            auto key_b = [&]() -> int32_t { return irow[((tile + 2) & 31) * kWideKeys + my_slot]; };
+            auto key_b = [&]() -> int32_t {
+                const int32_t j = irow[((tile + 2) & 31) * kWideKeys + my_slot];
+                return a.dense ? (tile + 2) * kWideKeys + my_slot : j;
+            };
             auto offs_b = [&](int32_t key) -> int32_t {
                 return has2 ? row_off(ric, tile + 2, key) : (qb ? q_off(tile & 1) : 0);
             };
@@ -1000,7 +1014,8 @@ __global__ __launch_bounds__(256, 1) void smla_wide_kernel(KernelArgs a) {
                 [&](int s) {
                     // (each LDS read is used a few steps after it is issued)
                     if (s == 20) {
-                        jv = irow[((tile - 2) & 31) * kWideKeys + slot];
+                        const int32_t j = irow[((tile - 2) & 31) * kWideKeys + slot];
+                        jv = a.dense ? (tile - 2) * kWideKeys + slot : j;
                     } else if (s == kBarStep + 2) {
                         // tile-2's partial sums, written at the end of tile-1
                         // and visible after the barrier
@@ -1042,7 +1057,8 @@ __global__ __launch_bounds__(256, 1) void smla_wide_kernel(KernelArgs a) {
         lds_barrier();
         auto finish = [&](const float (*pr)[kWideKeys], int tile) {
             const float tot = pr[0][slot] + pr[1][slot] + pr[2][slot] + pr[3][slot];
-            store_value(tile, tot, irow[tile * kWideKeys + slot]);
+            store_value(tile, tot,
+                        a.dense ? tile * kWideKeys + slot : irow[(tile & 31) * kWideKeys + slot]);
         };
         if (ntiles >= 2) finish(red[ntiles & 1], ntiles - 2);
         if (ntiles >= 1) finish(redl, ntiles - 1);
@@ -1140,7 +1156,8 @@ hipError_t occupancy_t(int* out) {
 bool uses_pipe(int ht, int64_t topk) { return ht == 4 && topk <= kVcap; }
 
 hipError_t launch(const KernelArgs& a, int ht, bool bf16, bool tnd, hipStream_t stream) {
-    if (uses_pipe(ht, a.K)) {
+    // (the dense case has no index list, so no limit on its entry count)
+    if (uses_pipe(ht, a.dense ? 0 : a.K)) {
         if (bf16) return tnd ? launch_wide_t<true, true>(a, stream) : launch_wide_t<true, false>(a, stream);
         return tnd ? launch_wide_t<false, true>(a, stream) : launch_wide_t<false, false>(a, stream);
     }

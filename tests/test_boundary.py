@@ -148,7 +148,7 @@ def test_metadata_tnd_derives_lengths():
     (dict(num_heads_q=129), 161002), (dict(head_dim=256), 161002),
     (dict(mask_mode=1), 161002), (dict(cmp_ratio=0), 161002), (dict(cmp_ratio=129), 161002),
     (dict(layout_q="TND"), 161002), (dict(layout_q="XYZ", layout_k="XYZ"), 161002),
-    (dict(topk=0), 161101), (dict(topk=-3), 161002), (dict(max_seqlen_q=0), 161002),
+    (dict(topk=-3), 161002), (dict(max_seqlen_q=0), 161002),
     (dict(batch_size=0), 161002), (dict(core_budget=-1), 161002),
 ])
 def test_metadata_errors(kw, code):
@@ -242,7 +242,7 @@ def _with(**kw):
     (dict(mask=1), 161002, b"mask_mode"), (dict(ratio=0), 161002, b"cmp_ratio"),
     (dict(ratio=129), 161002, b"cmp_ratio"), (dict(maxk=-1), 161002, b"max_seqlen_k"),
     (dict(sq=FAKE), 161101, b"seqused"), (dict(sk=FAKE), 161101, b"seqused"),
-    (dict(idx=None), 161101, b"dense"), (dict(K=0), 161002, b"topk"),
+    (dict(idx=None), 161002, b"topk must be 0"), (dict(K=0), 161002, b"topk"),
     (dict(meta=None), 161001, b"metadata"),
     (dict(layout=1, cu_q=None), 161001, b"cu_seqlens"),
     (dict(layout=1, cu_k=None), 161001, b"cu_seqlens"),
@@ -254,6 +254,28 @@ def test_main_call_errors(kw, code, msg):
     a = _with(**kw)
     assert call(a) == code, LIB.smla_last_error()
     assert msg in LIB.smla_last_error()
+
+
+def test_dense_metadata_and_call_checks():
+    # topk 0 (no sparse_indices) is the dense case: planned like any other
+    m = meta(topk=0).numpy()
+    assert m[14] == 0 and m[4] >= 1
+    # a dense call must carry topk 0 in its metadata too
+    a = base_args()
+    a["idx"] = None
+    a["K"] = 0
+    assert call(a) == 161002
+    assert b"does not match" in LIB.smla_last_error()
+
+
+def test_tnd_max_seqlen_k_below_the_longest_sequence_is_rejected():
+    import torch
+    cu = torch.tensor([0, 5, 12], dtype=torch.int32)
+    with pytest.raises(smla.SmlaError) as e:
+        smla.smla_l1norm_metadata(128, 1, 512, cu_seqlens_q=cu, cu_seqlens_k=cu, batch_size=2,
+                                  max_seqlen_k=6, topk=4, layout_q="TND", layout_k="TND",
+                                  core_budget=64)
+    assert e.value.status == 161002
 
 
 @pytest.mark.parametrize("field,value", [(5, 0), (6, 9), (7, 1), (8, 64), (9, 2), (10, 128),

@@ -80,10 +80,18 @@ def rows_view(p, o):
 
 def drawn_support(p):
     """(R, W) bool: the columns of each row's drawn (used) entries."""
-    R, K = p.rows, p.topk
-    idx = p.sparse_indices.reshape(R, K).astype(np.int64)
-    n = p.topk_length.reshape(R) if p.topk_length is not None else np.full(R, K)
-    take = (np.arange(K)[None, :] < n[:, None]) & (idx >= 0)
+    R = p.rows
+    if p.sparse_indices is None:
+        # dense: entry t is key t, for every visible key of the row
+        n = p.row_entries.reshape(R)
+        K = int(n.max()) if R else 0
+        idx = np.broadcast_to(np.arange(K, dtype=np.int64), (R, K))
+        take = np.arange(K)[None, :] < n[:, None]
+    else:
+        K = p.topk
+        idx = p.sparse_indices.reshape(R, K).astype(np.int64)
+        n = p.topk_length.reshape(R) if p.topk_length is not None else np.full(R, K)
+        take = (np.arange(K)[None, :] < n[:, None]) & (idx >= 0)
     col0 = np.zeros(R, dtype=np.int64)
     if p.layout == "TND":
         cq, ck = p.cu_seqlens_q, p.cu_seqlens_k
@@ -159,6 +167,19 @@ def medium_cases():
     cs.append(("tnd_g80_w5200_direct", C.gen("tnd_varlen", heads_q=80, topk=200,
                                               seqlens_q=(30, 20), seqlens_k=(3000, 2200),
                                               seed=51)))
+    # the dense case (no sparse_indices): both kernels, more entries per row
+    # than an index list could hold, LDS-assembled and direct rows, TND
+    cs.append(("dense_g128_s3000_causal", C.gen("tiny", heads_q=128, batch=1, seqlen_q=64,
+                                                 seqlen_k=3000, topk=0, mask_mode=3,
+                                                 seed=52)))
+    cs.append(("dense_g100_w5000_mask0", C.gen("tiny", heads_q=100, batch=1, seqlen_q=20,
+                                                seqlen_k=5000, topk=0, mask_mode=0,
+                                                seed=53)))
+    cs.append(("dense_g16_bsnd_causal", C.gen("tiny", heads_q=16, batch=2, seqlen_q=50,
+                                               seqlen_k=700, topk=0, mask_mode=3, seed=54)))
+    cs.append(("dense_g64_tnd_cmp2", C.gen("tnd_varlen", heads_q=64, topk=0, cmp_ratio=2,
+                                            cmp_residual=(1, 0), seqlens_q=(40, 25),
+                                            seqlens_k=(900, 3000), seed=55)))
     return cs
 
 
@@ -192,13 +213,14 @@ def test_random_lse_parity(smla):
 
 # ---------------------------------------------------------------- full size
 
-FULL = ["tiny", "bsnd_causal", "dsv32", "tnd_varlen", "compressed"]
+FULL = ["tiny", "bsnd_causal", "dsv32", "tnd_varlen", "compressed", "page_example_dense",
+        "dense_causal"]
 
 
 def sample_rows(p, count=48, seed=0):
     R = p.rows
     rng = np.random.Generator(np.random.PCG64(seed))
-    n = p.topk_length.reshape(R) if p.topk_length is not None else np.full(R, p.topk)
+    n = p.row_entries.reshape(R)
     pick = {0, R - 1, R // 2}
     ragged = np.nonzero((n % 32 != 0) & (n > 0))[0]
     if len(ragged):
