@@ -48,7 +48,7 @@ def algorithmic(p):
     flops = 2.0 * p.heads_q * p.head_dim * pairs
     nbytes = (p.q.numel() * p.q.element_size() + p.k.numel() * p.k.element_size()
               + p.rows * p.groups * 4                       # softmax_lse
-              + p.sparse_indices.size * 4
+              + (p.sparse_indices.size * 4 if p.sparse_indices is not None else 0)
               + (p.topk_length.size * 4 if p.topk_length is not None else 0)
               + (p.cu_seqlens_q.size * 8 if p.cu_seqlens_q is not None else 0)
               + (p.cmp_residual_k.size * 4 if p.cmp_residual_k is not None else 0)
@@ -86,7 +86,7 @@ def cpu_baseline(p, target_s):
     """Time the CPU oracle on evenly spaced rows of the workload."""
     import oracle
     R = p.rows
-    n = p.topk_length.reshape(R).astype(np.int64)
+    n = p.row_entries.reshape(R).astype(np.int64)
     # calibrate on a few rows per thread, then size the sample for ~target_s
     threads = oracle.num_threads()
     cal = np.linspace(0, R - 1, min(R, 4 * threads)).astype(np.int64)
