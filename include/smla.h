@@ -192,6 +192,49 @@ smla_status_t smla_softmax_l1norm(
     int64_t mask_mode, int32_t layout_q, int32_t layout_k, float* softmax_l1_norm,
     void* stream);
 
+/*
+ * smla_softmax_lse - the forward softmax_lse that smla_softmax_l1norm
+ * consumes, computed on the GPU over the same used entries; enqueues one
+ * kernel on `stream`.
+ *
+ * The article's parameter table (section 参数说明, input softmax_lse)
+ * defines this input as the forward attention pass's log-sum-exp and refers
+ * to the sparse_flash_mla operator for its formula, which the pages do not
+ * print; this call computes the plain definition over the entries that
+ * stage 1 and the mask of section 三阶段计算公式 use:
+ *
+ *   softmax_lse[row, g] = log sum_{t used} exp(softmax_scale * q[row,g,:] . k[key(t),:])
+ *
+ * in the natural base, -inf for a row with no used entry. It then holds
+ * that the main call's output rows sum to 1 for every row with a used
+ * entry.
+ *
+ * Arguments are those of smla_softmax_l1norm (same meaning, same layouts,
+ * same metadata from smla_l1norm_metadata), without the softmax_lse input
+ * and with softmax_lse as the output:
+ *
+ *   softmax_lse    fp32 out (B,N2,S1,G) | (N2,T1,G), every element written
+ *
+ * The work is split over the metadata's rows with this kernel's own
+ * co-residency on the device's CUs (metadata field 22), or over the
+ * metadata's core count (field 4) when the metadata was made with a
+ * core_budget.
+ *
+ * Errors: as smla_softmax_l1norm (SMLA_ERR_PARAM_INVALID when q, k or
+ * softmax_lse is NULL; k may be NULL when there are no keys). An empty q
+ * (R == 0) returns SMLA_SUCCESS and launches nothing; with no keys
+ * (T2 == 0) every row is -inf.
+ */
+smla_status_t smla_softmax_lse(
+    const void* q, const void* k, const int32_t* sparse_indices,
+    const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k, const int32_t* seqused_q,
+    const int32_t* seqused_k, const int32_t* cmp_residual_k, const int32_t* topk_length,
+    const int32_t* metadata_host, int32_t dtype, int64_t batch_size, int64_t seqlen_q,
+    int64_t seqlen_k, int64_t num_heads_q, int64_t num_heads_k, int64_t head_dim,
+    int64_t topk, double softmax_scale, int64_t max_seqlen_k, int64_t cmp_ratio,
+    int64_t mask_mode, int32_t layout_q, int32_t layout_k, float* softmax_lse,
+    void* stream);
+
 /* Elements of the output for the given shapes: B*S1*N2*S2 (BSND) or
  * T1*N2*T2 (TND); -1 for an unknown layout or a negative size. Host only. */
 int64_t smla_output_numel(int32_t layout, int64_t batch_size, int64_t seqlen_q,

@@ -12,7 +12,10 @@ Names and defaults follow the page's PyTorch API (the
 * :func:`sparse_flash_mla_softmax_l1_norm_metadata` (alias
   :func:`smla_l1norm_metadata`) returns the int32 (64,) metadata on the CPU;
 * :func:`sparse_flash_mla_softmax_l1_norm` (alias :func:`smla_softmax_l1norm`)
-  returns the fp32 output, (B,S1,N2,S2) or (T1,N2,T2).
+  returns the fp32 output, (B,S1,N2,S2) or (T1,N2,T2);
+* :func:`sparse_flash_mla_softmax_lse` (alias :func:`smla_softmax_lse`) returns
+  the forward softmax_lse that the main call consumes, computed on the GPU
+  over the same used entries.
 """
 
 from __future__ import annotations
@@ -25,7 +28,8 @@ import torch  # loads the HIP runtime the library binds to
 
 __all__ = [
     "SmlaError", "library_path", "smla_l1norm_metadata", "smla_softmax_l1norm",
-    "sparse_flash_mla_softmax_l1_norm_metadata", "sparse_flash_mla_softmax_l1_norm",
+    "smla_softmax_lse", "sparse_flash_mla_softmax_l1_norm_metadata",
+    "sparse_flash_mla_softmax_l1_norm", "sparse_flash_mla_softmax_lse",
     "output_shape", "SMLA_METADATA_SIZE",
 ]
 
@@ -67,6 +71,9 @@ def _load():
                                         i64, i64, i64, i64, dbl, i64, i64, i64, i32, i32, p,
                                         p]
     lib.smla_softmax_l1norm.restype = i32
+    lib.smla_softmax_lse.argtypes = [p, p, p, p, p, p, p, p, p, p, i32, i64, i64, i64, i64, i64,
+                                     i64, i64, dbl, i64, i64, i64, i32, i32, p, p]
+    lib.smla_softmax_lse.restype = i32
     lib.smla_output_numel.argtypes = [i32, i64, i64, i64, i64]
     lib.smla_output_numel.restype = i64
     lib.smla_last_error.argtypes = []
@@ -155,6 +162,93 @@ def _dev_i32(t, device, name) -> Optional[torch.Tensor]:
     return t.contiguous()
 
 
+class _Call:
+    """Checked, contiguous device arguments of one main or lse call."""
+
+
+def _marshal(q, k, sparse_indices, cu_seqlens_q, cu_seqlens_k, seqused_q, seqused_k,
+             cmp_residual_k, topk_length, layout_q, layout_k) -> _Call:
+    if q is None or k is None:
+        raise SmlaError(SMLA_ERR_PARAM_INVALID, "q and k are required")
+    if q.dtype not in _DTYPES or k.dtype != q.dtype:
+        raise SmlaError(SMLA_ERR_PARAM_INVALID, "q and k must share dtype fp16 or bf16")
+    dev = q.device
+    if dev.type != "cuda" or k.device != dev:
+        raise SmlaError(SMLA_ERR_PARAM_INVALID, "q and k must be on one GPU")
+    c = _Call()
+    c.dev = dev
+    c.lq, c.lk = _layout(layout_q), _layout(layout_k)
+    c.q, c.k = q.contiguous(), k.contiguous()
+    c.idx = _dev_i32(sparse_indices, dev, "sparse_indices")
+    c.cq = _dev_i32(cu_seqlens_q, dev, "cu_seqlens_q")
+    c.ck = _dev_i32(cu_seqlens_k, dev, "cu_seqlens_k")
+    c.sq = _dev_i32(seqused_q, dev, "seqused_q")
+    c.sk = _dev_i32(seqused_k, dev, "seqused_k")
+    c.cr = _dev_i32(cmp_residual_k, dev, "cmp_residual_k")
+    c.tl = _dev_i32(topk_length, dev, "topk_length")
+
+    if c.lq == 0:
+        if q.dim() != 4 or k.dim() != 4:
+            raise SmlaError(SMLA_ERR_PARAM_INVALID, "BSND q and k must be 4-D")
+        B, S1, N1, D = q.shape
+        _, S2, N2, _ = k.shape
+        if k.shape[0] != B or k.shape[3] != D:
+            raise SmlaError(SMLA_ERR_PARAM_INVALID, "k's B and D must match q's")
+        c.sq_len, c.sk_len = S1, S2
+    else:
+        if q.dim() != 3 or k.dim() != 3:
+            raise SmlaError(SMLA_ERR_PARAM_INVALID, "TND q and k must be 3-D")
+        T1, N1, D = q.shape
+        T2, N2, _ = k.shape
+        if k.shape[2] != D:
+            raise SmlaError(SMLA_ERR_PARAM_INVALID, "k's D must match q's")
+        B = (c.cq.numel() - 1) if c.cq is not None else 0
+        c.sq_len, c.sk_len = T1, T2
+    c.B, c.N1, c.N2, c.D = B, N1, N2, D
+    c.K = c.idx.shape[-1] if c.idx is not None else 0
+    c.out_shape = output_shape(q, k, "BSND" if c.lq == 0 else "TND")
+    G = N1 // N2 if N2 else 0
+    c.lse_shape = (B, N2, c.sq_len, G) if c.lq == 0 else (N2, c.sq_len, G)
+    if c.idx is not None:
+        want = (B, c.sq_len, N2, c.K) if c.lq == 0 else (c.sq_len, N2, c.K)
+        if tuple(c.idx.shape) != want:
+            raise SmlaError(SMLA_ERR_PARAM_INVALID, f"sparse_indices shape != {want}")
+    if c.tl is not None:
+        want = (B, c.sq_len, N2) if c.lq == 0 else (c.sq_len, N2)
+        if tuple(c.tl.shape) != want:
+            raise SmlaError(SMLA_ERR_PARAM_INVALID, f"topk_length shape != {want}")
+    if c.cr is not None and c.cr.numel() != B:
+        raise SmlaError(SMLA_ERR_PARAM_INVALID, "cmp_residual_k must have B elements")
+    if (c.cq is None) != (c.ck is None) or (c.cq is not None and c.ck.numel() != c.cq.numel()):
+        raise SmlaError(SMLA_ERR_PARAM_INVALID, "cu_seqlens_q/k must come as a pair of B+1")
+    return c
+
+
+def _out_tensor(out, shape, dev, what):
+    if out is None:
+        return torch.empty(shape, dtype=torch.float32, device=dev)
+    if (out.dtype != torch.float32 or tuple(out.shape) != tuple(shape)
+            or out.device != dev or not out.is_contiguous()):
+        raise SmlaError(SMLA_ERR_PARAM_INVALID, f"{what} must be contiguous fp32 of shape {shape}")
+    return out
+
+
+def _metadata(metadata):
+    if metadata is None:
+        raise SmlaError(SMLA_ERR_PARAM_NULLPTR, "metadata is required")
+    metadata = _host_i32(metadata)
+    if metadata.numel() != SMLA_METADATA_SIZE:
+        raise SmlaError(SMLA_ERR_PARAM_INVALID, "metadata must have 64 elements")
+    return metadata
+
+
+def _tail(c, softmax_scale, max_seqlen_k, cmp_ratio, mask_mode, out):
+    stream = torch.cuda.current_stream(c.dev).cuda_stream
+    return (_DTYPES[c.q.dtype], int(c.B), int(c.sq_len), int(c.sk_len), int(c.N1), int(c.N2),
+            int(c.D), int(c.K), float(softmax_scale), int(max_seqlen_k or 0), int(cmp_ratio),
+            int(mask_mode), c.lq, c.lk, _ptr(out), ctypes.c_void_p(stream))
+
+
 def sparse_flash_mla_softmax_l1_norm(
         q, k, softmax_lse, *, sparse_indices=None, cu_seqlens_q=None, cu_seqlens_k=None,
         seqused_q=None, seqused_k=None, cmp_residual_k=None, topk_length=None,
@@ -168,85 +262,58 @@ def sparse_flash_mla_softmax_l1_norm(
     (optional, fp32, contiguous, output shape) receives the result.
     Enqueued on the current stream.
     """
-    if q is None or k is None or softmax_lse is None:
+    if softmax_lse is None:
         raise SmlaError(SMLA_ERR_PARAM_INVALID, "q, k and softmax_lse are required")
-    if q.dtype not in _DTYPES or k.dtype != q.dtype:
-        raise SmlaError(SMLA_ERR_PARAM_INVALID, "q and k must share dtype fp16 or bf16")
+    c = _marshal(q, k, sparse_indices, cu_seqlens_q, cu_seqlens_k, seqused_q, seqused_k,
+                 cmp_residual_k, topk_length, layout_q, layout_k)
     if softmax_lse.dtype != torch.float32:
         raise SmlaError(SMLA_ERR_PARAM_INVALID, "softmax_lse must be float32")
-    dev = q.device
-    if dev.type != "cuda" or k.device != dev or softmax_lse.device != dev:
+    if softmax_lse.device != c.dev:
         raise SmlaError(SMLA_ERR_PARAM_INVALID, "q, k and softmax_lse must be on one GPU")
-    lq, lk = _layout(layout_q), _layout(layout_k)
-    q, k, softmax_lse = q.contiguous(), k.contiguous(), softmax_lse.contiguous()
-    idx = _dev_i32(sparse_indices, dev, "sparse_indices")
-    cq = _dev_i32(cu_seqlens_q, dev, "cu_seqlens_q")
-    ck = _dev_i32(cu_seqlens_k, dev, "cu_seqlens_k")
-    sq = _dev_i32(seqused_q, dev, "seqused_q")
-    sk = _dev_i32(seqused_k, dev, "seqused_k")
-    cr = _dev_i32(cmp_residual_k, dev, "cmp_residual_k")
-    tl = _dev_i32(topk_length, dev, "topk_length")
-
-    if lq == 0:
-        if q.dim() != 4 or k.dim() != 4:
-            raise SmlaError(SMLA_ERR_PARAM_INVALID, "BSND q and k must be 4-D")
-        B, S1, N1, D = q.shape
-        _, S2, N2, _ = k.shape
-        if k.shape[0] != B or k.shape[3] != D:
-            raise SmlaError(SMLA_ERR_PARAM_INVALID, "k's B and D must match q's")
-        sq_len, sk_len = S1, S2
-    else:
-        if q.dim() != 3 or k.dim() != 3:
-            raise SmlaError(SMLA_ERR_PARAM_INVALID, "TND q and k must be 3-D")
-        T1, N1, D = q.shape
-        T2, N2, _ = k.shape
-        if k.shape[2] != D:
-            raise SmlaError(SMLA_ERR_PARAM_INVALID, "k's D must match q's")
-        B = (cq.numel() - 1) if cq is not None else 0
-        sq_len, sk_len = T1, T2
-    G = N1 // N2 if N2 else 0
-    K = idx.shape[-1] if idx is not None else 0
-    shape = output_shape(q, k, "BSND" if lq == 0 else "TND")
-    lse_shape = (B, N2, S1, G) if lq == 0 else (N2, sq_len, G)
-    if tuple(softmax_lse.shape) != tuple(lse_shape):
+    softmax_lse = softmax_lse.contiguous()
+    if tuple(softmax_lse.shape) != tuple(c.lse_shape):
         raise SmlaError(SMLA_ERR_PARAM_INVALID,
-                        f"softmax_lse shape {tuple(softmax_lse.shape)} != {lse_shape}")
-    if idx is not None:
-        want = (B, S1, N2, K) if lq == 0 else (sq_len, N2, K)
-        if tuple(idx.shape) != want:
-            raise SmlaError(SMLA_ERR_PARAM_INVALID, f"sparse_indices shape != {want}")
-    if tl is not None:
-        want = (B, S1, N2) if lq == 0 else (sq_len, N2)
-        if tuple(tl.shape) != want:
-            raise SmlaError(SMLA_ERR_PARAM_INVALID, f"topk_length shape != {want}")
-    if cr is not None and cr.numel() != B:
-        raise SmlaError(SMLA_ERR_PARAM_INVALID, "cmp_residual_k must have B elements")
-    if (cq is None) != (ck is None) or (cq is not None and ck.numel() != cq.numel()):
-        raise SmlaError(SMLA_ERR_PARAM_INVALID, "cu_seqlens_q/k must come as a pair of B+1")
-
-    if out is None:
-        out = torch.empty(shape, dtype=torch.float32, device=dev)
-    elif (out.dtype != torch.float32 or tuple(out.shape) != tuple(shape)
-          or out.device != dev or not out.is_contiguous()):
-        raise SmlaError(SMLA_ERR_PARAM_INVALID, "out must be contiguous fp32 of the output shape")
+                        f"softmax_lse shape {tuple(softmax_lse.shape)} != {c.lse_shape}")
+    out = _out_tensor(out, c.out_shape, c.dev, "out")
     if out.numel() == 0:
         return out  # empty q or empty output: nothing to compute
-    if metadata is None:
-        raise SmlaError(SMLA_ERR_PARAM_NULLPTR, "metadata is required")
-    metadata = _host_i32(metadata)
-    if metadata.numel() != SMLA_METADATA_SIZE:
-        raise SmlaError(SMLA_ERR_PARAM_INVALID, "metadata must have 64 elements")
-    stream = torch.cuda.current_stream(dev).cuda_stream
-    with torch.cuda.device(dev):
+    metadata = _metadata(metadata)
+    with torch.cuda.device(c.dev):
         _check(_lib.smla_softmax_l1norm(
-            _ptr(q), _ptr(k), _ptr(softmax_lse), _ptr(idx), _ptr(cq), _ptr(ck), _ptr(sq),
-            _ptr(sk), _ptr(cr), _ptr(tl), _ptr(metadata), _DTYPES[q.dtype], int(B),
-            int(sq_len), int(sk_len), int(N1), int(N2), int(D), int(K),
-            float(softmax_scale), int(max_seqlen_k or 0), int(cmp_ratio), int(mask_mode),
-            lq, lk, _ptr(out), ctypes.c_void_p(stream)))
+            _ptr(c.q), _ptr(c.k), _ptr(softmax_lse), _ptr(c.idx), _ptr(c.cq), _ptr(c.ck),
+            _ptr(c.sq), _ptr(c.sk), _ptr(c.cr), _ptr(c.tl), _ptr(metadata),
+            *_tail(c, softmax_scale, max_seqlen_k, cmp_ratio, mask_mode, out)))
+    return out
+
+
+def sparse_flash_mla_softmax_lse(
+        q, k, *, sparse_indices=None, cu_seqlens_q=None, cu_seqlens_k=None,
+        seqused_q=None, seqused_k=None, cmp_residual_k=None, topk_length=None,
+        metadata=None, softmax_scale=1.0, max_seqlen_k=0, cmp_ratio=1, mask_mode=0,
+        layout_q="BSND", layout_k="BSND", out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """The forward softmax_lse over the same used entries, on the GPU.
+
+    ``lse[row, g] = log sum_{t used} exp(softmax_scale * q[row,g,:].k[key(t),:])``,
+    -inf for a row with no used entry; fp32 of shape (B,N2,S1,G) or
+    (N2,T1,G), the ``softmax_lse`` input of
+    :func:`sparse_flash_mla_softmax_l1_norm`. Takes that call's keyword
+    arguments (same metadata). Enqueued on the current stream.
+    """
+    c = _marshal(q, k, sparse_indices, cu_seqlens_q, cu_seqlens_k, seqused_q, seqused_k,
+                 cmp_residual_k, topk_length, layout_q, layout_k)
+    out = _out_tensor(out, c.lse_shape, c.dev, "out")
+    if out.numel() == 0:
+        return out  # empty q: nothing to compute
+    metadata = _metadata(metadata)
+    with torch.cuda.device(c.dev):
+        _check(_lib.smla_softmax_lse(
+            _ptr(c.q), _ptr(c.k), _ptr(c.idx), _ptr(c.cq), _ptr(c.ck), _ptr(c.sq), _ptr(c.sk),
+            _ptr(c.cr), _ptr(c.tl), _ptr(metadata),
+            *_tail(c, softmax_scale, max_seqlen_k, cmp_ratio, mask_mode, out)))
     return out
 
 
 # Names of the C entry points.
 smla_l1norm_metadata = sparse_flash_mla_softmax_l1_norm_metadata
 smla_softmax_l1norm = sparse_flash_mla_softmax_l1_norm
+smla_softmax_lse = sparse_flash_mla_softmax_lse

@@ -233,16 +233,26 @@ smla_status_t smla_l1norm_metadata(
     return ok();
 }
 
-smla_status_t smla_softmax_l1norm(
-    const void* q, const void* k, const float* softmax_lse,
-    const int32_t* sparse_indices, const int32_t* cu_seqlens_q,
-    const int32_t* cu_seqlens_k, const int32_t* seqused_q, const int32_t* seqused_k,
-    const int32_t* cmp_residual_k, const int32_t* topk_length,
-    const int32_t* metadata_host, int32_t dtype, int64_t batch_size, int64_t seqlen_q,
-    int64_t seqlen_k, int64_t num_heads_q, int64_t num_heads_k, int64_t head_dim,
-    int64_t topk, double softmax_scale, int64_t max_seqlen_k, int64_t cmp_ratio,
-    int64_t mask_mode, int32_t layout_q, int32_t layout_k, float* softmax_l1_norm,
-    void* stream) {
+}  // extern "C"
+
+namespace {
+
+// Checks shared by the main call (softmax_lse in, softmax_l1_norm out) and
+// the lse call (lse_in NULL, out = softmax_lse), then the kernel arguments.
+// *nothing_to_do is set when there are no rows (the page: an empty q returns
+// directly) or, for the main call, an empty output row.
+smla_status_t prepare(const void* q, const void* k, const int32_t* sparse_indices,
+                      const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k,
+                      const int32_t* seqused_q, const int32_t* seqused_k,
+                      const int32_t* cmp_residual_k, const int32_t* topk_length,
+                      const int32_t* metadata_host, int32_t dtype, int64_t batch_size,
+                      int64_t seqlen_q, int64_t seqlen_k, int64_t num_heads_q,
+                      int64_t num_heads_k, int64_t head_dim, int64_t topk,
+                      double softmax_scale, int64_t max_seqlen_k, int64_t cmp_ratio,
+                      int64_t mask_mode, int32_t layout_q, int32_t layout_k, bool lse_call,
+                      const float* lse_in, float* out, smla::KernelArgs* out_args,
+                      bool* nothing_to_do) {
+    *nothing_to_do = false;
     if (dtype != SMLA_DTYPE_FP16 && dtype != SMLA_DTYPE_BF16)
         return fail(SMLA_ERR_PARAM_INVALID, "dtype must be FLOAT16 or BFLOAT16");
     smla_status_t st = check_common(num_heads_q, num_heads_k, head_dim, layout_q, layout_k,
@@ -260,11 +270,17 @@ smla_status_t smla_softmax_l1norm(
     const int64_t R = tnd ? seqlen_q : batch_size * seqlen_q;
     const int64_t rows_k = tnd ? seqlen_k : batch_size * seqlen_k;
     const int64_t W = seqlen_k;
-    // empty q or empty output: nothing is read or written (page: an empty q
-    // returns directly)
-    if (R == 0 || W == 0) return ok();
+    // empty q (both calls) or empty output row (main call): nothing is read
+    // or written. Without keys every lse row is -inf, which the lse call
+    // still writes.
+    if (R == 0 || (!lse_call && W == 0)) {
+        *nothing_to_do = true;
+        return SMLA_SUCCESS;
+    }
 
-    if (!q || !k || !softmax_lse || !softmax_l1_norm)
+    if (lse_call && (!q || (!k && rows_k > 0) || !out))
+        return fail(SMLA_ERR_PARAM_INVALID, "q, k and softmax_lse (output) are required");
+    if (!lse_call && (!q || !k || !lse_in || !out))
         return fail(SMLA_ERR_PARAM_INVALID,
                     "q, k, softmax_lse and softmax_l1_norm are required");
     // no sparse_indices: the dense case, every key of the row's batch or
@@ -302,16 +318,17 @@ smla_status_t smla_softmax_l1norm(
     if (m[4] < 1 || m[4] > m[0])
         return fail(SMLA_ERR_PARAM_INVALID, "metadata core count is out of range");
 
-    smla::KernelArgs a;
+    smla::KernelArgs& a = *out_args;
+    a = smla::KernelArgs{};
     a.q = q;
     a.k = k;
-    a.lse = softmax_lse;
+    a.lse = lse_in;
+    a.out = out;
     a.idx = sparse_indices;
     a.topk_len = dense ? nullptr : topk_length;
     a.cu_q = cu_seqlens_q;
     a.cu_k = cu_seqlens_k;
     a.cmp_res = cmp_residual_k;
-    a.out = softmax_l1_norm;
     a.R = R;
     a.W = W;
     a.rows_k = rows_k;
@@ -330,10 +347,95 @@ smla_status_t smla_softmax_l1norm(
     a.inv_g = 1.0f / (float)a.G;
     a.num_wg = m[4];
     a.snake = m[19];
+    return SMLA_SUCCESS;
+}
 
+// Co-resident workgroups per CU of the lse kernel, queried once per variant.
+std::mutex g_lse_occ_mu;
+std::map<std::tuple<int, bool, bool>, int> g_lse_occ;
+
+hipError_t lse_capacity(int ht, bool bf16, bool tnd, int* per_cu) {
+    std::lock_guard<std::mutex> lk(g_lse_occ_mu);
+    auto it = g_lse_occ.find({ht, bf16, tnd});
+    if (it != g_lse_occ.end()) {
+        *per_cu = it->second;
+        return hipSuccess;
+    }
+    int occ = 0;
+    hipError_t e = smla::lse_resident_per_cu(ht, bf16, tnd, &occ);
+    if (e != hipSuccess) return e;
+    if (occ <= 0) return hipErrorInvalidConfiguration;
+    g_lse_occ[{ht, bf16, tnd}] = occ;
+    *per_cu = occ;
+    return hipSuccess;
+}
+
+}  // namespace
+
+extern "C" {
+
+smla_status_t smla_softmax_l1norm(
+    const void* q, const void* k, const float* softmax_lse,
+    const int32_t* sparse_indices, const int32_t* cu_seqlens_q,
+    const int32_t* cu_seqlens_k, const int32_t* seqused_q, const int32_t* seqused_k,
+    const int32_t* cmp_residual_k, const int32_t* topk_length,
+    const int32_t* metadata_host, int32_t dtype, int64_t batch_size, int64_t seqlen_q,
+    int64_t seqlen_k, int64_t num_heads_q, int64_t num_heads_k, int64_t head_dim,
+    int64_t topk, double softmax_scale, int64_t max_seqlen_k, int64_t cmp_ratio,
+    int64_t mask_mode, int32_t layout_q, int32_t layout_k, float* softmax_l1_norm,
+    void* stream) {
+    smla::KernelArgs a;
+    bool nothing = false;
+    smla_status_t st = prepare(q, k, sparse_indices, cu_seqlens_q, cu_seqlens_k, seqused_q,
+                               seqused_k, cmp_residual_k, topk_length, metadata_host, dtype,
+                               batch_size, seqlen_q, seqlen_k, num_heads_q, num_heads_k,
+                               head_dim, topk, softmax_scale, max_seqlen_k, cmp_ratio,
+                               mask_mode, layout_q, layout_k, false, softmax_lse,
+                               softmax_l1_norm, &a, &nothing);
+    if (st != SMLA_SUCCESS) return st;
+    if (nothing) return ok();
     const int ht = smla::head_tiles_for(a.G);
-    hipError_t e = smla::launch(a, ht, dtype == SMLA_DTYPE_BF16, tnd,
+    hipError_t e = smla::launch(a, ht, dtype == SMLA_DTYPE_BF16, layout_q == SMLA_LAYOUT_TND,
                                 static_cast<hipStream_t>(stream));
+    if (e != hipSuccess)
+        return fail(SMLA_ERR_RUNTIME, "kernel launch failed: %s", hipGetErrorString(e));
+    return ok();
+}
+
+smla_status_t smla_softmax_lse(
+    const void* q, const void* k, const int32_t* sparse_indices,
+    const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k, const int32_t* seqused_q,
+    const int32_t* seqused_k, const int32_t* cmp_residual_k, const int32_t* topk_length,
+    const int32_t* metadata_host, int32_t dtype, int64_t batch_size, int64_t seqlen_q,
+    int64_t seqlen_k, int64_t num_heads_q, int64_t num_heads_k, int64_t head_dim,
+    int64_t topk, double softmax_scale, int64_t max_seqlen_k, int64_t cmp_ratio,
+    int64_t mask_mode, int32_t layout_q, int32_t layout_k, float* softmax_lse,
+    void* stream) {
+    smla::KernelArgs a;
+    bool nothing = false;
+    smla_status_t st = prepare(q, k, sparse_indices, cu_seqlens_q, cu_seqlens_k, seqused_q,
+                               seqused_k, cmp_residual_k, topk_length, metadata_host, dtype,
+                               batch_size, seqlen_q, seqlen_k, num_heads_q, num_heads_k,
+                               head_dim, topk, softmax_scale, max_seqlen_k, cmp_ratio,
+                               mask_mode, layout_q, layout_k, true, nullptr, softmax_lse,
+                               &a, &nothing);
+    if (st != SMLA_SUCCESS) return st;
+    if (nothing) return ok();
+    const int ht = smla::head_tiles_for(a.G);
+    const bool bf16 = dtype == SMLA_DTYPE_BF16, tnd = layout_q == SMLA_LAYOUT_TND;
+    // the metadata's split was sized for the main call's kernel; this kernel
+    // has its own co-residency on the same CUs (field 22). With a caller's
+    // core budget (field 22 is 0) the metadata's core count stands.
+    const int32_t* m = metadata_host;
+    if (m[22] > 0) {
+        int per_cu = 0;
+        hipError_t e = lse_capacity(ht, bf16, tnd, &per_cu);
+        if (e != hipSuccess)
+            return fail(SMLA_ERR_RUNTIME, "occupancy query failed: %s", hipGetErrorString(e));
+        const int64_t cap = (int64_t)m[22] * per_cu;
+        a.num_wg = (int32_t)(a.R < cap ? a.R : cap);
+    }
+    hipError_t e = smla::launch_lse(a, ht, bf16, tnd, static_cast<hipStream_t>(stream));
     if (e != hipSuccess)
         return fail(SMLA_ERR_RUNTIME, "kernel launch failed: %s", hipGetErrorString(e));
     return ok();

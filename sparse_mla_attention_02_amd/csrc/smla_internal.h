@@ -16,7 +16,7 @@ struct KernelArgs {
     const int32_t* cu_q;      // (B+1) for TND
     const int32_t* cu_k;      // (B+1) for TND
     const int32_t* cmp_res;   // (B) or nullptr
-    float* out;               // (R, W) fp32
+    float* out;               // (R, W) fp32; the lse kernel: (R, G) fp32 softmax_lse
     int64_t R;                // query rows
     int64_t W;                // output row width (S2 or T2)
     int64_t rows_k;           // rows of k (B*S2 or T2)
@@ -46,5 +46,12 @@ bool uses_pipe(int head_tiles, int64_t topk);
 
 // Co-resident workgroups per CU of the variant used for (head_tiles, topk).
 hipError_t resident_per_cu(int head_tiles, bool bf16, bool tnd, int64_t topk, int* out);
+
+// The forward softmax_lse kernel: a.out receives (R, G) fp32.
+hipError_t launch_lse(const KernelArgs& a, int head_tiles, bool bf16, bool tnd,
+                      hipStream_t stream);
+
+// Co-resident workgroups per CU of the lse kernel for (head_tiles, bf16, tnd).
+hipError_t lse_resident_per_cu(int head_tiles, bool bf16, bool tnd, int* out);
 
 }  // namespace smla

@@ -47,6 +47,7 @@ constexpr int kTile = 32;           // keys per tile (MFMA N)
 // different bank groups (row * 65 mod 16 = row mod 16)
 constexpr int kPitch = kChunks + 1;
 constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
 constexpr int kVcap = 2048;         // values of one row kept in LDS for assembly
 constexpr int kStage = kTile * kPitch * 4 - 4;  // floats of one K tile usable as row stage
 
@@ -494,6 +495,202 @@ __global__ __launch_bounds__(64 * HT, 2) void smla_l1norm_kernel(KernelArgs a) {
         // end of row
     }
     // end of kernel
+}
+
+// ---------------------------------------------------------------------------
+// Forward softmax_lse over the same used entries: the input the operation
+// consumes (parameter table, softmax_lse: the forward attention pass's
+// log-sum-exp, whose formula the article defers to the sparse_flash_mla
+// operator; taken here as its plain definition)
+//   lse[r, g] = log sum_{t used} exp(scale * q[r,g,:] . K[key(t),:]),
+// -inf for a row without a used entry.
+//
+// Same row walk, gathers and 32-key tiles as the general kernel, with the
+// MFMA operands swapped (S = Ksel . Q^T): a lane's accumulator then holds 16
+// keys of one head, so the reduction over keys runs inside the lane as an
+// online maximum and rescaled sum (base 2); the two half-waves of a head
+// meet once at the end of the row.
+
+// One 32-key tile, S = K_tile . Q_tile^T for this wave's NB blocks of 32
+// heads (each K operand read feeds NB MFMAs), with the previous tile's
+// epilogue `epi` scheduled between the MFMAs.
+template <bool BF16, int NB, typename Epi>
+__device__ __forceinline__ void kq_tile(const uint4* __restrict__ src, const uint4 (*qa)[kChunks / 2],
+                                        int col, int half, f32x16_t* acc, Epi&& epi) {
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) acc[nb] = f32x16_t{};
+    const uint4* row = src + col * kPitch + half;
+#pragma unroll
+    for (int s = 0; s < kChunks / 2; ++s) {
+        const uint4 b = row[2 * s];
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb) acc[nb] = mfma_32x32x16<BF16>(b, qa[nb][s], acc[nb]);
+    }
+    epi();
+    constexpr int kLead = 4;
+    __builtin_amdgcn_sched_group_barrier(0x100, kLead, 0);
+#pragma unroll
+    for (int s = 0; s < kChunks / 2; ++s) {
+        __builtin_amdgcn_sched_group_barrier(0x008, NB, 0);
+        if (s < kChunks / 2 - kLead) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x002, 3 * NB, 0);
+    }
+}
+
+// Online update of one lane's (m, l) -- base-2 running maximum and sum of
+// 2^(x - m) -- with its 16 scores of a tile, x = acc * c. Bit
+// 8*(e/4) + e%4 of `used` says whether element e is a used entry.
+__device__ __forceinline__ void lse_update(const f32x16_t& acc, uint32_t used, float c,
+                                           float& m, float& l) {
+    constexpr float kNegInf = -__builtin_inff();
+    float x[16];
+    float mt = kNegInf;
+#pragma unroll
+    for (int e = 0; e < 16; ++e) {
+        x[e] = ((used >> (8 * (e >> 2) + (e & 3))) & 1u) ? acc[e] * c : kNegInf;
+        mt = __builtin_fmaxf(mt, x[e]);
+    }
+    const float mn = __builtin_fmaxf(m, mt);
+    const float base = mn == kNegInf ? 0.0f : mn;  // nothing used yet: every term is 0
+    float sum = l * __builtin_amdgcn_exp2f(m - base);
+#pragma unroll
+    for (int e = 0; e < 16; ++e) sum += __builtin_amdgcn_exp2f(x[e] - base);
+    m = mn;
+    l = sum;
+}
+
+// WAVES waves per workgroup, each with NB blocks of 32 heads (1 x 1 for up
+// to 32 heads, 2 x 1 for up to 64, 2 x 2 for up to 128). One wave per SIMD
+// at two workgroups per CU, so each wave has the whole register file: Q
+// takes NB x 128 registers.
+template <int NB, int WAVES, bool BF16, bool TND>
+__global__ __launch_bounds__(64 * WAVES, 2) void smla_lse_kernel(KernelArgs a) {
+    __shared__ uint4 kbuf0[kTile * kPitch];
+    __shared__ uint4 kbuf1[kTile * kPitch];
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int half = lane >> 5;
+    const int col = lane & 31;
+    const uint4* __restrict__ k4 = static_cast<const uint4*>(a.k);
+    const uint4* __restrict__ q4 = static_cast<const uint4*>(a.q);
+    // lane (col, half) holds head head0 + 32*nb of Q as MFMA B operand of
+    // block nb and, in that block's accumulator, keys 8*(e/4) + 4*half + e%4
+    // of a tile for that head; heads past G read zeros and are never written
+    const int head0 = wave * 32 * NB + col;
+
+    uint4 qa[NB][kChunks / 2];
+    auto load_q = [&](int64_t r) {
+        const __amdgpu_buffer_rsrc_t rq = rsrc(q4 + r * a.G * kChunks, (uint32_t)a.G * 1024u);
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb) {
+            const uint32_t qoff = (uint32_t)(head0 + 32 * nb) * 1024u + (uint32_t)half * 16u;
+#pragma unroll
+            for (int s = 0; s < kChunks / 2; ++s)
+                qa[nb][s] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(
+                                                          rq, qoff + 32u * s, 0, 2 /* nt */));
+        }
+    };
+
+    int64_t it = 0;
+    int64_t r = row_of(a, 0, blockIdx.x);
+    load_q(r < a.R ? r : a.R - 1);
+
+    for (; it * a.num_wg < a.R; ++it) {
+        r = row_of(a, it, blockIdx.x);
+        if (r >= a.R) continue;
+        const int64_t r_next = (it + 1) * a.num_wg < a.R ? row_of(a, it + 1, blockIdx.x) : a.R;
+        const RowInfo ri = decode_row<TND>(a, r);
+        const int32_t* __restrict__ irow = a.idx + r * a.K;
+        const int ntiles = (ri.n + kTile - 1) / kTile;
+
+        const __amdgpu_buffer_rsrc_t ridx = rsrc(irow, a.dense ? 0u : (uint32_t)a.K * 4u);
+        auto tile_idx = [&](int tile) -> int32_t {
+            const int32_t e = tile * kTile + col;
+            const int32_t j = __builtin_amdgcn_raw_buffer_load_b32(ridx, (uint32_t)e * 4u, 0, 0);
+            return a.dense ? e : j;
+        };
+        auto used = [&](int tile, int kk, int32_t j) -> bool {
+            return tile * kTile + kk < ri.n && (uint32_t)j < (uint32_t)ri.vis;
+        };
+        int32_t key_cur = tile_idx(0);
+        int32_t key_nxt = tile_idx(1);
+
+        // slot kk of a tile is moved by wave kk % WAVES, one 1 KB row per
+        // instruction; unused slots fetch row 0 (never counted)
+        const __amdgpu_buffer_rsrc_t krs = k_rsrc(k4, ri.kbase);
+        auto gather = [&](uint4* dst, int tile, int32_t idx_reg) {
+            const int32_t rows = used(tile, col, idx_reg) ? idx_reg : 0;
+#pragma unroll
+            for (int i = 0; i < kTile / WAVES; ++i) {
+                const int kk = wave + i * WAVES;
+                const int32_t j = __builtin_amdgcn_readlane(rows, kk);
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(krs, SMLA_LDS(dst + kk * kPitch), 16,
+                                                         lane << 4, j << 10, 0, 0);
+            }
+        };
+        if (ntiles > 0) gather(kbuf0, 0, key_cur);
+
+        float m[NB], l[NB];
+        f32x16_t acc[NB], acc_prev[NB];
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb) {
+            m[nb] = -__builtin_inff();
+            l[nb] = 0.0f;
+            acc_prev[nb] = f32x16_t{};
+        }
+        uint32_t used_prev = 0;  // this lane's view (shifted by 4*half) of tile-1's used slots
+        auto epilogue = [&] {
+#pragma unroll
+            for (int nb = 0; nb < NB; ++nb)
+                lse_update(acc_prev[nb], used_prev, a.c_scale, m[nb], l[nb]);
+        };
+        auto body = [&](int tile, const uint4* cur, uint4* nxt) {
+            // gathers of this tile landed; every wave is done reading `nxt`
+            __builtin_amdgcn_s_waitcnt(0);
+            __syncthreads();
+            if (tile + 1 < ntiles) gather(nxt, tile + 1, key_nxt);
+            const int32_t key_nn = tile_idx(tile + 2);
+            // slot kk of the tile is used: bit kk (lanes kk and kk + 32 agree)
+            const uint32_t mask =
+                (uint32_t)__builtin_amdgcn_ballot_w64(used(tile, col, key_cur));
+            kq_tile<BF16, NB>(cur, qa, col, half, acc, epilogue);
+#pragma unroll
+            for (int nb = 0; nb < NB; ++nb) acc_prev[nb] = acc[nb];
+            used_prev = mask >> (4 * half);
+            key_cur = key_nxt;
+            key_nxt = key_nn;
+        };
+        for (int tile = 0; tile < ntiles; tile += 2) {
+            body(tile, kbuf0, kbuf1);
+            if (tile + 1 < ntiles) body(tile + 1, kbuf1, kbuf0);
+        }
+        if (ntiles > 0) epilogue();
+        // the next row's Q (a clamped row after the last one) is in flight
+        // during the combine and store
+        load_q(r_next < a.R ? r_next : r);
+
+        // the two half-waves of a head: (m, l) and (m', l') combine into
+        // M = max(m, m'), L = l 2^(m-M) + l' 2^(m'-M); lse = ln2 (M + log2 L)
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb) {
+            const float m2 = __shfl_xor(m[nb], 32);
+            const float l2 = __shfl_xor(l[nb], 32);
+            const float mm = __builtin_fmaxf(m[nb], m2);
+            const float base = mm == -__builtin_inff() ? 0.0f : mm;
+            const float L = l[nb] * __builtin_amdgcn_exp2f(m[nb] - base) +
+                            l2 * __builtin_amdgcn_exp2f(m2 - base);
+            // a used entry contributes 2^0 = 1 at the maximum, so L >= 1
+            // whenever anything is used
+            const float v =
+                L > 0.0f ? (mm + __builtin_amdgcn_logf(L)) * kLn2 : -__builtin_inff();
+            const int h = head0 + 32 * nb;
+            if (half == 0 && h < a.G) a.out[r * a.G + h] = v;
+        }
+        // every wave is done with kbuf0 before the next row gathers into it
+        __syncthreads();
+    }
 }
 
 // ---------------------------------------------------------------------------
@@ -1133,6 +1330,25 @@ hipError_t occupancy_t(int* out) {
         0);
 }
 
+// head tiles HT (1, 2 or 4 blocks of 32 heads) -> NB blocks per wave x WAVES
+template <int HT, bool BF16, bool TND>
+hipError_t launch_lse_t(const KernelArgs& a, hipStream_t stream) {
+    constexpr int NB = HT == 4 ? 2 : 1;
+    constexpr int WAVES = HT / NB;
+    hipLaunchKernelGGL((smla_lse_kernel<NB, WAVES, BF16, TND>), dim3(a.num_wg),
+                       dim3(64 * WAVES), 0, stream, a);
+    return hipGetLastError();
+}
+
+template <int HT, bool BF16, bool TND>
+hipError_t occupancy_lse_t(int* out) {
+    constexpr int NB = HT == 4 ? 2 : 1;
+    constexpr int WAVES = HT / NB;
+    return hipOccupancyMaxActiveBlocksPerMultiprocessor(
+        out, reinterpret_cast<const void*>(&smla_lse_kernel<NB, WAVES, BF16, TND>),
+        64 * WAVES, 0);
+}
+
 }  // namespace
 
 #define SMLA_DISPATCH(FN, ...)                                                        \
@@ -1170,6 +1386,14 @@ hipError_t resident_per_cu(int ht, bool bf16, bool tnd, int64_t topk, int* out) 
         return tnd ? occupancy_wide_t<false, true>(out) : occupancy_wide_t<false, false>(out);
     }
     SMLA_DISPATCH(occupancy_t, out);
+}
+
+hipError_t launch_lse(const KernelArgs& a, int ht, bool bf16, bool tnd, hipStream_t stream) {
+    SMLA_DISPATCH(launch_lse_t, a, stream);
+}
+
+hipError_t lse_resident_per_cu(int ht, bool bf16, bool tnd, int* out) {
+    SMLA_DISPATCH(occupancy_lse_t, out);
 }
 
 }  // namespace smla

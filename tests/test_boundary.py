@@ -308,3 +308,58 @@ def test_empty_q_returns_without_looking_at_pointers():
     a = base_args(S1=0)
     a["N2"] = 2
     assert call(a) == 161002
+
+
+# ---------------------------------------------------------------- lse call
+
+def call_lse(a):
+    md = a["meta"]
+    mp = md.ctypes.data if md is not None else None
+    return LIB.smla_softmax_lse(
+        a["q"], a["k"], a["idx"], a["cu_q"], a["cu_k"], a["sq"], a["sk"], a["res"],
+        a["tlen"], mp, a["dtype"], a["B"], a["S1"], a["S2"], a["N1"], a["N2"], a["D"], a["K"],
+        a["scale"], a["maxk"], a["ratio"], a["mask"], a["lq"], a["lk"], a["out"], a["stream"])
+
+
+def test_lse_call_is_declared_and_stops_at_core_count():
+    assert "smla_softmax_lse" in header_functions()
+    for layout in (0, 1):
+        assert call_lse(base_args(layout)) == 161002
+        assert b"core count" in LIB.smla_last_error()
+
+
+@pytest.mark.parametrize("kw,code,msg", [
+    (dict(q=None), 161002, b"required"), (dict(k=None), 161002, b"required"),
+    (dict(out=None), 161002, b"required"),
+    (dict(dtype=2), 161002, b"dtype"), (dict(lk=1), 161002, b"equal"),
+    (dict(N2=2), 161002, b"N2"), (dict(N1=129), 161002, b"N1"), (dict(D=256), 161002, b"512"),
+    (dict(mask=1), 161002, b"mask_mode"), (dict(ratio=129), 161002, b"cmp_ratio"),
+    (dict(sq=FAKE), 161101, b"seqused"),
+    (dict(idx=None), 161002, b"topk must be 0"), (dict(K=0), 161002, b"topk"),
+    (dict(meta=None), 161001, b"metadata"),
+    (dict(layout=1, cu_q=None), 161001, b"cu_seqlens"),
+    (dict(mask=3, ratio=4, res=None), 161001, b"cmp_residual_k"),
+    (dict(mask=0, tlen=None), 161001, b"topk_length"),
+])
+def test_lse_call_errors(kw, code, msg):
+    a = _with(**kw)
+    assert call_lse(a) == code, LIB.smla_last_error()
+    assert msg in LIB.smla_last_error()
+
+
+def test_lse_call_checks_the_metadata_and_empty_q():
+    a = base_args()
+    a["meta"][14] = 16
+    assert call_lse(a) == 161002
+    assert b"does not match" in LIB.smla_last_error()
+    a = base_args(S1=0)
+    for k in ("q", "k", "idx", "tlen", "out"):
+        a[k] = None
+    a["meta"] = None
+    assert call_lse(a) == 0
+    # without keys the rows are still written (-inf), so the call goes on to
+    # the metadata check
+    a = base_args(layout=1, S2=0)
+    a["k"] = None
+    assert call_lse(a) == 161002
+    assert b"core count" in LIB.smla_last_error()

@@ -1,0 +1,147 @@
+"""The GPU softmax_lse producer against the CPU oracle's lse, through the C ABI.
+
+``smla_softmax_lse`` computes, per row and head, the log-sum-exp of the
+scaled scores over the row's used entries (-inf for a row with none): the
+softmax_lse input of the main call (the article's parameter table names it
+the forward pass's log-sum-exp).
+
+Bar: |gpu - oracle| <= 2e-5 wherever the oracle's lse is finite, and -inf
+exactly where it is -inf. An lse error d scales every probability
+exp(s - lse) of its head by exp(-d), so this is the same 2e-5 relative bound
+the main call's outputs are held to. End to end, the main call fed with the
+GPU's lse must give rows that sum to 1 within 1e-4 (every row with a used
+entry), and match the oracle's output for that same lse within 2e-5.
+"""
+
+from __future__ import annotations
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads
+from tests import cases as C
+from tests.test_gpu_parity import (MEDIUM, ROWSUM_TOL, TINY, TOL, _t, rows_view, run_gpu,
+                                   sample_rows, say)
+
+pytestmark = pytest.mark.gpu
+
+TOL_LSE = 2e-5
+
+
+@pytest.fixture(scope="module")
+def smla():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import sparse_mla_attention_02_amd as m
+    return m
+
+
+def metadata(smla, p, core_budget=0):
+    return smla.smla_l1norm_metadata(
+        p.heads_q, p.heads_k, p.head_dim,
+        cu_seqlens_q=_t(p.cu_seqlens_q, "cpu"), cu_seqlens_k=_t(p.cu_seqlens_k, "cpu"),
+        cmp_residual_k=_t(p.cmp_residual_k, "cpu"), batch_size=p.batch,
+        max_seqlen_q=p.max_seqlen_q, max_seqlen_k=p.max_seqlen_k, topk=p.topk,
+        layout_q=p.layout, layout_k=p.layout, mask_mode=p.mask_mode, cmp_ratio=p.cmp_ratio,
+        core_budget=core_budget)
+
+
+def run_lse(smla, p, core_budget=0):
+    """smla_softmax_lse for Problem p; returns (R, G) float32 numpy."""
+    md = metadata(smla, p, core_budget)
+    lse = smla.smla_softmax_lse(
+        p.q.cuda(), p.k.cuda(), sparse_indices=_t(p.sparse_indices),
+        cu_seqlens_q=_t(p.cu_seqlens_q), cu_seqlens_k=_t(p.cu_seqlens_k),
+        cmp_residual_k=_t(p.cmp_residual_k), topk_length=_t(p.topk_length), metadata=md,
+        softmax_scale=p.softmax_scale, max_seqlen_k=p.max_seqlen_k, cmp_ratio=p.cmp_ratio,
+        mask_mode=p.mask_mode, layout_q=p.layout, layout_k=p.layout)
+    torch.cuda.synchronize()
+    assert tuple(lse.shape) == tuple(p.lse_shape())
+    return lse.cpu().numpy().reshape(p.rows, p.groups)
+
+
+def check_lse(name, got, want):
+    dead = np.isneginf(want)
+    assert np.array_equal(np.isneginf(got), dead), f"{name}: -inf pattern"
+    live = ~dead
+    assert np.isfinite(got[live]).all(), f"{name}: non-finite lse"
+    err = np.abs(got[live].astype(np.float64) - want[live].astype(np.float64))
+    worst = float(err.max()) if err.size else 0.0
+    say(f"    max |lse gpu - oracle| = {worst:.2e}")
+    assert worst <= TOL_LSE, f"{name}: max |lse gpu - oracle| = {worst:.3e}"
+
+
+def check_end_to_end(name, smla, p, lse_gpu, rows=None):
+    """The main call fed with the GPU's lse: rows with a used entry sum to 1;
+    on `rows` (all if None) it matches the oracle's output for that lse."""
+    o = rows_view(p, run_gpu(smla, p, lse=lse_gpu.reshape(p.lse_shape()))).cpu().numpy()
+    live = p.row_entries.reshape(p.rows) > 0
+    sums = o.astype(np.float64).sum(axis=1)
+    assert np.all(np.abs(sums[live] - 1.0) <= ROWSUM_TOL), f"{name}: row sums with GPU lse"
+    assert not o[~live].any(), f"{name}: rows without entries must be zero"
+    sel = np.arange(p.rows) if rows is None else rows
+    e = oracle.l1norm(p, rows=None if rows is None else rows,
+                      softmax_lse=lse_gpu.reshape(p.lse_shape()))
+    err = np.abs(o[sel].astype(np.float64) - e.astype(np.float64))
+    assert float(err.max()) <= TOL, f"{name}: output with GPU lse vs oracle"
+
+
+@pytest.mark.parametrize("case", range(len(TINY)), ids=[n for n, _ in TINY])
+def test_lse_tiny(smla, case):
+    name, p = TINY[case]
+    p = C.clone(p)
+    say(f"[lse tiny] {name} layout={p.layout} R={p.rows} G={p.groups} K={p.topk}")
+    want, _ = oracle.lse(p)
+    got = run_lse(smla, p)
+    check_lse(name, got, want)
+
+
+@pytest.mark.parametrize("case", range(len(MEDIUM)), ids=[n for n, _ in MEDIUM])
+def test_lse_medium(smla, case):
+    name, p = MEDIUM[case]
+    p = C.clone(p)
+    say(f"[lse medium] {name} layout={p.layout} R={p.rows} G={p.groups} K={p.topk} "
+        f"dtype={p.dtype}")
+    want, _ = oracle.lse(p)
+    got = run_lse(smla, p)
+    check_lse(name, got, want)
+    check_end_to_end(name, smla, p, got)
+
+
+def test_lse_core_budget_split_gives_the_same_bits(smla):
+    """With a caller's core budget the rows are split over that many
+    workgroups instead of the kernel's co-resident count; each row's value
+    does not depend on which workgroup computes it."""
+    p = C.gen("tnd_varlen", heads_q=128, topk=300, seqlens_q=(70, 33, 90),
+              seqlens_k=(500, 64, 900), seed=61)
+    say("[lse] core budget 7 vs device split")
+    a = run_lse(smla, p)
+    b = run_lse(smla, p, core_budget=7)
+    assert np.array_equal(a.view(np.uint32), b.view(np.uint32))
+
+
+def test_lse_without_keys_is_minus_inf(smla):
+    p = C.gen("tnd_varlen", heads_q=16, topk=4, seqlens_q=(3, 5), seqlens_k=(0, 0), seed=62)
+    say("[lse] no keys")
+    got = run_lse(smla, p)
+    assert np.isneginf(got).all()
+
+
+FULL = ["dsv32", "tnd_varlen", "compressed", "bsnd_causal", "page_example_dense",
+        "dense_causal"]
+
+
+@pytest.mark.parametrize("name", FULL)
+def test_lse_full_size(smla, name):
+    say(f"[lse full] {name}: generating inputs")
+    p = workloads.generate(name)
+    rows = sample_rows(p)
+    say(f"[lse full] {name}: GPU lse (R={p.rows} G={p.groups} K={p.topk})")
+    got = run_lse(smla, p)
+    say(f"[lse full] {name}: oracle lse on {len(rows)} sampled rows")
+    want, _ = oracle.lse(p, rows=rows)
+    check_lse(name, got[rows], want)
+    say(f"[lse full] {name}: main call with the GPU lse, every row")
+    check_end_to_end(name, smla, p, got, rows=rows)
