@@ -42,17 +42,19 @@ def log(msg):
     print(f"[bench] {msg}", file=sys.stderr, flush=True)
 
 
-def algorithmic(p):
-    """(QK flops, unique HBM bytes) of one call on Problem p."""
+def algorithmic(p, op="l1norm"):
+    """(QK flops, unique HBM bytes) of one call on Problem p: the main call
+    (softmax_lse in, the zero-filled output row out) or the lse call (the
+    softmax_lse out, no output row)."""
     pairs = p.valid_pairs()
     flops = 2.0 * p.heads_q * p.head_dim * pairs
     nbytes = (p.q.numel() * p.q.element_size() + p.k.numel() * p.k.element_size()
-              + p.rows * p.groups * 4                       # softmax_lse
+              + p.rows * p.groups * 4                       # softmax_lse (in or out)
               + (p.sparse_indices.size * 4 if p.sparse_indices is not None else 0)
               + (p.topk_length.size * 4 if p.topk_length is not None else 0)
               + (p.cu_seqlens_q.size * 8 if p.cu_seqlens_q is not None else 0)
               + (p.cmp_residual_k.size * 4 if p.cmp_residual_k is not None else 0)
-              + p.rows * p.out_width * 4)                   # output, zero-filled
+              + (p.rows * p.out_width * 4 if op == "l1norm" else 0))  # output row
     return flops, float(nbytes), pairs
 
 
@@ -82,17 +84,24 @@ def measured_traffic(kernel, workload):
         return None
 
 
-def cpu_baseline(p, target_s):
-    """Time the CPU oracle on evenly spaced rows of the workload."""
+def cpu_baseline(p, target_s, op="l1norm"):
+    """Time the CPU oracle (oracle_l1norm given lse, or oracle_lse) on evenly
+    spaced rows of the workload."""
     import oracle
     R = p.rows
     n = p.row_entries.reshape(R).astype(np.int64)
     # calibrate on a few rows per thread, then size the sample for ~target_s
     threads = oracle.num_threads()
     cal = np.linspace(0, R - 1, min(R, 4 * threads)).astype(np.int64)
-    oracle.l1norm(p, rows=cal[:threads])       # warm the thread pool
+    def run(rows):
+        if op == "lse":
+            oracle.lse(p, rows=rows)
+        else:
+            oracle.l1norm(p, rows=rows)
+
+    run(cal[:threads])       # warm the thread pool
     t0 = time.perf_counter()
-    oracle.l1norm(p, rows=cal)
+    run(cal)
     t_cal = time.perf_counter() - t0
     per_pair = t_cal / max(int(n[cal].sum()), 1)
     want_pairs = target_s / max(per_pair, 1e-12)
@@ -100,14 +109,15 @@ def cpu_baseline(p, target_s):
     rows = np.linspace(0, R - 1, count).astype(np.int64)
     log(f"cpu baseline: oracle on {count} rows (~{count * n.mean() * per_pair:.1f} s)")
     t0 = time.perf_counter()
-    oracle.l1norm(p, rows=rows)
+    run(rows)
     t = time.perf_counter() - t0
     pairs = int(n[rows].sum())
     flops = 2.0 * p.heads_q * p.head_dim * pairs
     return {"value": flops / t / 1e12, "unit": "TFLOP/s", "cores": threads,
             "kind": "oracle",
             "sample": f"{count} evenly spaced rows of {R} ({pairs} valid pairs), "
-                      f"oracle_l1norm given lse, {t:.1f} s wall"}
+                      + ("oracle_lse" if op == "lse" else "oracle_l1norm given lse")
+                      + f", {t:.1f} s wall"}
 
 
 def main():
@@ -119,6 +129,9 @@ def main():
                     help="untimed steps run for this long before the warmup steps: an idle "
                          "GPU takes on the order of 100 ms of load to reach its working clock")
     ap.add_argument("--workload", default="dsv32")
+    ap.add_argument("--op", choices=("l1norm", "lse"), default="l1norm",
+                    help="l1norm: the Softmax-L1Norm call (the hot path); lse: the GPU "
+                         "softmax_lse producer on the same workload")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -157,7 +170,7 @@ def main():
 
     log(f"generating workload {args.workload}")
     p = workloads.generate(args.workload)
-    flops, nbytes, pairs = algorithmic(p)
+    flops, nbytes, pairs = algorithmic(p, args.op)
     lse = workloads.lse_standin(p)
     p.softmax_lse = lse
 
@@ -170,7 +183,10 @@ def main():
     cu_q, cu_k, res = t(p.cu_seqlens_q), t(p.cu_seqlens_k), t(p.cmp_residual_k)
     cu_q_h = None if p.cu_seqlens_q is None else torch.from_numpy(p.cu_seqlens_q)
     cu_k_h = None if p.cu_seqlens_k is None else torch.from_numpy(p.cu_seqlens_k)
-    out = torch.empty(p.out_shape(), dtype=torch.float32, device=dev)
+    if args.op == "lse":
+        out = torch.empty(p.lse_shape(), dtype=torch.float32, device=dev)
+    else:
+        out = torch.empty(p.out_shape(), dtype=torch.float32, device=dev)
     stream = torch.cuda.current_stream(dev)
 
     def step(before=None, after=None):
@@ -179,14 +195,17 @@ def main():
             batch_size=p.batch, max_seqlen_q=p.max_seqlen_q, max_seqlen_k=p.max_seqlen_k,
             topk=p.topk, layout_q=p.layout, layout_k=p.layout, mask_mode=p.mask_mode,
             cmp_ratio=p.cmp_ratio, device=0)
+        kw = dict(sparse_indices=idx, cu_seqlens_q=cu_q, cu_seqlens_k=cu_k,
+                  cmp_residual_k=res, topk_length=tlen, metadata=md,
+                  softmax_scale=p.softmax_scale, max_seqlen_k=p.max_seqlen_k,
+                  cmp_ratio=p.cmp_ratio, mask_mode=p.mask_mode, layout_q=p.layout,
+                  layout_k=p.layout, out=out)
         if before is not None:
             before.record(stream)
-        smla.smla_softmax_l1norm(
-            q, k, lse_d, sparse_indices=idx, cu_seqlens_q=cu_q, cu_seqlens_k=cu_k,
-            cmp_residual_k=res, topk_length=tlen, metadata=md,
-            softmax_scale=p.softmax_scale, max_seqlen_k=p.max_seqlen_k,
-            cmp_ratio=p.cmp_ratio, mask_mode=p.mask_mode, layout_q=p.layout,
-            layout_k=p.layout, out=out)
+        if args.op == "lse":
+            smla.smla_softmax_lse(q, k, **kw)
+        else:
+            smla.smla_softmax_l1norm(q, k, lse_d, **kw)
         if after is not None:
             after.record(stream)
         return md
@@ -230,15 +249,18 @@ def main():
     else:
         roof = {"bound": "hbm", "achieved": round(k_gbps, 1), "peak": PEAK_HBM_GBPS,
                 "unit": "GB/s", "frac": round(k_gbps / PEAK_HBM_GBPS, 4)}
-    kernel = KERNELS.get(int(md[24]), "unknown")
+    kernel = "smla_lse_kernel" if args.op == "lse" else KERNELS.get(int(md[24]), "unknown")
     roof["traffic"] = measured_traffic(kernel, p.name)
     roof["kernel"] = kernel
     roof["kernel_ms"] = round(kms, 4)
     roof["algorithmic_flops"] = flops
     roof["algorithmic_bytes"] = nbytes
 
+    metric = "QK TFLOP/s + HBM GB/s, sparse softmax-L1Norm N1=128 topk=2048 D=512"
+    if args.op == "lse":
+        metric = "QK TFLOP/s, GPU softmax_lse over the same selected keys"
     line = {
-        "metric": "QK TFLOP/s + HBM GB/s, sparse softmax-L1Norm N1=128 topk=2048 D=512",
+        "metric": metric,
         "value": round(tflops, 2), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
         "warmup": args.warmup, "prewarm_steps": n_pre, "ms_per_step": round(ms_step, 4),
         "higher_is_better": True,
@@ -248,13 +270,14 @@ def main():
                    "seqlen_q": p.seqlen_q, "seqlen_k": p.seqlen_k, "heads_q": p.heads_q,
                    "heads_k": p.heads_k, "head_dim": p.head_dim, "topk": p.topk,
                    "mask_mode": p.mask_mode, "cmp_ratio": p.cmp_ratio,
-                   "valid_pairs": pairs, "workgroups": int(md[4]),
-                   "lse": "stand-in"},
+                   "valid_pairs": pairs, "op": args.op,
+                   "workgroups": int(md[4]) if args.op == "l1norm" else None,
+                   "lse": "stand-in" if args.op == "l1norm" else "computed"},
         "roofline": roof,
         "cpu_baseline": None,
     }
     if not args.no_cpu_baseline:
-        line["cpu_baseline"] = cpu_baseline(p, args.cpu_seconds)
+        line["cpu_baseline"] = cpu_baseline(p, args.cpu_seconds, args.op)
     print(json.dumps(line), flush=True)
 
 
