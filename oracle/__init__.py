@@ -54,11 +54,11 @@ class COracle:
 
     def __init__(self, path: str):
         lib = ctypes.CDLL(path)
-        common = [_p, _p, _p, _p, _p, _p, _i64, _i64, _i64, _i64, _i64, _i64, _i64,
+        common = [_p, _p, _p, _p, _p, _p, _p, _p, _i64, _i64, _i64, _i64, _i64, _i64, _i64,
                   _i64, _i64, ctypes.c_double, _p, _i64]
         lib.oracle_lse.argtypes = [_p] + common + [_p, _p]
         lib.oracle_lse.restype = ctypes.c_int
-        lib.oracle_l1norm.argtypes = [_p, _p, _p] + common[1:] + [_p]
+        lib.oracle_l1norm.argtypes = [_p, _p, _p] + common[1:] + [_i64, _i64, _p]
         lib.oracle_l1norm.restype = ctypes.c_int
         lib.oracle_num_threads.argtypes = []
         lib.oracle_num_threads.restype = ctypes.c_int
@@ -98,9 +98,10 @@ class COracle:
         l = np.ascontiguousarray(full[a.rows])
         out = np.empty((len(a.rows), p.out_width), dtype=np.float32)
         rc = self.lib.oracle_l1norm(_ptr(a.q), _ptr(a.k), _ptr(l), *a.common()[1:],
+                                    int(bool(getattr(p, "kwide", False))), p.out_width,
                                     _ptr(out))
         if rc != 0:
-            raise ValueError("oracle_l1norm: undecodable row id")
+            raise ValueError("oracle_l1norm: undecodable row id or a column past the width")
         return out
 
     def num_threads(self) -> int:
@@ -145,6 +146,8 @@ class _Args:
         self.cu_q = _c32(p.cu_seqlens_q)
         self.cu_k = _c32(p.cu_seqlens_k)
         self.res = _c32(p.cmp_residual_k)
+        self.su_q = _c32(getattr(p, "seqused_q", None))
+        self.su_k = _c32(getattr(p, "seqused_k", None))
         self.layout = 0 if p.layout == "BSND" else 1
         self.dims = (self.layout, p.batch, p.seqlen_q, p.seqlen_k, G, D, p.topk,
                      p.mask_mode, p.cmp_ratio)
@@ -152,7 +155,8 @@ class _Args:
 
     def common(self):
         return [_ptr(self.k), _ptr(self.idx), _ptr(self.tlen), _ptr(self.cu_q),
-                _ptr(self.cu_k), _ptr(self.res), *self.dims, self.scale,
+                _ptr(self.cu_k), _ptr(self.res), _ptr(self.su_q), _ptr(self.su_k),
+                *self.dims, self.scale,
                 _ptr(self.rows), len(self.rows)]
 
 

@@ -36,7 +36,17 @@
  *     entry are all 0); repeated indices accumulate;
  *   - dense case (idx == NULL): the row's entries are its sequence's keys in
  *     order, entry t being key t (n = S2_b); topk_length does not apply;
- *     mask and output columns are those of the sparse case.
+ *     mask and output columns are those of the sparse case;
+ *   - seqused_q / seqused_k (parameter table: the number of q / k tokens of
+ *     each batch that actually take part), clamped to [0, S1_b] / [0, S2_b]:
+ *     a query i >= seqused_q[b] uses no entry (its row is 0, its lse -inf),
+ *     a key j >= seqused_k[b] is never used (as if not visible); the causal
+ *     alignment keeps S1_b and S2_b. The pages give no example of either:
+ *     parity of this reading is unpinned by the pages;
+ *   - K-wide output (the shape-inference section: the last output dimension
+ *     is K when sparse_indices is given, else S2 (BSND) or max_seqlen_k
+ *     (TND)): entry t's value goes to column t of a row of that width,
+ *     instead of to the key's column.
  *
  * The forward softmax_lse itself (oracle_lse) is not part of the operation:
  * it is the log-sum-exp over the same used entries that the forward pass
@@ -62,6 +72,8 @@ typedef struct {
     int64_t s2;     /* its number of (compressed) keys */
     int64_t kbase;  /* first k row belonging to it */
     int64_t col0;   /* first output column belonging to it */
+    int64_t q_used; /* queries of it that take part (seqused_q, else s1) */
+    int64_t k_used; /* keys of it that take part (seqused_k, else s2) */
 } row_info;
 
 typedef struct {
@@ -71,9 +83,21 @@ typedef struct {
     const int32_t* cu_q;     /* (B+1) for TND */
     const int32_t* cu_k;
     const int32_t* cmp_res;  /* (B) or NULL */
+    const int32_t* su_q;     /* seqused_q (B) or NULL */
+    const int32_t* su_k;     /* seqused_k (B) or NULL */
     int64_t layout, B, S1, S2, G, D, K, mask_mode, cmp_ratio;
     double scale;
 } problem;
+
+static int64_t clamp64(int64_t v, int64_t lo, int64_t hi) {
+    return v < lo ? lo : (v > hi ? hi : v);
+}
+
+/* seqused limits of a decoded row */
+static void set_used(const problem* p, row_info* ri) {
+    ri->q_used = p->su_q ? clamp64(p->su_q[ri->b], 0, ri->s1) : ri->s1;
+    ri->k_used = p->su_k ? clamp64(p->su_k[ri->b], 0, ri->s2) : ri->s2;
+}
 
 static int decode_row(const problem* p, int64_t r, row_info* ri) {
     if (p->layout == LAYOUT_BSND) {
@@ -83,6 +107,7 @@ static int decode_row(const problem* p, int64_t r, row_info* ri) {
         ri->s2 = p->S2;
         ri->kbase = ri->b * p->S2;
         ri->col0 = 0;
+        set_used(p, ri);
         return 0;
     }
     for (int64_t b = 0; b < p->B; ++b) {
@@ -93,6 +118,7 @@ static int decode_row(const problem* p, int64_t r, row_info* ri) {
             ri->s2 = p->cu_k[b + 1] - p->cu_k[b];
             ri->kbase = p->cu_k[b];
             ri->col0 = p->cu_k[b];
+            set_used(p, ri);
             return 0;
         }
     }
@@ -108,11 +134,12 @@ static int visible(const problem* p, const row_info* ri, int64_t j) {
 
 /* number of leading entries of row r that are looked at */
 static int64_t selected_count(const problem* p, const row_info* ri, int64_t r) {
+    if (ri->i >= ri->q_used) return 0; /* query not taking part */
     if (!p->idx) return ri->s2; /* dense: selectedKv = K */
     if (!p->topk_len) {
         if (p->mask_mode == 0) return p->K;
         int64_t nvis = 0;  /* keys of the row's sequence it can see */
-        for (int64_t j = 0; j < ri->s2; ++j) nvis += visible(p, ri, j);
+        for (int64_t j = 0; j < ri->k_used; ++j) nvis += visible(p, ri, j);
         return nvis < p->K ? nvis : p->K;
     }
     int64_t n = p->topk_len[r];
@@ -124,7 +151,7 @@ static int64_t selected_count(const problem* p, const row_info* ri, int64_t r) {
 /* key index of entry t if the entry is used, else -1 */
 static int64_t used_key(const problem* p, const row_info* ri, int64_t r, int64_t t) {
     int64_t j = p->idx ? p->idx[r * p->K + t] : t;
-    if (j < 0 || j >= ri->s2) return -1;
+    if (j < 0 || j >= ri->k_used) return -1;
     if (!visible(p, ri, j)) return -1;
     return j;
 }
@@ -142,11 +169,12 @@ static double score(const problem* p, const float* qrow, int64_t g,
 static void fill_problem(problem* p, const float* k, const int32_t* idx,
                          const int32_t* topk_len, const int32_t* cu_q,
                          const int32_t* cu_k, const int32_t* cmp_res,
-                         int64_t layout, int64_t B, int64_t S1, int64_t S2,
+                         const int32_t* su_q, const int32_t* su_k, int64_t layout, int64_t B, int64_t S1, int64_t S2,
                          int64_t G, int64_t D, int64_t K, int64_t mask_mode,
                          int64_t cmp_ratio, double scale) {
     p->k = k; p->idx = idx; p->topk_len = topk_len;
     p->cu_q = cu_q; p->cu_k = cu_k; p->cmp_res = cmp_res;
+    p->su_q = su_q; p->su_k = su_k;
     p->layout = layout; p->B = B; p->S1 = S1; p->S2 = S2; p->G = G; p->D = D;
     p->K = K; p->mask_mode = mask_mode; p->cmp_ratio = cmp_ratio;
     p->scale = (double)(float)scale;
@@ -165,13 +193,14 @@ static void fill_problem(problem* p, const float* k, const int32_t* idx,
  */
 int oracle_lse(const float* q_rows, const float* k, const int32_t* idx,
                const int32_t* topk_len, const int32_t* cu_q, const int32_t* cu_k,
-               const int32_t* cmp_res, int64_t layout, int64_t B, int64_t S1,
+               const int32_t* cmp_res, const int32_t* su_q, const int32_t* su_k,
+               int64_t layout, int64_t B, int64_t S1,
                int64_t S2, int64_t G, int64_t D, int64_t K, int64_t mask_mode,
                int64_t cmp_ratio, double scale, const int64_t* rows, int64_t nrows,
                float* lse_rows, int32_t* nused) {
     problem p;
-    fill_problem(&p, k, idx, topk_len, cu_q, cu_k, cmp_res, layout, B, S1, S2, G, D,
-                 K, mask_mode, cmp_ratio, scale);
+    fill_problem(&p, k, idx, topk_len, cu_q, cu_k, cmp_res, su_q, su_k, layout, B, S1,
+                 S2, G, D, K, mask_mode, cmp_ratio, scale);
     int bad = 0;
 #pragma omp parallel for schedule(dynamic, 1) reduction(| : bad)
     for (int64_t x = 0; x < nrows; ++x) {
@@ -212,21 +241,24 @@ int oracle_lse(const float* q_rows, const float* k, const int32_t* idx,
 /*
  * The operation itself, for the rows listed in rows[]:
  *   out[c] = 0 for every column c of the row, then for every used entry t
- *   with key j:  out[col0 + j] += (1/G) * sum_g exp(s[g, t] - lse[g]).
+ *   with key j:  out[col0 + j] += (1/G) * sum_g exp(s[g, t] - lse[g])
+ *   (K-wide output: out[t] instead of out[col0 + j]).
  *
  * lse_rows: (nrows, G) float32, the softmax_lse values of those rows
- * out_rows: (nrows, W) float32 out, W = S2 (BSND) or T2 (TND)
+ * out_rows: (nrows, W) float32 out; W = S2 (BSND) or T2 (TND), or with
+ *           kwide the K-wide width (K; dense: S2 or max_seqlen_k)
  */
 int oracle_l1norm(const float* q_rows, const float* k, const float* lse_rows,
                   const int32_t* idx, const int32_t* topk_len, const int32_t* cu_q,
-                  const int32_t* cu_k, const int32_t* cmp_res, int64_t layout,
+                  const int32_t* cu_k, const int32_t* cmp_res, const int32_t* su_q,
+                  const int32_t* su_k, int64_t layout,
                   int64_t B, int64_t S1, int64_t S2, int64_t G, int64_t D, int64_t K,
                   int64_t mask_mode, int64_t cmp_ratio, double scale,
-                  const int64_t* rows, int64_t nrows, float* out_rows) {
+                  const int64_t* rows, int64_t nrows, int64_t kwide, int64_t W,
+                  float* out_rows) {
     problem p;
-    fill_problem(&p, k, idx, topk_len, cu_q, cu_k, cmp_res, layout, B, S1, S2, G, D,
-                 K, mask_mode, cmp_ratio, scale);
-    int64_t W = S2; /* BSND: S2; TND: T2 */
+    fill_problem(&p, k, idx, topk_len, cu_q, cu_k, cmp_res, su_q, su_k, layout, B, S1,
+                 S2, G, D, K, mask_mode, cmp_ratio, scale);
     int bad = 0;
 #pragma omp parallel for schedule(dynamic, 1) reduction(| : bad)
     for (int64_t x = 0; x < nrows; ++x) {
@@ -243,7 +275,9 @@ int oracle_l1norm(const float* q_rows, const float* k, const float* lse_rows,
             double psum = 0.0;
             for (int64_t g = 0; g < G; ++g)
                 psum += exp(score(&p, qrow, g, &ri, j) - (double)lse[g]);
-            acc[ri.col0 + j] += psum / (double)G;
+            const int64_t c = kwide ? t : ri.col0 + j;
+            if (c >= W) { bad |= 2; continue; } /* no room: the caller's W is wrong */
+            acc[c] += psum / (double)G;
         }
         float* o = out_rows + x * W;
         for (int64_t c = 0; c < W; ++c) o[c] = (float)acc[c];

@@ -155,6 +155,55 @@ def tiny_cases():
     return cs + edged
 
 
+def with_seqused(p, seqused_q=None, seqused_k=None):
+    """Copy of p with per-batch seqused_q / seqused_k counts."""
+    c = clone(p)
+    c.seqused_q = None if seqused_q is None else np.asarray(seqused_q, dtype=np.int32)
+    c.seqused_k = None if seqused_k is None else np.asarray(seqused_k, dtype=np.int32)
+    return c
+
+
+def as_kwide(p):
+    """Copy of p asking for the K-wide output (entry t at column t)."""
+    c = clone(p)
+    c.kwide = True
+    return c
+
+
+def next3_cases():
+    """Tiny problems for seqused_q / seqused_k and the K-wide output."""
+    cs = []
+    cs.append(("su_bsnd_causal", with_seqused(
+        gen("tiny", heads_q=3, batch=2, seqlen_q=6, seqlen_k=9, topk=6, mask_mode=3,
+            seed=31), seqused_q=(4, 6), seqused_k=(5, 9))))
+    cs.append(("su_tnd_mask0", with_seqused(
+        gen("tnd_varlen", heads_q=4, topk=5, mask_mode=0, seqlens_q=(4, 3),
+            seqlens_k=(7, 5), seed=32), seqused_q=(2, 3), seqused_k=(4, 0))))
+    cs.append(("su_no_topk_length", with_seqused(
+        gen("tiny", heads_q=2, seqlen_q=6, seqlen_k=8, topk=8, mask_mode=3,
+            with_topk_length=False, seed=33), seqused_k=(5,))))
+    cs.append(("su_dense_tnd_cmp2", with_seqused(
+        gen("tnd_varlen", heads_q=2, topk=0, cmp_ratio=2, cmp_residual=(1, 0),
+            seqlens_q=(5, 3), seqlens_k=(4, 6), seed=34), seqused_q=(5, 1),
+        seqused_k=(2, 6))))
+    cs.append(("kw_bsnd_edges", as_kwide(inject_edges(
+        gen("tiny", heads_q=4, batch=2, seqlen_q=5, seqlen_k=9, topk=6, mask_mode=3,
+            seed=35), seed=5))))
+    cs.append(("kw_tnd_edges", as_kwide(inject_edges(
+        gen("tnd_varlen", heads_q=3, topk=5, seqlens_q=(3, 4), seqlens_k=(6, 8),
+            seed=36), seed=6))))
+    cs.append(("kw_dense_tnd", as_kwide(
+        gen("tnd_varlen", heads_q=2, topk=0, seqlens_q=(3, 4), seqlens_k=(5, 2),
+            seed=37))))
+    cs.append(("kw_dense_bsnd_mask0", as_kwide(
+        gen("tiny", heads_q=3, batch=1, seqlen_q=4, seqlen_k=6, topk=0, mask_mode=0,
+            seed=38))))
+    cs.append(("kw_su_tnd", as_kwide(with_seqused(
+        gen("tnd_varlen", heads_q=5, topk=4, seqlens_q=(4, 5), seqlens_k=(6, 7),
+            seed=39), seqused_q=(3, 5), seqused_k=(6, 3)))))
+    return cs
+
+
 def load_hand_examples():
     with open(os.path.join(GOLDEN, "hand_examples.json")) as f:
         doc = json.load(f)

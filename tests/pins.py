@@ -22,6 +22,18 @@ What fixes each expected value:
 * ``pin_permutation``    entry order and a joint head permutation do not
                          change the result.
 * ``pin_hand``           hand-derived closed forms (tests/golden).
+
+seqused_q / seqused_k and the K-wide output (readings of the pages, which
+give no example of either; their parity is unpinned by the pages):
+
+* ``pin_next3_brute``        the dense formulation on seqused / K-wide cases.
+* ``pin_seqused_identity``   counts equal to the layout's lengths change
+                             nothing, bit for bit.
+* ``pin_seqused_k_padding``  a key past seqused_k acts as an index of -1.
+* ``pin_seqused_q_rows``     rows past seqused_q are 0 (lse -inf); the other
+                             rows are unchanged, bit for bit.
+* ``pin_kwide_gather``       the K-wide row is the scatter row read at each
+                             used entry's key column, 0 elsewhere.
 """
 
 from __future__ import annotations
@@ -270,5 +282,107 @@ def pin_hand(orc):
         np.testing.assert_allclose(o, exp_out, rtol=1e-6, atol=1e-12, err_msg=name)
 
 
+# ----------------------------------------------------------------------------
+# seqused_q / seqused_k and the K-wide output
+
+def _lengths(p):
+    b = C.seq_bounds(p)
+    return [q1 - q0 for (_, q0, q1, _, _) in b], [k1 - k0 for (_, _, _, k0, k1) in b]
+
+
+def _same_bits(a, b):
+    return np.array_equal(np.asarray(a).view(np.uint32), np.asarray(b).view(np.uint32))
+
+
+def pin_next3_brute(orc, problems):
+    pin_brute(orc, C.next3_cases())
+
+
+def pin_seqused_identity(orc, problems):
+    for name, p in problems:
+        s1s, s2s = _lengths(p)
+        c = C.with_seqused(p, s1s, s2s)
+        lp, _ = orc.lse(p)
+        lc, _ = orc.lse(c)
+        assert _same_bits(lp, lc), name
+        p = C.clone(p)
+        p.softmax_lse = lp.reshape(p.lse_shape())
+        c.softmax_lse = p.softmax_lse
+        assert _same_bits(orc.l1norm(p), orc.l1norm(c)), name
+
+
+def pin_seqused_k_padding(orc, problems):
+    for name, p in problems:
+        # the entry count must not depend on the keys (mask 3 without
+        # topk_length caps it by the keys a row sees)
+        if p.sparse_indices is None or (p.topk_length is None and p.mask_mode == 3):
+            continue
+        _, s2s = _lengths(p)
+        su_k = [max(s2 - 2, 0) for s2 in s2s]
+        c = C.with_seqused(p, None, su_k)
+        d = C.clone(p)
+        idx = d.sparse_indices.reshape(d.rows, d.topk)
+        for (b, q0, q1, _, _) in C.seq_bounds(d):
+            blk = idx[q0:q1]
+            blk[blk >= su_k[b]] = -1
+        lc, _ = orc.lse(c)
+        ld, _ = orc.lse(d)
+        assert _same_bits(lc, ld), name
+        c.softmax_lse = lc.reshape(c.lse_shape())
+        d.softmax_lse = c.softmax_lse
+        assert _same_bits(orc.l1norm(c), orc.l1norm(d)), name
+
+
+def pin_seqused_q_rows(orc, problems):
+    for name, p in problems:
+        s1s, _ = _lengths(p)
+        su_q = [s1 // 2 for s1 in s1s]
+        c = C.with_seqused(p, su_q, None)
+        lp, _ = orc.lse(p)
+        lc, _ = orc.lse(c)
+        p = C.clone(p)
+        p.softmax_lse = lp.reshape(p.lse_shape())
+        c.softmax_lse = p.softmax_lse
+        op, oc = orc.l1norm(p), orc.l1norm(c)
+        for (b, q0, q1, _, _) in C.seq_bounds(p):
+            live = slice(q0, q0 + su_q[b])
+            dead = slice(q0 + su_q[b], q1)
+            assert np.isneginf(lc[dead]).all() and not oc[dead].any(), name
+            assert _same_bits(lc[live], lp[live]) and _same_bits(oc[live], op[live]), name
+
+
+def pin_kwide_gather(orc, problems):
+    for name, p in problems:
+        p = C.clone(p)
+        orc.fill_lse(p)
+        o = orc.l1norm(p)
+        c = C.as_kwide(p)
+        ok = orc.l1norm(c)
+        want = np.zeros((p.rows, c.out_width))
+        R, K = p.rows, p.topk
+        idx = None if p.sparse_indices is None else p.sparse_indices.reshape(R, K)
+        tl = None if p.topk_length is None else p.topk_length.reshape(R)
+        for (b, q0, q1, k0, k1) in C.seq_bounds(p):
+            s2 = k1 - k0
+            c0 = C.out_col0(p, b)
+            res = 0 if p.cmp_residual_k is None else int(p.cmp_residual_k[b])
+            vis = library_visibility(q1 - q0, s2, p.cmp_ratio, res, p.mask_mode)
+            for r in range(q0, q1):
+                if idx is None:  # dense: entry t is key t
+                    want[r, :s2] = o[r, c0:c0 + s2]
+                    continue
+                if tl is not None:
+                    n = min(max(int(tl[r]), 0), K)
+                else:
+                    n = K if p.mask_mode == 0 else min(K, int(vis[r - q0].sum()))
+                js = [int(idx[r, t]) for t in range(n)]
+                for t, j in enumerate(js):
+                    if 0 <= j < s2 and vis[r - q0, j] and js.count(j) == 1:
+                        want[r, t] = o[r, c0 + j]
+        assert _same_bits(ok.astype(np.float32), want.astype(np.float32)), name
+
+
 ALL_PINS = [pin_brute, pin_rowsum, pin_support, pin_torch_softmax, pin_sdpa_full,
-            pin_q_zero, pin_arbitrary_lse, pin_permutation]
+            pin_q_zero, pin_arbitrary_lse, pin_permutation, pin_next3_brute,
+            pin_seqused_identity, pin_seqused_k_padding, pin_seqused_q_rows,
+            pin_kwide_gather]

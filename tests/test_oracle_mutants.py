@@ -24,7 +24,12 @@ MUTANTS = {
     "no_div_G": ("psum / (double)G", "psum"),
     "lse_head0": ("(double)lse[g])", "(double)lse[0])"),
     "q_head0": ("const float* qg = qrow + g * p->D;", "const float* qg = qrow;"),
-    "tnd_no_col0": ("acc[ri.col0 + j]", "acc[j]"),
+    "tnd_no_col0": ("kwide ? t : ri.col0 + j;", "kwide ? t : j;"),
+    "seqused_k_ignored": ("j >= ri->k_used) return -1;", "j >= ri->s2) return -1;"),
+    "seqused_q_ignored": ("if (ri->i >= ri->q_used) return 0;", ""),
+    "seqused_k_off_by_one": ("clamp64(p->su_k[ri->b], 0, ri->s2)",
+                             "clamp64(p->su_k[ri->b] + 1, 0, ri->s2)"),
+    "kwide_key_column": ("kwide ? t : ri.col0 + j;", "ri.col0 + j;"),
     "tnd_global_k": ("p->k + (ri->kbase + j) * p->D", "p->k + j * p->D"),
     "causal_off_by_one": ("(j + 1) * r <= ri->i + 1 +", "(j + 1) * r <= ri->i + 2 +"),
     "causal_strict": ("(j + 1) * r <= ri->i", "(j + 1) * r < ri->i"),
@@ -63,7 +68,7 @@ def test_mutant_is_caught(tmp_path, name):
     for pin in pins.ALL_PINS:
         try:
             pin(orc, CASES)
-        except AssertionError:
+        except (AssertionError, ValueError):  # ValueError: the oracle's own range check
             failed.append(pin.__name__)
     try:
         pins.pin_hand(orc)

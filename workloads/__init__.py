@@ -76,6 +76,9 @@ class Problem:
     max_seqlen_k: int
     softmax_lse: Optional[np.ndarray] = None  # float32 (B,N2,S1,G) or (N2,T1,G)
     row_entries: Optional[np.ndarray] = None  # int64 (R,): keys drawn, or (dense) visible
+    seqused_q: Optional[np.ndarray] = None    # int32 (B,): queries of each batch taking part
+    seqused_k: Optional[np.ndarray] = None    # int32 (B,): keys of each batch taking part
+    kwide: bool = False                       # output of K columns (entry t -> column t)
 
     @property
     def groups(self) -> int:
@@ -88,13 +91,18 @@ class Problem:
 
     @property
     def out_width(self) -> int:
-        """Last output dimension: S2 (BSND) or T2 (TND)."""
-        return self.seqlen_k
+        """Last output dimension: S2 (BSND) or T2 (TND); K-wide: K, or without
+        indices S2 (BSND) or max_seqlen_k (TND)."""
+        if not self.kwide:
+            return self.seqlen_k
+        if self.sparse_indices is not None:
+            return self.topk
+        return self.seqlen_k if self.layout == "BSND" else self.max_seqlen_k
 
     def out_shape(self):
         if self.layout == "BSND":
-            return (self.batch, self.seqlen_q, self.heads_k, self.seqlen_k)
-        return (self.seqlen_q, self.heads_k, self.seqlen_k)
+            return (self.batch, self.seqlen_q, self.heads_k, self.out_width)
+        return (self.seqlen_q, self.heads_k, self.out_width)
 
     def lse_shape(self):
         if self.layout == "BSND":
