@@ -48,7 +48,7 @@ enum {
     SMLA_ERR_PARAM_NULLPTR = 161001,
     SMLA_ERR_PARAM_INVALID = 161002,
     SMLA_ERR_UNSUPPORTED = 161101, /* valid on the page, not built here
-                                      (seqused_q/k) */
+                                      (no call returns it at present) */
     SMLA_ERR_RUNTIME = 561001      /* a HIP runtime call failed */
 };
 
@@ -93,7 +93,8 @@ enum { SMLA_MASK_NONE = 0, SMLA_MASK_RIGHT_DOWN_CAUSAL = 3 };
  *   cu_seqlens_q_host, cu_seqlens_k_host  int32 (B+1), required for TND
  *                                         (prefix sums, first entry 0);
  *                                         ignored for BSND
- *   seqused_q_host, seqused_k_host      must be NULL (not supported)
+ *   seqused_q_host, seqused_k_host      optional, not used (the split is
+ *                                         by rows)
  *   cmp_residual_k_host, topk_length_host  optional, only range-checked
  *                                         lengths are not used for balance
  *   batch_size     B (> 0): batches for BSND, sequences for TND (the
@@ -115,7 +116,7 @@ enum { SMLA_MASK_NONE = 0, SMLA_MASK_RIGHT_DOWN_CAUSAL = 3 };
  *
  * Errors: SMLA_ERR_PARAM_NULLPTR (metadata_host NULL, TND without
  * cu_seqlens), SMLA_ERR_PARAM_INVALID (out-of-range value, layout mismatch,
- * inconsistent cu_seqlens), SMLA_ERR_UNSUPPORTED (seqused_*),
+ * inconsistent cu_seqlens),
  * SMLA_ERR_RUNTIME (device query failed; only when core_budget == 0).
  */
 smla_status_t smla_l1norm_metadata(
@@ -147,7 +148,13 @@ smla_status_t smla_l1norm_metadata(
  *                  the mask lets the key through. Used entries of one row
  *                  must be distinct (duplicates are not supported).
  *   cu_seqlens_q, cu_seqlens_k  int32 (B+1) device, required for TND
- *   seqused_q, seqused_k        must be NULL (not supported)
+ *   seqused_q, seqused_k        int32 (B) device, optional (parameter
+ *                  table: the q / k tokens of each batch that take part):
+ *                  a query i >= seqused_q[b] uses no entry (its output row
+ *                  is 0), a key j >= seqused_k[b] is never used (as if not
+ *                  visible); the causal alignment keeps S1_b and S2_b. The
+ *                  pages give no example of either: this reading is this
+ *                  library's own
  *   cmp_residual_k int32 (B): original key length of batch b is
  *                  S2_b*cmp_ratio + cmp_residual_k[b]; required when
  *                  mask_mode == 3 and cmp_ratio != 1, else may be NULL (0)
@@ -176,12 +183,43 @@ smla_status_t smla_l1norm_metadata(
  * is NULL (as on the page) or a value/shape is out of range or does not
  * match the metadata; SMLA_ERR_PARAM_NULLPTR when a conditionally required
  * pointer is NULL (metadata, cu_seqlens for TND, cmp_residual_k,
- * topk_length); SMLA_ERR_UNSUPPORTED for seqused_*;
+ * topk_length);
  * SMLA_ERR_RUNTIME if the launch fails. An empty q (R == 0) or an empty
  * output (S2/T2 == 0) returns SMLA_SUCCESS once the attributes are checked,
  * before any pointer or the metadata is looked at, and launches nothing.
  */
 smla_status_t smla_softmax_l1norm(
+    const void* q, const void* k, const float* softmax_lse,
+    const int32_t* sparse_indices, const int32_t* cu_seqlens_q,
+    const int32_t* cu_seqlens_k, const int32_t* seqused_q, const int32_t* seqused_k,
+    const int32_t* cmp_residual_k, const int32_t* topk_length,
+    const int32_t* metadata_host, int32_t dtype, int64_t batch_size, int64_t seqlen_q,
+    int64_t seqlen_k, int64_t num_heads_q, int64_t num_heads_k, int64_t head_dim,
+    int64_t topk, double softmax_scale, int64_t max_seqlen_k, int64_t cmp_ratio,
+    int64_t mask_mode, int32_t layout_q, int32_t layout_k, float* softmax_l1_norm,
+    void* stream);
+
+/*
+ * smla_softmax_l1norm_kwide - the main call with the K-wide output of the
+ * article's shape-inference section (源码实现解读, shape 推导): the last
+ * output dimension is K when sparse_indices is given, and without it S2
+ * (BSND) or max_seqlen_k (TND). Entry t of a row (index t of its
+ * sparse_indices row, or key t without them) puts its value in column t;
+ * columns of unused entries are 0.
+ *
+ * Arguments are smla_softmax_l1norm's, with
+ *
+ *   softmax_l1_norm fp32 out (B,S1,N2,K') | (T1,N2,K'), K' = topk, or
+ *                  without sparse_indices S2 (BSND) or max_seqlen_k (TND);
+ *                  every element written
+ *   max_seqlen_k   without sparse_indices in TND: the output width; it
+ *                  must equal the metadata's (field 13)
+ *
+ * Errors: as smla_softmax_l1norm, plus SMLA_ERR_PARAM_INVALID for a TND
+ * max_seqlen_k that differs from the metadata's without sparse_indices.
+ * A width of 0 returns SMLA_SUCCESS and launches nothing.
+ */
+smla_status_t smla_softmax_l1norm_kwide(
     const void* q, const void* k, const float* softmax_lse,
     const int32_t* sparse_indices, const int32_t* cu_seqlens_q,
     const int32_t* cu_seqlens_k, const int32_t* seqused_q, const int32_t* seqused_k,

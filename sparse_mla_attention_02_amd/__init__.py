@@ -71,6 +71,8 @@ def _load():
                                         i64, i64, i64, i64, dbl, i64, i64, i64, i32, i32, p,
                                         p]
     lib.smla_softmax_l1norm.restype = i32
+    lib.smla_softmax_l1norm_kwide.argtypes = lib.smla_softmax_l1norm.argtypes
+    lib.smla_softmax_l1norm_kwide.restype = i32
     lib.smla_softmax_lse.argtypes = [p, p, p, p, p, p, p, p, p, p, i32, i64, i64, i64, i64, i64,
                                      i64, i64, dbl, i64, i64, i64, i32, i32, p, p]
     lib.smla_softmax_lse.restype = i32
@@ -219,6 +221,9 @@ def _marshal(q, k, sparse_indices, cu_seqlens_q, cu_seqlens_k, seqused_q, sequse
             raise SmlaError(SMLA_ERR_PARAM_INVALID, f"topk_length shape != {want}")
     if c.cr is not None and c.cr.numel() != B:
         raise SmlaError(SMLA_ERR_PARAM_INVALID, "cmp_residual_k must have B elements")
+    for t, name in ((c.sq, "seqused_q"), (c.sk, "seqused_k")):
+        if t is not None and t.numel() != B:
+            raise SmlaError(SMLA_ERR_PARAM_INVALID, f"{name} must have B elements")
     if (c.cq is None) != (c.ck is None) or (c.cq is not None and c.ck.numel() != c.cq.numel()):
         raise SmlaError(SMLA_ERR_PARAM_INVALID, "cu_seqlens_q/k must come as a pair of B+1")
     return c
@@ -253,13 +258,17 @@ def sparse_flash_mla_softmax_l1_norm(
         q, k, softmax_lse, *, sparse_indices=None, cu_seqlens_q=None, cu_seqlens_k=None,
         seqused_q=None, seqused_k=None, cmp_residual_k=None, topk_length=None,
         metadata=None, softmax_scale=1.0, max_seqlen_k=0, cmp_ratio=1, mask_mode=0,
-        layout_q="BSND", layout_k="BSND", out: Optional[torch.Tensor] = None) -> torch.Tensor:
+        layout_q="BSND", layout_k="BSND", out: Optional[torch.Tensor] = None,
+        kwide: bool = False) -> torch.Tensor:
     """Softmax-L1Norm: head mean of exp(mask(q.k_sel^T*scale) - lse).
 
     All tensors must be on the same GPU; they are made contiguous (the page's
     op definition declares AutoContiguous inputs). ``metadata`` (int32 (64,),
     from the metadata call) is required and must be on the CPU. ``out``
     (optional, fp32, contiguous, output shape) receives the result.
+    ``kwide`` (not a page argument) selects the K-wide output of the page's
+    shape inference: entry t's value at column t of a row of K columns
+    (without sparse_indices: S2, or max_seqlen_k for TND).
     Enqueued on the current stream.
     """
     if softmax_lse is None:
@@ -274,12 +283,17 @@ def sparse_flash_mla_softmax_l1_norm(
     if tuple(softmax_lse.shape) != tuple(c.lse_shape):
         raise SmlaError(SMLA_ERR_PARAM_INVALID,
                         f"softmax_lse shape {tuple(softmax_lse.shape)} != {c.lse_shape}")
-    out = _out_tensor(out, c.out_shape, c.dev, "out")
+    shape = c.out_shape
+    if kwide:
+        w = c.K if c.idx is not None else (c.sk_len if c.lq == 0 else int(max_seqlen_k or 0))
+        shape = tuple(shape[:-1]) + (w,)
+    out = _out_tensor(out, shape, c.dev, "out")
     if out.numel() == 0:
         return out  # empty q or empty output: nothing to compute
     metadata = _metadata(metadata)
+    fn = _lib.smla_softmax_l1norm_kwide if kwide else _lib.smla_softmax_l1norm
     with torch.cuda.device(c.dev):
-        _check(_lib.smla_softmax_l1norm(
+        _check(fn(
             _ptr(c.q), _ptr(c.k), _ptr(softmax_lse), _ptr(c.idx), _ptr(c.cq), _ptr(c.ck),
             _ptr(c.sq), _ptr(c.sk), _ptr(c.cr), _ptr(c.tl), _ptr(metadata),
             *_tail(c, softmax_scale, max_seqlen_k, cmp_ratio, mask_mode, out)))

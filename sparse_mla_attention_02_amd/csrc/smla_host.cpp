@@ -143,14 +143,15 @@ smla_status_t smla_l1norm_metadata(
     int64_t batch_size, int64_t max_seqlen_q, int64_t max_seqlen_k, int64_t topk,
     int32_t layout_q, int32_t layout_k, int64_t mask_mode, int64_t cmp_ratio,
     int32_t device, int32_t core_budget, int32_t* metadata_host) {
+    // (the split is by rows; these refine nothing here)
     (void)cmp_residual_k_host;
     (void)topk_length_host;
+    (void)seqused_q_host;
+    (void)seqused_k_host;
     if (!metadata_host) return fail(SMLA_ERR_PARAM_NULLPTR, "metadata_host is NULL");
     smla_status_t st = check_common(num_heads_q, num_heads_k, head_dim, layout_q, layout_k,
                                     mask_mode, cmp_ratio);
     if (st != SMLA_SUCCESS) return st;
-    if (seqused_q_host || seqused_k_host)
-        return fail(SMLA_ERR_UNSUPPORTED, "seqused_q / seqused_k are not supported");
     // topk == 0: the dense case (no sparse_indices)
     if (topk < 0) return fail(SMLA_ERR_PARAM_INVALID, "topk must be >= 0");
     if (core_budget < 0) return fail(SMLA_ERR_PARAM_INVALID, "core_budget must be >= 0");
@@ -237,10 +238,11 @@ smla_status_t smla_l1norm_metadata(
 
 namespace {
 
-// Checks shared by the main call (softmax_lse in, softmax_l1_norm out) and
-// the lse call (lse_in NULL, out = softmax_lse), then the kernel arguments.
-// *nothing_to_do is set when there are no rows (the page: an empty q returns
-// directly) or, for the main call, an empty output row.
+// Checks shared by the main call (softmax_lse in, softmax_l1_norm out; kwide:
+// the K-wide output) and the lse call (lse_in NULL, out = softmax_lse), then
+// the kernel arguments. *nothing_to_do is set when there are no rows (the
+// page: an empty q returns directly) or, for the main call, an empty output
+// row.
 smla_status_t prepare(const void* q, const void* k, const int32_t* sparse_indices,
                       const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k,
                       const int32_t* seqused_q, const int32_t* seqused_k,
@@ -250,8 +252,8 @@ smla_status_t prepare(const void* q, const void* k, const int32_t* sparse_indice
                       int64_t num_heads_k, int64_t head_dim, int64_t topk,
                       double softmax_scale, int64_t max_seqlen_k, int64_t cmp_ratio,
                       int64_t mask_mode, int32_t layout_q, int32_t layout_k, bool lse_call,
-                      const float* lse_in, float* out, smla::KernelArgs* out_args,
-                      bool* nothing_to_do) {
+                      bool kwide, const float* lse_in, float* out,
+                      smla::KernelArgs* out_args, bool* nothing_to_do) {
     *nothing_to_do = false;
     if (dtype != SMLA_DTYPE_FP16 && dtype != SMLA_DTYPE_BF16)
         return fail(SMLA_ERR_PARAM_INVALID, "dtype must be FLOAT16 or BFLOAT16");
@@ -259,8 +261,6 @@ smla_status_t prepare(const void* q, const void* k, const int32_t* sparse_indice
                                     mask_mode, cmp_ratio);
     if (st != SMLA_SUCCESS) return st;
     if (max_seqlen_k < 0) return fail(SMLA_ERR_PARAM_INVALID, "max_seqlen_k must be >= 0");
-    if (seqused_q || seqused_k)
-        return fail(SMLA_ERR_UNSUPPORTED, "seqused_q / seqused_k are not supported");
     if (batch_size < 0 || seqlen_q < 0 || seqlen_k < 0)
         return fail(SMLA_ERR_PARAM_INVALID, "sizes must be >= 0");
     const bool tnd = layout_q == SMLA_LAYOUT_TND;
@@ -269,7 +269,10 @@ smla_status_t prepare(const void* q, const void* k, const int32_t* sparse_indice
 
     const int64_t R = tnd ? seqlen_q : batch_size * seqlen_q;
     const int64_t rows_k = tnd ? seqlen_k : batch_size * seqlen_k;
-    const int64_t W = seqlen_k;
+    const bool dense = !sparse_indices;
+    // output row width: S2 / T2, or K-wide (the shape-inference section) K,
+    // without sparse_indices S2 (BSND) or max_seqlen_k (TND)
+    const int64_t W = !kwide ? seqlen_k : (!dense ? topk : (tnd ? max_seqlen_k : seqlen_k));
     // empty q (both calls) or empty output row (main call): nothing is read
     // or written. Without keys every lse row is -inf, which the lse call
     // still writes.
@@ -286,7 +289,6 @@ smla_status_t prepare(const void* q, const void* k, const int32_t* sparse_indice
     // no sparse_indices: the dense case, every key of the row's batch or
     // sequence (stage 1 of the page's formula selects the whole K); topk
     // is then 0 and topk_length does not apply
-    const bool dense = !sparse_indices;
     if (dense && topk != 0)
         return fail(SMLA_ERR_PARAM_INVALID, "topk must be 0 without sparse_indices");
     if (!dense && topk < 1)
@@ -315,6 +317,10 @@ smla_status_t prepare(const void* q, const void* k, const int32_t* sparse_indice
         return fail(SMLA_ERR_PARAM_INVALID, "metadata does not match the call's shapes");
     if (!tnd && (m[12] != seqlen_q || m[13] != seqlen_k))
         return fail(SMLA_ERR_PARAM_INVALID, "metadata does not match S1/S2");
+    if (kwide && dense && tnd && m[13] != max_seqlen_k)
+        return fail(SMLA_ERR_PARAM_INVALID,
+                    "K-wide TND output without sparse_indices: max_seqlen_k must be the "
+                    "metadata's max_seqlen_k");
     if (m[4] < 1 || m[4] > m[0])
         return fail(SMLA_ERR_PARAM_INVALID, "metadata core count is out of range");
 
@@ -329,6 +335,9 @@ smla_status_t prepare(const void* q, const void* k, const int32_t* sparse_indice
     a.cu_q = cu_seqlens_q;
     a.cu_k = cu_seqlens_k;
     a.cmp_res = cmp_residual_k;
+    a.su_q = seqused_q;
+    a.su_k = seqused_k;
+    a.kwide = kwide ? 1 : 0;
     a.R = R;
     a.W = W;
     a.rows_k = rows_k;
@@ -390,7 +399,35 @@ smla_status_t smla_softmax_l1norm(
                                seqused_k, cmp_residual_k, topk_length, metadata_host, dtype,
                                batch_size, seqlen_q, seqlen_k, num_heads_q, num_heads_k,
                                head_dim, topk, softmax_scale, max_seqlen_k, cmp_ratio,
-                               mask_mode, layout_q, layout_k, false, softmax_lse,
+                               mask_mode, layout_q, layout_k, false, false, softmax_lse,
+                               softmax_l1_norm, &a, &nothing);
+    if (st != SMLA_SUCCESS) return st;
+    if (nothing) return ok();
+    const int ht = smla::head_tiles_for(a.G);
+    hipError_t e = smla::launch(a, ht, dtype == SMLA_DTYPE_BF16, layout_q == SMLA_LAYOUT_TND,
+                                static_cast<hipStream_t>(stream));
+    if (e != hipSuccess)
+        return fail(SMLA_ERR_RUNTIME, "kernel launch failed: %s", hipGetErrorString(e));
+    return ok();
+}
+
+smla_status_t smla_softmax_l1norm_kwide(
+    const void* q, const void* k, const float* softmax_lse,
+    const int32_t* sparse_indices, const int32_t* cu_seqlens_q,
+    const int32_t* cu_seqlens_k, const int32_t* seqused_q, const int32_t* seqused_k,
+    const int32_t* cmp_residual_k, const int32_t* topk_length,
+    const int32_t* metadata_host, int32_t dtype, int64_t batch_size, int64_t seqlen_q,
+    int64_t seqlen_k, int64_t num_heads_q, int64_t num_heads_k, int64_t head_dim,
+    int64_t topk, double softmax_scale, int64_t max_seqlen_k, int64_t cmp_ratio,
+    int64_t mask_mode, int32_t layout_q, int32_t layout_k, float* softmax_l1_norm,
+    void* stream) {
+    smla::KernelArgs a;
+    bool nothing = false;
+    smla_status_t st = prepare(q, k, sparse_indices, cu_seqlens_q, cu_seqlens_k, seqused_q,
+                               seqused_k, cmp_residual_k, topk_length, metadata_host, dtype,
+                               batch_size, seqlen_q, seqlen_k, num_heads_q, num_heads_k,
+                               head_dim, topk, softmax_scale, max_seqlen_k, cmp_ratio,
+                               mask_mode, layout_q, layout_k, false, true, softmax_lse,
                                softmax_l1_norm, &a, &nothing);
     if (st != SMLA_SUCCESS) return st;
     if (nothing) return ok();
@@ -417,8 +454,8 @@ smla_status_t smla_softmax_lse(
                                seqused_k, cmp_residual_k, topk_length, metadata_host, dtype,
                                batch_size, seqlen_q, seqlen_k, num_heads_q, num_heads_k,
                                head_dim, topk, softmax_scale, max_seqlen_k, cmp_ratio,
-                               mask_mode, layout_q, layout_k, true, nullptr, softmax_lse,
-                               &a, &nothing);
+                               mask_mode, layout_q, layout_k, true, false, nullptr,
+                               softmax_lse, &a, &nothing);
     if (st != SMLA_SUCCESS) return st;
     if (nothing) return ok();
     const int ht = smla::head_tiles_for(a.G);

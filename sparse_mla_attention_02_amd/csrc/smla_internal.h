@@ -16,9 +16,11 @@ struct KernelArgs {
     const int32_t* cu_q;      // (B+1) for TND
     const int32_t* cu_k;      // (B+1) for TND
     const int32_t* cmp_res;   // (B) or nullptr
+    const int32_t* su_q;      // seqused_q (B) or nullptr
+    const int32_t* su_k;      // seqused_k (B) or nullptr
     float* out;               // (R, W) fp32; the lse kernel: (R, G) fp32 softmax_lse
     int64_t R;                // query rows
-    int64_t W;                // output row width (S2 or T2)
+    int64_t W;                // output row width (S2 or T2; K-wide: the entry count)
     int64_t rows_k;           // rows of k (B*S2 or T2)
     int32_t B;                // batches or sequences
     int32_t S1, S2;           // BSND per-batch lengths
@@ -31,6 +33,7 @@ struct KernelArgs {
     int32_t num_wg;           // workgroups launched (metadata field 4)
     int32_t snake;            // row order: 1 = snake, 0 = plain strided
     int32_t dense;            // 1: no sparse_indices, entry t of a row is key t (idx NULL)
+    int32_t kwide;            // 1: entry t's value goes to column t of a W = K wide row
 };
 
 // Head tiles of 32 heads each that one row needs: 1, 2 or 4.

@@ -140,12 +140,13 @@ __device__ __forceinline__ RowInfo decode_row(const KernelArgs& a, int64_t r) {
         i = r - q0;
         kbase = uload(a.cu_k, b);
         s2 = (int64_t)uload(a.cu_k, b + 1) - kbase;
-        // never reach past the k tensor or the output row
+        // never reach past the k tensor or the output row (K-wide rows hold
+        // entries, not key columns)
         if (kbase < 0) kbase = 0;
         if (s2 > a.rows_k - kbase) s2 = a.rows_k - kbase;
-        if (s2 > a.W - kbase) s2 = a.W - kbase;
+        if (!a.kwide && s2 > a.W - kbase) s2 = a.W - kbase;
         if (s2 < 0) s2 = 0;
-        col0 = kbase;
+        col0 = a.kwide ? 0 : kbase;
     } else {
         // rows and k rows number fewer than 2^31 (checked on the host): 32-bit
         // division
@@ -173,6 +174,14 @@ __device__ __forceinline__ RowInfo decode_row(const KernelArgs& a, int64_t r) {
             if (vis < 0) vis = 0;
         }
     }
+    // seqused_k: keys past the count take no part (the visible keys stay a
+    // prefix); seqused_q: a query past the count uses nothing. Both counts
+    // are clamped to the sequence's lengths.
+    if (a.su_k) {
+        const int64_t ku = uload(a.su_k, b);
+        if (ku < vis) vis = ku < 0 ? 0 : ku;
+    }
+    if (a.su_q && i >= (int64_t)uload(a.su_q, b)) vis = 0;
     // entries to look at (selectBlockCount): topk_length clamped to [0, K];
     // without it K, or under the causal mask no more than the visible keys.
     // Dense (no sparse_indices): the row's keys in order, so the visible ones
@@ -334,8 +343,9 @@ __global__ __launch_bounds__(64 * HT, 2) void smla_l1norm_kernel(KernelArgs a) {
         const int32_t* __restrict__ irow = a.idx + r * a.K;
         const int ntiles = (ri.n + kTile - 1) / kTile;
         // columns [seg0, seg1) can hold values; everything else is zero
+        // (K-wide: the columns are the entries [0, n))
         const int64_t seg0 = ri.col0;
-        const int64_t seg1 = ri.col0 + (ntiles > 0 ? ri.vis : 0);
+        const int64_t seg1 = ri.col0 + (ntiles > 0 ? (a.kwide ? ri.n : ri.vis) : 0);
 
         // raw index of slot `col` of a tile (any value; checked where used);
         // dense: the entry itself (the descriptor then has no range, so the
@@ -403,7 +413,7 @@ __global__ __launch_bounds__(64 * HT, 2) void smla_l1norm_kernel(KernelArgs a) {
             } else {
                 const int32_t j = __shfl(key, slot);
                 if (lane < kSlotsPerWave && tile >= 0 && used(tile, slot, j))
-                    orow[ri.col0 + j] = v;
+                    orow[a.kwide ? tile * kTile + slot : ri.col0 + j] = v;
             }
         };
 
@@ -471,7 +481,7 @@ __global__ __launch_bounds__(64 * HT, 2) void smla_l1norm_kernel(KernelArgs a) {
                     const int t = tid + i * NT;
                     const int32_t j = jre[i];
                     if (t < ri.n && (uint32_t)j < (uint32_t)ri.vis) {
-                        const int64_t c = ri.col0 + j - c0;
+                        const int64_t c = (a.kwide ? t : ri.col0 + j) - c0;
                         if (c >= 0 && c < len) stage[c + m0] = vals[t];
                     }
                 }
@@ -1153,14 +1163,16 @@ __global__ __launch_bounds__(256, 1) void smla_wide_kernel(KernelArgs a) {
             const int e = tile * kWideKeys + slot;
             const bool used =
                 lane < kRowsPerWave && tile >= 0 && e < ric.n && (uint32_t)j < (uint32_t)ric.vis;
+            // the entry's column: its key's (col0 + j), or K-wide the entry e
+            const int32_t c = a.kwide ? e : (int32_t)(ric.col0 + j);
             if (ROWBUF) {
-                // (col0 + j < W <= kRowCap; other lanes write their own sink)
-                rowbuf[used ? (int)(ric.col0 + j) : kRowCap + lane] = tot * a.inv_g;
+                // (c < W <= kRowCap; other lanes write their own sink)
+                rowbuf[used ? c : kRowCap + lane] = tot * a.inv_g;
             } else {
                 // (the builtin's data operand is an integer: pass the bits)
                 __builtin_amdgcn_raw_buffer_store_b32(
                     __builtin_bit_cast(uint32_t, tot * a.inv_g), orsrc,
-                    used ? (int)((uint32_t)(ric.col0 + j) * 4u) : 0x7ffffff0, 0, 0);
+                    used ? (int)((uint32_t)c * 4u) : 0x7ffffff0, 0, 0);
             }
         };
 

@@ -164,10 +164,10 @@ def test_metadata_error_paths_raw():
     # metadata pointer NULL
     assert f(128, 1, 512, None, None, None, None, None, None, 1, 8, 8, 4, 0, 0, 0, 1, 0, 36,
              None) == 161001
-    # seqused given
+    # seqused given: accepted (the split does not use it)
     one = np.zeros(1, dtype=np.int32)
-    assert f(128, 1, 512, None, None, one.ctypes.data, None, None, None, 1, 8, 8, 4, 0, 0, 0,
-             1, 0, 36, m.ctypes.data) == 161101
+    assert f(128, 1, 512, None, None, one.ctypes.data, one.ctypes.data, None, None, 1, 8, 8,
+             4, 0, 0, 0, 1, 0, 36, m.ctypes.data) == 0
     # TND without cu_seqlens
     assert f(128, 1, 512, None, None, None, None, None, None, 1, 0, 0, 4, 1, 1, 0, 1, 0, 36,
              m.ctypes.data) == 161001
@@ -241,7 +241,7 @@ def _with(**kw):
     (dict(N1=0), 161002, b"N1"), (dict(N1=129), 161002, b"N1"), (dict(D=256), 161002, b"512"),
     (dict(mask=1), 161002, b"mask_mode"), (dict(ratio=0), 161002, b"cmp_ratio"),
     (dict(ratio=129), 161002, b"cmp_ratio"), (dict(maxk=-1), 161002, b"max_seqlen_k"),
-    (dict(sq=FAKE), 161101, b"seqused"), (dict(sk=FAKE), 161101, b"seqused"),
+    (dict(sq=FAKE), 161002, b"core count"), (dict(sk=FAKE), 161002, b"core count"),
     (dict(idx=None), 161002, b"topk must be 0"), (dict(K=0), 161002, b"topk"),
     (dict(meta=None), 161001, b"metadata"),
     (dict(layout=1, cu_q=None), 161001, b"cu_seqlens"),
@@ -334,7 +334,7 @@ def test_lse_call_is_declared_and_stops_at_core_count():
     (dict(dtype=2), 161002, b"dtype"), (dict(lk=1), 161002, b"equal"),
     (dict(N2=2), 161002, b"N2"), (dict(N1=129), 161002, b"N1"), (dict(D=256), 161002, b"512"),
     (dict(mask=1), 161002, b"mask_mode"), (dict(ratio=129), 161002, b"cmp_ratio"),
-    (dict(sq=FAKE), 161101, b"seqused"),
+    (dict(sq=FAKE), 161002, b"core count"),
     (dict(idx=None), 161002, b"topk must be 0"), (dict(K=0), 161002, b"topk"),
     (dict(meta=None), 161001, b"metadata"),
     (dict(layout=1, cu_q=None), 161001, b"cu_seqlens"),
@@ -363,3 +363,41 @@ def test_lse_call_checks_the_metadata_and_empty_q():
     a["k"] = None
     assert call_lse(a) == 161002
     assert b"core count" in LIB.smla_last_error()
+
+
+# ---------------------------------------------------------------- K-wide call
+
+def call_kwide(a):
+    md = a["meta"]
+    mp = md.ctypes.data if md is not None else None
+    return LIB.smla_softmax_l1norm_kwide(
+        a["q"], a["k"], a["lse"], a["idx"], a["cu_q"], a["cu_k"], a["sq"], a["sk"], a["res"],
+        a["tlen"], mp, a["dtype"], a["B"], a["S1"], a["S2"], a["N1"], a["N2"], a["D"], a["K"],
+        a["scale"], a["maxk"], a["ratio"], a["mask"], a["lq"], a["lk"], a["out"], a["stream"])
+
+
+def test_kwide_call_is_declared_and_checked_like_the_main_call():
+    assert "smla_softmax_l1norm_kwide" in header_functions()
+    for layout in (0, 1):
+        assert call_kwide(base_args(layout)) == 161002
+        assert b"core count" in LIB.smla_last_error()
+    for kw, code in [(dict(lse=None), 161002), (dict(out=None), 161002), (dict(N2=2), 161002),
+                     (dict(meta=None), 161001), (dict(mask=0, tlen=None), 161001)]:
+        assert call_kwide(_with(**kw)) == code, (kw, LIB.smla_last_error())
+
+
+def test_kwide_dense_tnd_width_is_max_seqlen_k():
+    # dense TND K-wide rows are max_seqlen_k wide, which must be the metadata's
+    a = base_args(layout=1, K=0)
+    a["idx"] = None
+    a["meta"][13] = 64
+    a["maxk"] = 63
+    assert call_kwide(a) == 161002
+    assert b"max_seqlen_k" in LIB.smla_last_error()
+    a["maxk"] = 64
+    assert call_kwide(a) == 161002
+    assert b"core count" in LIB.smla_last_error()
+    # width 0: nothing to do, no pointer looked at
+    a["maxk"] = 0
+    a["out"] = None
+    assert call_kwide(a) == 0
