@@ -145,3 +145,27 @@ def test_lse_full_size(smla, name):
     check_lse(name, got[rows], want)
     say(f"[lse full] {name}: main call with the GPU lse, every row")
     check_end_to_end(name, smla, p, got, rows=rows)
+
+
+@pytest.mark.parametrize("heads", [16, 128])
+def test_lse_score_jump(smla, heads):
+    """Eight keys scaled by 100 and moved to the end of every row's index
+    list: their scores lie far above the base the earlier tiles set (well
+    past the range the 16-head kernel's lazy step accepts), so the last tile
+    must rebase exactly. Scores are large here, so the bar is relative:
+    |d| <= 2e-5 * max(1, |lse|)."""
+    p = C.gen("tiny", heads_q=heads, batch=1, seqlen_q=8, seqlen_k=300, topk=256, mask_mode=0,
+              seed=63)
+    idx = p.sparse_indices.reshape(p.rows, p.topk)
+    jump = np.arange(8) * 37
+    for r in range(p.rows):
+        late = np.isin(idx[r], jump)
+        idx[r] = np.concatenate([idx[r][~late], idx[r][late]])
+    p.k.reshape(-1, p.head_dim)[torch.from_numpy(jump)] *= 100
+    say(f"[lse] score jump, G={heads}")
+    want, _ = oracle.lse(p)
+    got = run_lse(smla, p)
+    assert np.isfinite(got).all()
+    d = np.abs(got.astype(np.float64) - want.astype(np.float64))
+    assert (d <= 2e-5 * np.maximum(1.0, np.abs(want))).all(), float(d.max())
+    assert np.abs(want).max() > 50  # the jump is really there
