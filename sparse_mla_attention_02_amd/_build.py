@@ -26,6 +26,9 @@ def command(out: str) -> list:
     return [hipcc(), f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-shared",
             # keep the compiler from forming packed fp32 VALU instructions
             "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+            # MFMA results in VGPRs: the pipelined kernel's epilogue then reads
+            # its scores without an AGPR-to-VGPR copy per element
+            "-mllvm", "-amdgpu-mfma-vgpr-form",
             "-Wall", "-Wno-unused-command-line-argument",
             "-I", INCLUDE, "-I", CSRC, "-x", "hip", *SOURCES, "-o", out]
 

@@ -953,21 +953,25 @@ __device__ __forceinline__ void wide_tile(const uint4* __restrict__ cur,
     acc0 = f32x16_t{};
     acc1 = f32x16_t{};
     float sum = 0.0f, t = 0.0f, ex = 0.0f;
-    int32_t soff = 0, soa = 0, kb = 0;
+    int32_t soa[2] = {0, 0}, sob[2] = {0, 0}, kb = 0;
     int32_t ma = (int32_t)m0a, mb = (int32_t)m0b;
     pin_s(ma);
     pin_s(mb);
 #pragma unroll
     for (int s = 0; s < kSteps; ++s) {
+        // One wave per SIMD issues one instruction per 4 cycles, and the matrix
+        // core takes 32 cycles per MFMA: the step's other instructions are split
+        // between the two MFMAs (seven issue slots before each MFMA's successor
+        // can start), instead of queueing after the second one.
         __builtin_amdgcn_sched_barrier(0);
         acc0 = mfma_32x32x16<BF16>(qa0[s], ring[s & 7], acc0);
-        acc1 = mfma_32x32x16<BF16>(qa1[s], ring[s & 7], acc1);
-        // keeps the MFMAs in their step (as pure operations they may
-        // otherwise be sunk towards the far uses of the accumulators)
-        asm volatile("" ::"a"(acc0), "a"(acc1));
-        if (s == kBarStep) barrier_after_vmcnt(0);
-        ring[(s + kLead) & 7] =
-            s + kLead < kSteps ? cur[2 * (s + kLead)] : nxt[2 * (s + kLead - kSteps)];
+        // keeps the MFMA in its slot (as a pure operation it may otherwise be
+        // sunk towards the far uses of the accumulator); the accumulators live
+        // in VGPRs, so the epilogue reads the scores without a copy (Q, the A
+        // operand, sits in AGPRs, which the matrix core reads at full rate)
+        asm volatile("" ::"v"(acc0));
+        // first gap: the sum of element s-2, the exp of element s-1, the read of
+        // element s, and the scalar offset of the next step's load
         if (s >= 2) {
             sum += ex;
             pin(sum);
@@ -976,34 +980,39 @@ __device__ __forceinline__ void wide_tile(const uint4* __restrict__ cur,
             ex = __builtin_amdgcn_exp2f(t);
             pin(ex);
         }
-        // the previous tile's score, read from the accumulator register where
-        // its MFMAs left it (left to the compiler, the whole accumulator set is
-        // copied out before the first MFMA of the tile, which then waits for
-        // the last MFMA of the previous tile to drain); the last write to it
-        // is at least a step and the tail of the previous tile away
-        float pv;
-        asm volatile("v_accvgpr_read_b32 %0, %1" : "=v"(pv) : "a"(s < 16 ? prev0[s] : prev1[s - 16]));
+        // the previous tile's score, read where its MFMAs left it
+        const float pv = s < 16 ? prev0[s] : prev1[s - 16];
+        // (the load of step s+1 takes it: a scalar written by a VALU
+        // instruction needs five wait states before a load reads it)
+        if (s <= 8) {
+            soa[s & 1] = __builtin_amdgcn_readlane(offa, s + 7);
+            pin_s(soa[s & 1]);
+        } else if (s >= 24 && s <= 30) {
+            sob[s & 1] = __builtin_amdgcn_readlane(offb, s - 24);
+            pin_s(sob[s & 1]);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+        acc1 = mfma_32x32x16<BF16>(qa1[s], ring[s & 7], acc1);
+        asm volatile("" ::"v"(acc1));
+        // second gap: the operand read 8 steps ahead, the fma of element s and
+        // the gather loads
+        if (s == kBarStep) barrier_after_vmcnt(0);
+        ring[(s + kLead) & 7] =
+            s + kLead < kSteps ? cur[2 * (s + kLead)] : nxt[2 * (s + kLead - kSteps)];
         t = __builtin_fmaf(pv, c, -l2[s]);
         pin(t);
         if (s >= 1 && s <= 9) {  // stream A: row s + 6 of tile t+1
-            dma_row(desc_a, (uint32_t)ma, soa, voff);
+            dma_row(desc_a, (uint32_t)ma, soa[(s - 1) & 1], voff);
             ma += (int32_t)stepa;
             pin_s(ma);
         }
         if (s >= 25) {  // stream B: row s - 25 of tile t+2
-            dma_row(desc_b, (uint32_t)mb, soff, voff);
+            dma_row(desc_b, (uint32_t)mb, sob[(s - 1) & 1], voff);
             mb += (int32_t)stepb;
             pin_s(mb);
         }
         if (s == 12) kb = key_b();
         if (s == 20) offb = offs_b(kb);
-        if (s <= 8) {
-            soa = __builtin_amdgcn_readlane(offa, s + 7);
-            pin_s(soa);
-        } else if (s >= 24 && s <= 30) {
-            soff = __builtin_amdgcn_readlane(offb, s - 24);
-            pin_s(soff);
-        }
         mid(s);
     }
     __builtin_amdgcn_sched_barrier(0);
@@ -1017,7 +1026,7 @@ __device__ __forceinline__ void wide_tile(const uint4* __restrict__ cur,
 // written out once with 16-byte stores at the row end; the index list is then
 // single-buffered to make room. Otherwise rows are zero-filled in memory and
 // the values stored straight to their columns.
-template <bool BF16, bool TND, bool ROWBUF>
+template <bool BF16, bool TND, bool ROWBUF, bool DENSE>
 __global__ __launch_bounds__(256, 1) void smla_wide_kernel(KernelArgs a) {
     constexpr int HT = 4;
     constexpr int NT = 256;
@@ -1068,7 +1077,7 @@ __global__ __launch_bounds__(256, 1) void smla_wide_kernel(KernelArgs a) {
     // row r's index list into ibuf[slot] (kIdxOps loads; entries past K read
     // as zero)
     auto load_idx_row = [&](int64_t r, int slot) {
-        if (a.dense) return;  // no index list: entry t is key t
+        if (DENSE) return;  // no index list: entry t is key t
         const i32x4_t id = raw_desc(a.idx + r * a.K, (uint32_t)a.K * 4u);
 #pragma unroll
         for (int i = 0; i < kIdxOps; ++i) {
@@ -1155,9 +1164,9 @@ __global__ __launch_bounds__(256, 1) void smla_wide_kernel(KernelArgs a) {
         if (nt == 0) return 0;
         const i32x4_t kd = k_desc(ri);
         const int32_t* il = ibuf[slot];
-        const int32_t o0 = row_off(ri, 0, a.dense ? my_slot : il[my_slot]);
+        const int32_t o0 = row_off(ri, 0, DENSE ? my_slot : il[my_slot]);
         const int32_t o1 =
-            row_off(ri, 1, nt > 1 ? (a.dense ? kWideKeys + my_slot : il[kWideKeys + my_slot]) : 0);
+            row_off(ri, 1, nt > 1 ? (DENSE ? kWideKeys + my_slot : il[kWideKeys + my_slot]) : 0);
         int32_t so[kRowsPerWave];
 #pragma unroll
         for (int i = 0; i < kRowsPerWave; ++i) {
@@ -1278,7 +1287,7 @@ __global__ __launch_bounds__(256, 1) void smla_wide_kernel(KernelArgs a) {
             float parts[4], tot = 0.0f, sum_prev;
             auto key_b = [&]() -> int32_t {
                 const int32_t j = irow[((tile + 2) & 31) * kWideKeys + my_slot];
-                return a.dense ? (tile + 2) * kWideKeys + my_slot : j;
+                return DENSE ? (tile + 2) * kWideKeys + my_slot : j;
             };
             auto offs_b = [&](int32_t key) -> int32_t {
                 return has2 ? row_off(ric, tile + 2, key) : (qb ? q_off(tile & 1) : 0);
@@ -1293,7 +1302,7 @@ __global__ __launch_bounds__(256, 1) void smla_wide_kernel(KernelArgs a) {
                     // (each LDS read is used a few steps after it is issued)
                     if (s == 20) {
                         const int32_t j = irow[((tile - 2) & 31) * kWideKeys + slot];
-                        jv = a.dense ? (tile - 2) * kWideKeys + slot : j;
+                        jv = DENSE ? (tile - 2) * kWideKeys + slot : j;
                     } else if (s == kBarStep + 2) {
                         // tile-2's partial sums, written at the end of tile-1
                         // and visible after the barrier
@@ -1336,7 +1345,7 @@ __global__ __launch_bounds__(256, 1) void smla_wide_kernel(KernelArgs a) {
         auto finish = [&](const float (*pr)[kWideKeys], int tile) {
             const float tot = pr[0][slot] + pr[1][slot] + pr[2][slot] + pr[3][slot];
             store_value(tile, tot,
-                        a.dense ? tile * kWideKeys + slot : irow[(tile & 31) * kWideKeys + slot]);
+                        DENSE ? tile * kWideKeys + slot : irow[(tile & 31) * kWideKeys + slot]);
         };
         if (ntiles >= 2) finish(red[ntiles & 1], ntiles - 2);
         if (ntiles >= 1) finish(redl, ntiles - 1);
@@ -1378,19 +1387,27 @@ __global__ __launch_bounds__(256, 1) void smla_wide_kernel(KernelArgs a) {
 
 template <bool BF16, bool TND>
 hipError_t launch_wide_t(const KernelArgs& a, hipStream_t stream) {
-    if (a.W <= kRowCap)
-        hipLaunchKernelGGL((smla_wide_kernel<BF16, TND, true>), dim3(a.num_wg), dim3(256), 0,
-                           stream, a);
-    else
-        hipLaunchKernelGGL((smla_wide_kernel<BF16, TND, false>), dim3(a.num_wg), dim3(256), 0,
-                           stream, a);
+    // (dense rows, without an index list, are a variant of their own: the
+    // choice would otherwise be a branch in every tile)
+    const dim3 grid(a.num_wg), block(256);
+    if (a.W <= kRowCap) {
+        if (a.dense)
+            hipLaunchKernelGGL((smla_wide_kernel<BF16, TND, true, true>), grid, block, 0, stream, a);
+        else
+            hipLaunchKernelGGL((smla_wide_kernel<BF16, TND, true, false>), grid, block, 0, stream, a);
+    } else {
+        if (a.dense)
+            hipLaunchKernelGGL((smla_wide_kernel<BF16, TND, false, true>), grid, block, 0, stream, a);
+        else
+            hipLaunchKernelGGL((smla_wide_kernel<BF16, TND, false, false>), grid, block, 0, stream, a);
+    }
     return hipGetLastError();
 }
 
 template <bool BF16, bool TND>
 hipError_t occupancy_wide_t(int* out) {
     return hipOccupancyMaxActiveBlocksPerMultiprocessor(
-        out, reinterpret_cast<const void*>(&smla_wide_kernel<BF16, TND, true>), 256, 0);
+        out, reinterpret_cast<const void*>(&smla_wide_kernel<BF16, TND, true, false>), 256, 0);
 }
 
 template <int HT, bool BF16, bool TND>
