@@ -936,33 +936,32 @@ constexpr int kWideBufBytes = kWideKeys * kRowBytes;
 // the MFMA stream does not drain between tiles. `mid(s)` is the caller's
 // spread-out work, called at the end of step s.
 constexpr int kBarStep = 24;
-template <bool BF16, typename Key, typename Offs, typename Mid>
+template <bool BF16, typename Mid1, typename Mid2>
 __device__ __forceinline__ void wide_tile(const uint4* __restrict__ cur,
                                           const uint4* __restrict__ nxt, uint4 (&ring)[8],
                                           const uint4* qa0, const uint4* qa1,
                                           const f32x16_t& prev0, const f32x16_t& prev1,
-                                          const float* l2, float c, float* prev_sum,
-                                          i32x4_t desc_a, i32x4_t desc_b, uint32_t m0a,
-                                          uint32_t stepa,
-                                          int32_t offa, uint32_t m0b, uint32_t stepb,
-                                          Key key_b, Offs offs_b, int32_t& offb, uint32_t voff,
-                                          Mid mid,
-                                          f32x16_t& acc0, f32x16_t& acc1) {
+                                          const float* l2, float c, float& pt, float& pex,
+                                          float& psum, i32x4_t desc_a, i32x4_t desc_b,
+                                          int32_t m0a, int32_t stepa, int32_t offa, int32_t m0b,
+                                          int32_t stepb, const int32_t& offb, uint32_t voff,
+                                          Mid1 mid1, Mid2 mid2, f32x16_t& acc0,
+                                          f32x16_t& acc1) {
     constexpr int kSteps = kChunks / 2;
     constexpr int kLead = 8;
     acc0 = f32x16_t{};
     acc1 = f32x16_t{};
     float sum = 0.0f, t = 0.0f, ex = 0.0f;
-    int32_t soa[2] = {0, 0}, sob[2] = {0, 0}, kb = 0;
-    int32_t ma = (int32_t)m0a, mb = (int32_t)m0b;
+    int32_t soa[2] = {0, 0}, sob[2] = {0, 0};
+    int32_t ma = m0a, mb = m0b;
     pin_s(ma);
     pin_s(mb);
 #pragma unroll
     for (int s = 0; s < kSteps; ++s) {
         // One wave per SIMD issues one instruction per 4 cycles, and the matrix
         // core takes 32 cycles per MFMA: the step's other instructions are split
-        // between the two MFMAs (seven issue slots before each MFMA's successor
-        // can start), instead of queueing after the second one.
+        // between the two MFMAs (about six issue slots before each MFMA's
+        // successor can start), instead of queueing after the second one.
         __builtin_amdgcn_sched_barrier(0);
         acc0 = mfma_32x32x16<BF16>(qa0[s], ring[s & 7], acc0);
         // keeps the MFMA in its slot (as a pure operation it may otherwise be
@@ -970,8 +969,15 @@ __device__ __forceinline__ void wide_tile(const uint4* __restrict__ cur,
         // in VGPRs, so the epilogue reads the scores without a copy (Q, the A
         // operand, sits in AGPRs, which the matrix core reads at full rate)
         asm volatile("" ::"v"(acc0));
-        // first gap: the sum of element s-2, the exp of element s-1, the read of
-        // element s, and the scalar offset of the next step's load
+        // first gap: the previous tile's last two elements (step 0), the sum of
+        // element s-2, the exp of element s-1 and the scalar offset of the
+        // next step's load
+        if (s == 0) {
+            psum += pex;
+            pin(psum);
+            pex = __builtin_amdgcn_exp2f(pt);
+            pin(pex);
+        }
         if (s >= 2) {
             sum += ex;
             pin(sum);
@@ -980,8 +986,6 @@ __device__ __forceinline__ void wide_tile(const uint4* __restrict__ cur,
             ex = __builtin_amdgcn_exp2f(t);
             pin(ex);
         }
-        // the previous tile's score, read where its MFMAs left it
-        const float pv = s < 16 ? prev0[s] : prev1[s - 16];
         // (the load of step s+1 takes it: a scalar written by a VALU
         // instruction needs five wait states before a load reads it)
         if (s <= 8) {
@@ -991,35 +995,47 @@ __device__ __forceinline__ void wide_tile(const uint4* __restrict__ cur,
             sob[s & 1] = __builtin_amdgcn_readlane(offb, s - 24);
             pin_s(sob[s & 1]);
         }
+        mid1(s);
         __builtin_amdgcn_sched_barrier(0);
         acc1 = mfma_32x32x16<BF16>(qa1[s], ring[s & 7], acc1);
         asm volatile("" ::"v"(acc1));
-        // second gap: the operand read 8 steps ahead, the fma of element s and
-        // the gather loads
+        // second gap: the operand read 8 steps ahead, the fma of element s
+        // (the previous tile's score, read where its MFMAs left it) and the
+        // gather loads
+        if (s == 0) {
+            psum += pex;  // the previous tile's sum, written out by mid1(1)
+            pin(psum);
+        }
         if (s == kBarStep) barrier_after_vmcnt(0);
         ring[(s + kLead) & 7] =
             s + kLead < kSteps ? cur[2 * (s + kLead)] : nxt[2 * (s + kLead - kSteps)];
-        t = __builtin_fmaf(pv, c, -l2[s]);
+        t = __builtin_fmaf(s < 16 ? prev0[s] : prev1[s - 16], c, -l2[s]);
         pin(t);
         if (s >= 1 && s <= 9) {  // stream A: row s + 6 of tile t+1
             dma_row(desc_a, (uint32_t)ma, soa[(s - 1) & 1], voff);
-            ma += (int32_t)stepa;
+            ma += stepa;
             pin_s(ma);
         }
         if (s >= 25) {  // stream B: row s - 25 of tile t+2
             dma_row(desc_b, (uint32_t)mb, sob[(s - 1) & 1], voff);
-            mb += (int32_t)stepb;
+            mb += stepb;
             pin_s(mb);
         }
-        if (s == 12) kb = key_b();
-        if (s == 20) offb = offs_b(kb);
-        mid(s);
+        mid2(s);
     }
     __builtin_amdgcn_sched_barrier(0);
-    sum += ex;
-    ex = __builtin_amdgcn_exp2f(t);
-    *prev_sum = sum + ex;
+    // this tile's last two elements are finished by the next tile's step 0
+    pt = t;
+    pex = ex;
+    psum = sum;
 }
+
+// A compile-time tile parity (tile & 1), so that the buffer addresses of a
+// tile fold into constants.
+template <int P>
+struct Par {
+    static constexpr int value = P;
+};
 
 // ROWBUF (output rows of at most kRowCap columns): each row is assembled in
 // LDS (zeroed at the row start, values written as they are finished) and
@@ -1267,68 +1283,166 @@ __global__ __launch_bounds__(256, 1) void smla_wide_kernel(KernelArgs a) {
             for (int i = 0; i < 8; ++i) ring[i] = r0[2 * i];
         }
         f32x16_t xa0, xa1, xb0 = {}, xb1 = {};
-        auto body = [&](int tile, const f32x16_t& prev0, const f32x16_t& prev1, f32x16_t& acc0,
-                        f32x16_t& acc1) {
+        // The scalar state of a tile's two load streams: buffer descriptors,
+        // LDS destinations and their steps. A stream whose tile does not exist
+        // takes the next row's Q (stream A only from tile 1 on: tile 0's
+        // offsets come from the row start) or, with no next row, the dummy row.
+        struct Ctl {
+            int32_t da[4], db[4];
+            int32_t m0a, m0b, sa, sb;
+        };
+        auto ctl_of = [&](auto P, int tile) -> Ctl {
+            constexpr int par = decltype(P)::value;  // tile & 1
             const bool has1 = tile + 1 < ntiles, has2 = tile + 2 < ntiles;
-            // streams whose tile does not exist take the next row's Q (stream
-            // A only from tile 1 on: tile 0's offsets come from the row start)
             const bool qa = !has1 && more && tile >= 1, qb = !has2 && more;
-            const uint4* cur = kbuf[tile & 1] + (32 * kh + col) * kPitch + half;
-            const uint4* nxt = kbuf[(tile + 1) & 1] + (32 * kh + col) * kPitch + half;
-            const uint32_t m0a = __builtin_amdgcn_readfirstlane(
-                has1 || qa ? kbuf_lds + (uint32_t)(((tile + 1) & 1) * kWideBufBytes +
-                                                   (kRowsPerWave * wave + 7) * kRowBytes)
-                           : dummy_lds);
-            const uint32_t m0b = __builtin_amdgcn_readfirstlane(
-                has2 || qb ? kbuf_lds + (uint32_t)((tile & 1) * kWideBufBytes +
-                                                   kRowsPerWave * wave * kRowBytes)
-                           : dummy_lds);
-            int32_t jv = -1, offb = 0;
-            float parts[4], tot = 0.0f, sum_prev;
-            auto key_b = [&]() -> int32_t {
-                const int32_t j = irow[((tile + 2) & 31) * kWideKeys + my_slot];
-                return DENSE ? (tile + 2) * kWideKeys + my_slot : j;
-            };
-            auto offs_b = [&](int32_t key) -> int32_t {
-                return has2 ? row_off(ric, tile + 2, key) : (qb ? q_off(tile & 1) : 0);
-            };
-            wide_tile<BF16>(
-                cur, nxt, ring, qa0, qa1, prev0, prev1, l2, a.c_scale, &sum_prev,
-                uniform_desc(has1 ? kdesc : qdesc), uniform_desc(has2 ? kdesc : qdesc), m0a,
-                has1 || qa ? (uint32_t)kRowBytes : 0u, offa, m0b,
-                has2 || qb ? (uint32_t)kRowBytes : 0u,
-                key_b, offs_b, offb, voff16,
-                [&](int s) {
-                    // (each LDS read is used a few steps after it is issued)
-                    if (s == 20) {
-                        const int32_t j = irow[((tile - 2) & 31) * kWideKeys + slot];
-                        jv = DENSE ? (tile - 2) * kWideKeys + slot : j;
-                    } else if (s == kBarStep + 2) {
-                        // tile-2's partial sums, written at the end of tile-1
-                        // and visible after the barrier
+            const i32x4_t da = uniform_desc(has1 ? kdesc : qdesc);
+            const i32x4_t db = uniform_desc(has2 ? kdesc : qdesc);
+            Ctl r;
 #pragma unroll
-                        for (int p = 0; p < 4; ++p) parts[p] = red[tile & 1][p][slot];
-                    } else if (s == kBarStep + 4) {
+            for (int i = 0; i < 4; ++i) {
+                r.da[i] = da[i];
+                r.db[i] = db[i];
+            }
+            r.m0a = __builtin_amdgcn_readfirstlane((int32_t)(
+                has1 || qa ? kbuf_lds + (uint32_t)((1 - par) * kWideBufBytes +
+                                                   (kRowsPerWave * wave + 7) * kRowBytes)
+                           : dummy_lds));
+            r.m0b = __builtin_amdgcn_readfirstlane(
+                (int32_t)(has2 || qb ? kbuf_lds + (uint32_t)(par * kWideBufBytes +
+                                                             kRowsPerWave * wave * kRowBytes)
+                                     : dummy_lds));
+            r.sa = has1 || qa ? kRowBytes : 0;
+            r.sb = has2 || qb ? kRowBytes : 0;
+            return r;
+        };
+        // the state of a tile with two more tiles after it: both streams
+        // gather key rows
+        auto ctl_steady = [&](auto P) -> Ctl {
+            constexpr int par = decltype(P)::value;
+            Ctl r;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                r.da[i] = __builtin_amdgcn_readfirstlane(kdesc[i]);
+                r.db[i] = r.da[i];
+            }
+            r.m0a = __builtin_amdgcn_readfirstlane((int32_t)(
+                kbuf_lds + (uint32_t)((1 - par) * kWideBufBytes +
+                                      (kRowsPerWave * wave + 7) * kRowBytes)));
+            r.m0b = __builtin_amdgcn_readfirstlane((int32_t)(
+                kbuf_lds + (uint32_t)(par * kWideBufBytes + kRowsPerWave * wave * kRowBytes)));
+            r.sa = kRowBytes;
+            r.sb = kRowBytes;
+            return r;
+        };
+        // the previous tile's unfinished epilogue (see wide_tile)
+        float pt = 0.0f, pex = 0.0f, psum = 0.0f;
+        // Tile `tile` (parity P): `cc` holds its stream state, `oa` the gather
+        // offsets of tile+1 (formed by tile-1); tile+2's offsets are formed in
+        // step 18 into `ob`. Tile-2's values are stored in steps 25..30: its
+        // index is read in step 14 and its destination formed in step 21, its
+        // four partial sums (finished in its step 0, written in step 1) read
+        // after the barrier.
+        auto body = [&](auto P, auto STEADY, int tile, const Ctl& cc, int32_t oa, int32_t& ob,
+                        const f32x16_t& prev0, const f32x16_t& prev1, f32x16_t& acc0,
+                        f32x16_t& acc1) {
+            constexpr int par = decltype(P)::value;
+            constexpr bool steady = decltype(STEADY)::value != 0;
+            const uint4* cur = kbuf[par] + (32 * kh + col) * kPitch + half;
+            const uint4* nxt = kbuf[1 - par] + (32 * kh + col) * kPitch + half;
+            int32_t kb = 0, jv = -1, sdst = 0;
+            float parts[4], tot = 0.0f;
+            wide_tile<BF16>(
+                cur, nxt, ring, qa0, qa1, prev0, prev1, l2, a.c_scale, pt, pex, psum,
+                i32x4_t{cc.da[0], cc.da[1], cc.da[2], cc.da[3]},
+                i32x4_t{cc.db[0], cc.db[1], cc.db[2], cc.db[3]}, cc.m0a, cc.sa, oa, cc.m0b, cc.sb, ob, voff16,
+                [&](int s) {  // first gap
+                    if (s == 1) {
+                        // tile-2's partial sums, finished in step 0 (tiles 0
+                        // and 1: an unused slot)
+                        red[par][2 * hg + half][32 * kh + col] = psum;
+                    } else if (s == kBarStep + 1) {
+                        // tile-2's partial sums of every wave, written in step
+                        // 1 and visible after the barrier
+                        parts[0] = red[par][0][slot];
+                        parts[1] = red[par][1][slot];
+                    } else if (s == kBarStep + 2) {
+                        parts[2] = red[par][2][slot];
+                        parts[3] = red[par][3][slot];
+                    } else if (s == kBarStep + 3) {
                         tot = parts[0] + parts[1];
                         pin(tot);
-                    } else if (s == kBarStep + 5) {
+                    } else if (s == kBarStep + 4) {
                         tot += parts[2];
                         pin(tot);
-                    } else if (s == kBarStep + 6) {
+                    } else if (s == kBarStep + 5) {
                         tot += parts[3];
                         pin(tot);
-                    } else if (s == kBarStep + 7) {
-                        store_value(tile - 2, tot, tile >= 2 ? jv : -1);
+                    } else if (s == kBarStep + 6) {
+                        const float v = tot * a.inv_g;
+                        if (ROWBUF) {
+                            // (a column below W <= kRowCap, or this lane's sink)
+                            rowbuf[sdst] = v;
+                        } else {
+                            // (the builtin's data operand is an integer: pass
+                            // the bits; an offset past the row is dropped)
+                            __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, v),
+                                                                  orsrc, sdst, 0, 0);
+                        }
+                    }
+                },
+                [&](int s) {  // second gap (each LDS read is used steps later)
+                    // (the tile number is pinned in the step, so that no part
+                    // of the step's work is hoisted into an earlier step)
+                    int32_t tl = tile;
+                    if (s == 12 || s == 14 || s == 18 || s == 21) pin_s(tl);
+                    if (s == 12) {
+                        kb = DENSE ? (tl + 2) * kWideKeys + my_slot
+                                   : irow[((tl + 2) & 31) * kWideKeys + my_slot];
+                    } else if (s == 14) {
+                        jv = DENSE ? (tl - 2) * kWideKeys + slot
+                                   : irow[((tl - 2) & 31) * kWideKeys + slot];
+                    } else if (s == 18) {
+                        // (a steady tile has tile+2; otherwise stream B takes
+                        // the next row's Q, if there is one)
+                        const bool has2 = steady || tl + 2 < ntiles;
+                        ob = has2 ? row_off(ric, tl + 2, kb) : (more ? q_off(par) : 0);
+                    } else if (s == 21) {
+                        // entry e = (tile-2)*64 + slot of lanes < 16: its
+                        // column (its key's col0 + j, or K-wide e) if used
+                        const int e = (tl - 2) * kWideKeys + slot;
+                        const bool used = lane < kRowsPerWave && tl >= 2 && e < ric.n &&
+                                          (uint32_t)jv < (uint32_t)ric.vis;
+                        const int32_t cc2 = a.kwide ? e : (int32_t)(ric.col0 + jv);
+                        sdst = ROWBUF ? (used ? cc2 : kRowCap + lane)
+                                      : (used ? (int32_t)((uint32_t)cc2 * 4u) : 0x7ffffff0);
                     }
                 },
                 acc0, acc1);
-            offa = offb;
-            red[(tile - 1) & 1][2 * hg + half][32 * kh + col] = sum_prev;  // tile 0: unused
         };
-        for (int tile = 0; tile < ntiles; tile += 2) {
-            body(tile, xb0, xb1, xa0, xa1);
+        // Pairs of tiles with two more after them run the steady body (stream
+        // state fixed per parity); the last two or three tiles of a row form
+        // their state at each tile boundary. Even tiles fill xa from xb, odd
+        // tiles xb from xa. (Both loops are unrolled by two, so that each
+        // register set keeps its registers across the tiles of a loop.)
+        const Ctl cs0 = ctl_steady(Par<0>{}), cs1 = ctl_steady(Par<1>{});
+        int32_t offb = 0;
+        int tile = 0;
+        for (; tile + 3 < ntiles; tile += 2) {
+            body(Par<0>{}, Par<1>{}, tile, cs0, offa, offb, xb0, xb1, xa0, xa1);
+            body(Par<1>{}, Par<1>{}, tile + 1, cs1, offb, offa, xa0, xa1, xb0, xb1);
+        }
+        for (; tile < ntiles; tile += 2) {
+            const Ctl c0 = ctl_of(Par<0>{}, tile);
+            body(Par<0>{}, Par<0>{}, tile, c0, offa, offb, xb0, xb1, xa0, xa1);
             if (tile + 1 >= ntiles) break;
-            body(tile + 1, xa0, xa1, xb0, xb1);
+            const Ctl c1 = ctl_of(Par<1>{}, tile + 1);
+            body(Par<1>{}, Par<0>{}, tile + 1, c1, offb, offa, xa0, xa1, xb0, xb1);
+        }
+        // tile ntiles-2's epilogue still lacks its last two elements
+        if (ntiles >= 2) {
+            psum += pex;
+            psum += __builtin_amdgcn_exp2f(pt);
+            red[ntiles & 1][2 * hg + half][32 * kh + col] = psum;
         }
         const f32x16_t& prev0 = (ntiles & 1) ? xa0 : xb0;
         const f32x16_t& prev1 = (ntiles & 1) ? xa1 : xb1;
