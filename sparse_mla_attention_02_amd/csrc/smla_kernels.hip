@@ -814,6 +814,8 @@ __device__ __forceinline__ void consume(int32_t v) { asm volatile("" ::"v"(v)); 
 // Keeps a value's computation at this point of the instruction stream (pure
 // arithmetic is otherwise free to move to its first use).
 __device__ __forceinline__ void pin(float& v) { asm volatile("" : "+v"(v)); }
+// The same for an integer kept in a vector register.
+__device__ __forceinline__ void pin_v(int32_t& v) { asm volatile("" : "+v"(v)); }
 // The same for a wave-uniform value kept in a scalar register (the
 // readfirstlane costs nothing where the compiler already knows the value is
 // uniform, and makes it legal where it cannot prove it).
@@ -970,8 +972,8 @@ __device__ __forceinline__ void wide_tile(const uint4* __restrict__ cur,
         // operand, sits in AGPRs, which the matrix core reads at full rate)
         asm volatile("" ::"v"(acc0));
         // first gap: the previous tile's last two elements (step 0), the sum of
-        // element s-2, the exp of element s-1 and the scalar offset of the
-        // next step's load
+        // element s-2, the exp of element s-1, the fma of element s and the
+        // scalar offset of the next step's load
         if (s == 0) {
             psum += pex;
             pin(psum);
@@ -988,6 +990,10 @@ __device__ __forceinline__ void wide_tile(const uint4* __restrict__ cur,
         }
         // (the load of step s+1 takes it: a scalar written by a VALU
         // instruction needs five wait states before a load reads it)
+        // the fma of element s (the previous tile's score, read where its
+        // MFMAs left it)
+        t = __builtin_fmaf(s < 16 ? prev0[s] : prev1[s - 16], c, -l2[s]);
+        pin(t);
         if (s <= 8) {
             soa[s & 1] = __builtin_amdgcn_readlane(offa, s + 7);
             pin_s(soa[s & 1]);
@@ -999,9 +1005,7 @@ __device__ __forceinline__ void wide_tile(const uint4* __restrict__ cur,
         __builtin_amdgcn_sched_barrier(0);
         acc1 = mfma_32x32x16<BF16>(qa1[s], ring[s & 7], acc1);
         asm volatile("" ::"v"(acc1));
-        // second gap: the operand read 8 steps ahead, the fma of element s
-        // (the previous tile's score, read where its MFMAs left it) and the
-        // gather loads
+        // second gap: the operand read 8 steps ahead and the gather loads
         if (s == 0) {
             psum += pex;  // the previous tile's sum, written out by mid1(1)
             pin(psum);
@@ -1009,8 +1013,6 @@ __device__ __forceinline__ void wide_tile(const uint4* __restrict__ cur,
         if (s == kBarStep) barrier_after_vmcnt(0);
         ring[(s + kLead) & 7] =
             s + kLead < kSteps ? cur[2 * (s + kLead)] : nxt[2 * (s + kLead - kSteps)];
-        t = __builtin_fmaf(s < 16 ? prev0[s] : prev1[s - 16], c, -l2[s]);
-        pin(t);
         if (s >= 1 && s <= 9) {  // stream A: row s + 6 of tile t+1
             dma_row(desc_a, (uint32_t)ma, soa[(s - 1) & 1], voff);
             ma += stepa;
@@ -1168,8 +1170,9 @@ __global__ __launch_bounds__(256, 1) void smla_wide_kernel(KernelArgs a) {
     // byte offset of the key row of slot my_slot of `tile` holding raw index
     // j: j's row if the entry is used, else row 0 (loaded, never read)
     auto row_off = [&](const RowInfo& ri, int tile, int32_t j) -> int32_t {
-        return (tile * kWideKeys + my_slot < ri.n && (uint32_t)j < (uint32_t)ri.vis) ? (j << 10)
-                                                                                       : 0;
+        // (bitwise: a short-circuit here compiles to a branch)
+        return ((tile * kWideKeys + my_slot < ri.n) & ((uint32_t)j < (uint32_t)ri.vis)) ? (j << 10)
+                                                                                         : 0;
     };
     // A row's start: tile 0 (16 rows) into buffer 0 and rows 0..6 of tile 1
     // into buffer 1 (to the dummy row when there is no tile 1), 23 loads in
@@ -1406,15 +1409,17 @@ __global__ __launch_bounds__(256, 1) void smla_wide_kernel(KernelArgs a) {
                         // the next row's Q, if there is one)
                         const bool has2 = steady || tl + 2 < ntiles;
                         ob = has2 ? row_off(ric, tl + 2, kb) : (more ? q_off(par) : 0);
+                        pin_v(ob);  // (computed here, not where it is used)
                     } else if (s == 21) {
                         // entry e = (tile-2)*64 + slot of lanes < 16: its
                         // column (its key's col0 + j, or K-wide e) if used
                         const int e = (tl - 2) * kWideKeys + slot;
-                        const bool used = lane < kRowsPerWave && tl >= 2 && e < ric.n &&
-                                          (uint32_t)jv < (uint32_t)ric.vis;
+                        const bool used = (lane < kRowsPerWave) & (tl >= 2) & (e < ric.n) &
+                                          ((uint32_t)jv < (uint32_t)ric.vis);
                         const int32_t cc2 = a.kwide ? e : (int32_t)(ric.col0 + jv);
                         sdst = ROWBUF ? (used ? cc2 : kRowCap + lane)
                                       : (used ? (int32_t)((uint32_t)cc2 * 4u) : 0x7ffffff0);
+                        pin_v(sdst);
                     }
                 },
                 acc0, acc1);
