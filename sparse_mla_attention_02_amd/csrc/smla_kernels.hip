@@ -1436,12 +1436,30 @@ __global__ __launch_bounds__(256, 1) void smla_wide_kernel(KernelArgs a) {
             body(Par<0>{}, Par<1>{}, tile, cs0, offa, offb, xb0, xb1, xa0, xa1);
             body(Par<1>{}, Par<1>{}, tile + 1, cs1, offb, offa, xa0, xa1, xb0, xb1);
         }
+        // the next row's index list into L2 (one dword per 128-byte line, 8 KB
+        // in one load, into the dummy row), two or three tiles before the row
+        // end loads it into LDS; the key rows keep their place in L2
+        if (!DENSE && more && wave == 0)
+            dma_dword(raw_desc(a.idx + rln * a.K, (uint32_t)a.K * 4u), dummy_lds, 0, voff16 << 3);
         for (; tile < ntiles; tile += 2) {
             const Ctl c0 = ctl_of(Par<0>{}, tile);
             body(Par<0>{}, Par<0>{}, tile, c0, offa, offb, xb0, xb1, xa0, xa1);
             if (tile + 1 >= ntiles) break;
             const Ctl c1 = ctl_of(Par<1>{}, tile + 1);
             body(Par<1>{}, Par<0>{}, tile + 1, c1, offb, offa, xa0, xa1, xb0, xb1);
+        }
+        // Every wave has passed the last tile's barrier, so no operand read of
+        // the last tile's buffer is pending: the rows of the next row's Q that
+        // the last tiles did not load (see the streams in the tile loop) and
+        // its lse are loaded now, before the row is finished and written out.
+        if (more) {
+            if (ntiles >= 2) {
+                stage_q_rows(rln, (ntiles - 1) & 1, 7, kRowsPerWave);
+            } else {
+                stage_q_rows(rln, 0, ntiles == 1 ? 7 : 0, kRowsPerWave);
+                stage_q_rows(rln, 1, 0, kRowsPerWave);
+            }
+            stage_lse(rln);
         }
         // tile ntiles-2's epilogue still lacks its last two elements
         if (ntiles >= 2) {
@@ -1475,19 +1493,11 @@ __global__ __launch_bounds__(256, 1) void smla_wide_kernel(KernelArgs a) {
             write_row(a.out + rc * a.W, rowbuf, a.W, tid, NT);
         }
 
-        // the next row: index list and zeroed output, then the rows of its Q
-        // the last tiles did not load (see the streams in the tile loop) and
-        // its lse; every wave reads its heads back, then buffer 0 takes the
-        // next row's first tile
+        // the next row: index list and zeroed output; once its Q and lse have
+        // landed every wave reads its heads back, then buffer 0 takes the next
+        // row's first tile
         prepare_next();
         if (more) {
-            if (ntiles >= 2) {
-                stage_q_rows(rln, (ntiles - 1) & 1, 7, kRowsPerWave);
-            } else {
-                stage_q_rows(rln, 0, ntiles == 1 ? 7 : 0, kRowsPerWave);
-                stage_q_rows(rln, 1, 0, kRowsPerWave);
-            }
-            stage_lse(rln);
             barrier_after_vmcnt(0);
             read_q_lse();
             lds_barrier();
