@@ -11,7 +11,6 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libsmla.so")
-SOURCES = [os.path.join(CSRC, "smla_host.cpp"), os.path.join(CSRC, "smla_kernels.hip")]
 ARCH = "gfx950"
 
 
@@ -22,31 +21,47 @@ def hipcc() -> str:
     raise RuntimeError("hipcc not found")
 
 
-def command(out: str) -> list:
-    return [hipcc(), f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-shared",
-            # keep the compiler from forming packed fp32 VALU instructions
-            "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
-            # MFMA results in VGPRs: the pipelined kernel's epilogue then reads
-            # its scores without an AGPR-to-VGPR copy per element
-            "-mllvm", "-amdgpu-mfma-vgpr-form",
-            "-Wall", "-Wno-unused-command-line-argument",
-            "-I", INCLUDE, "-I", CSRC, "-x", "hip", *SOURCES, "-o", out]
+COMMON = ["--offload-arch=" + ARCH, "-O3", "-std=c++17", "-fPIC",
+          # keep the compiler from forming packed fp32 VALU instructions
+          "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+          "-Wall", "-Wno-unused-command-line-argument", "-I", INCLUDE, "-I", CSRC]
+KERNELS = os.path.join(CSRC, "smla_kernels.hip")
+HOST = os.path.join(CSRC, "smla_host.cpp")
+
+
+def commands(out: str, tmp: str) -> list:
+    """The compile and link commands: the kernel file twice (the pipelined and
+    general kernels with MFMA results in VGPRs, so that the pipelined kernel's
+    epilogue reads its scores without a copy; the softmax_lse kernel with the
+    compiler's default), the host code once, then one shared library."""
+    main_o = os.path.join(tmp, "kernels.o")
+    lse_o = os.path.join(tmp, "kernels_lse.o")
+    host_o = os.path.join(tmp, "host.o")
+    cc = hipcc()
+    return [
+        [cc, *COMMON, "-mllvm", "-amdgpu-mfma-vgpr-form", "-x", "hip", "-c", KERNELS, "-o", main_o],
+        [cc, *COMMON, "-DSMLA_LSE_TU", "-x", "hip", "-c", KERNELS, "-o", lse_o],
+        [cc, *COMMON, "-x", "hip", "-c", HOST, "-o", host_o],
+        [cc, "--offload-arch=" + ARCH, "-shared", "-fPIC", main_o, lse_o, host_o, "-o", out],
+    ]
 
 
 def build(verbose: bool = False) -> str:
     """Compile every source into ``libsmla.so`` (always recompiles)."""
-    tmp = LIB + ".tmp%d" % os.getpid()
-    cmd = command(tmp)
-    if verbose:
-        print(" ".join(cmd), flush=True)
-    res = subprocess.run(cmd, capture_output=True, text=True)
-    out = "\n".join(l for l in (res.stdout + res.stderr).splitlines()
-                    if "packed-fp32-ops" not in l)
-    if res.returncode != 0:
-        raise RuntimeError("hipcc failed:\n" + out)
-    if verbose and out.strip():
-        print(out, flush=True)
-    os.replace(tmp, LIB)
+    import tempfile
+    out = LIB + ".tmp%d" % os.getpid()
+    with tempfile.TemporaryDirectory(prefix="smla_build_") as tmp:
+        for cmd in commands(out, tmp):
+            if verbose:
+                print(" ".join(cmd), flush=True)
+            res = subprocess.run(cmd, capture_output=True, text=True)
+            msg = "\n".join(l for l in (res.stdout + res.stderr).splitlines()
+                            if "packed-fp32-ops" not in l)
+            if res.returncode != 0:
+                raise RuntimeError("hipcc failed:\n" + msg)
+            if verbose and msg.strip():
+                print(msg, flush=True)
+    os.replace(out, LIB)
     return LIB
 
 
