@@ -872,6 +872,31 @@ __device__ __forceinline__ void dma_row(i32x4_t desc, uint32_t m0, int32_t soff,
         : "s"(m0), "v"(voff), "s"(desc), "s"(soff)
         : "memory", "m0");
 }
+// The loads of one stream in the tile loop go to consecutive LDS rows: the
+// first sets M0 and each load then steps it by `step` in place, so the loads
+// after the first need neither an M0 write nor its wait state (the compiler
+// never writes M0 in the pipelined kernel; these are its only users while a
+// stream runs).
+__device__ __forceinline__ void dma_row_first(i32x4_t desc, uint32_t m0, int32_t soff,
+                                              uint32_t voff, int32_t step) {
+    asm volatile(
+        "s_mov_b32 m0, %0\n\t"
+        "s_nop 0\n\t"
+        "buffer_load_dwordx4 %1, %2, %3 offen lds\n\t"
+        "s_add_u32 m0, m0, %4"
+        :
+        : "s"(m0), "v"(voff), "s"(desc), "s"(soff), "s"(step)
+        : "memory", "m0", "scc");
+}
+__device__ __forceinline__ void dma_row_next(i32x4_t desc, int32_t soff, uint32_t voff,
+                                             int32_t step) {
+    asm volatile(
+        "buffer_load_dwordx4 %0, %1, %2 offen lds\n\t"
+        "s_add_u32 m0, m0, %3"
+        :
+        : "v"(voff), "s"(desc), "s"(soff), "s"(step)
+        : "memory", "m0", "scc");
+}
 // The same with the non-temporal hint, for data read once (Q rows, index
 // lists): the key rows, which are gathered again and again, keep their
 // place in L2.
@@ -973,9 +998,6 @@ __device__ __forceinline__ void wide_tile(const uint4* __restrict__ cur,
     acc1 = f32x16_t{};
     float sum = 0.0f, t = 0.0f, ex = 0.0f;
     int32_t soa[2] = {0, 0}, sob[2] = {0, 0};
-    int32_t ma = m0a, mb = m0b;
-    pin_s(ma);
-    pin_s(mb);
 #pragma unroll
     for (int s = 0; s < kSteps; ++s) {
         // One wave per SIMD issues one instruction per 4 cycles, and the matrix
@@ -1031,16 +1053,14 @@ __device__ __forceinline__ void wide_tile(const uint4* __restrict__ cur,
         if (s == kBarStep) barrier_after_vmcnt(0);
         ring[(s + kLead) & 7] =
             s + kLead < kSteps ? cur[2 * (s + kLead)] : nxt[2 * (s + kLead - kSteps)];
-        if (s >= 1 && s <= 9) {  // stream A: row s + 6 of tile t+1
-            dma_row(desc_a, (uint32_t)ma, soa[(s - 1) & 1], voff);
-            ma += stepa;
-            pin_s(ma);
-        }
-        if (s >= 25) {  // stream B: row s - 25 of tile t+2
-            dma_row(desc_b, (uint32_t)mb, sob[(s - 1) & 1], voff);
-            mb += stepb;
-            pin_s(mb);
-        }
+        if (s == 1)  // stream A: row s + 6 of tile t+1
+            dma_row_first(desc_a, (uint32_t)m0a, soa[0], voff, stepa);
+        else if (s >= 2 && s <= 9)
+            dma_row_next(desc_a, soa[(s - 1) & 1], voff, stepa);
+        if (s == 25)  // stream B: row s - 25 of tile t+2
+            dma_row_first(desc_b, (uint32_t)m0b, sob[0], voff, stepb);
+        else if (s >= 26)
+            dma_row_next(desc_b, sob[(s - 1) & 1], voff, stepb);
         mid2(s);
     }
     __builtin_amdgcn_sched_barrier(0);
