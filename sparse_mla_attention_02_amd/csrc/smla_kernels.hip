@@ -129,6 +129,23 @@ __device__ __forceinline__ int32_t uload(const int32_t* p, int64_t i) {
     return ((cint_ptr)p)[i];
 }
 
+// Marks a loaded register as used here, on every path: the compiler then
+// waits for its load at this point instead of before a later reuse of the
+// register, where the wait would also cover the loads in flight since.
+__device__ __forceinline__ void consume(int32_t v) { asm volatile("" ::"v"(v)); }
+// Keeps a value's computation at this point of the instruction stream (pure
+// arithmetic is otherwise free to move to its first use).
+__device__ __forceinline__ void pin(float& v) { asm volatile("" : "+v"(v)); }
+// The same for an integer kept in a vector register.
+__device__ __forceinline__ void pin_v(int32_t& v) { asm volatile("" : "+v"(v)); }
+// The same for a wave-uniform value kept in a scalar register (the
+// readfirstlane costs nothing where the compiler already knows the value is
+// uniform, and makes it legal where it cannot prove it).
+__device__ __forceinline__ void pin_s(int32_t& v) {
+    v = __builtin_amdgcn_readfirstlane(v);
+    asm volatile("" : "+s"(v));
+}
+
 // Row -> (batch, position) decode, mask limit and entry count.
 // Right-down causal with compression ratio r and residual res: the query at
 // position i of a sequence with s1 queries and s2 compressed keys is at
@@ -562,6 +579,84 @@ __device__ __forceinline__ void kq_tile(const uint4* __restrict__ src, const uin
     }
 }
 
+// One 32-key tile for two blocks of 32 heads (S = K_tile . Q_tile^T, each K
+// operand read feeding both MFMAs), with the previous tile's exact online
+// log-sum-exp update (the arithmetic of lse_update below, in the same
+// order) laid out between the MFMAs. One wave per SIMD issues one
+// instruction per 4 cycles and each MFMA keeps the matrix core busy for 32,
+// so each gap holds about six instructions: steps 0..15 form the masked
+// scaled scores of element s and their running maximum (block 0 in the
+// first gap, block 1 in the second), steps 15..16 the new bases, and steps
+// 16..31 add each element's exp2 to the rescaled sum. Bit
+// 8*(e/4) + e%4 of `used` says whether element e is a used entry.
+template <bool BF16>
+__device__ __forceinline__ void kq_tile_exact2(const uint4* __restrict__ src,
+                                               const uint4 (*qa)[kChunks / 2], int col, int half,
+                                               f32x16_t* acc, const f32x16_t* prev,
+                                               uint32_t used, float c, float* m, float* l) {
+    constexpr float kNegInf = -__builtin_inff();
+    constexpr int kSteps = kChunks / 2;
+    constexpr int kLead = 4;
+    acc[0] = f32x16_t{};
+    acc[1] = f32x16_t{};
+    const uint4* row = src + col * kPitch + half;
+    uint4 ring[kLead];
+#pragma unroll
+    for (int i = 0; i < kLead; ++i) ring[i] = row[2 * i];
+    float x0[16], x1[16], mt0 = kNegInf, mt1 = kNegInf, b0 = 0.0f, b1 = 0.0f, s0 = 0.0f,
+                          s1 = 0.0f, m0n = kNegInf, m1n = kNegInf;
+    bool u = false;
+    auto base_of = [&](float mo, float mt, float lo, float& mn, float& b, float& sum) {
+        mn = __builtin_fmaxf(mo, mt);
+        b = mn == kNegInf ? 0.0f : mn;  // nothing used yet: every term is 0
+        sum = lo * __builtin_amdgcn_exp2f(mo - b);
+    };
+#pragma unroll
+    for (int st = 0; st < kSteps; ++st) {
+        __builtin_amdgcn_sched_barrier(0);
+        acc[0] = mfma_32x32x16<BF16>(ring[st % kLead], qa[0][st], acc[0]);
+        asm volatile("" ::"a"(acc[0]));
+        if (st < 16) {
+            const int e = st;
+            u = (used >> (8 * (e >> 2) + (e & 3))) & 1u;
+            x0[e] = u ? prev[0][e] * c : kNegInf;
+            mt0 = __builtin_fmaxf(mt0, x0[e]);
+            pin(mt0);
+        } else {
+            s0 += __builtin_amdgcn_exp2f(x0[st - 16] - b0);
+            pin(s0);
+        }
+        if (st == 16) {
+            base_of(m[1], mt1, l[1], m1n, b1, s1);
+            pin(s1);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+        acc[1] = mfma_32x32x16<BF16>(ring[st % kLead], qa[1][st], acc[1]);
+        asm volatile("" ::"a"(acc[1]));
+        if (st + kLead < kSteps) ring[st % kLead] = row[2 * (st + kLead)];
+        if (st < 16) {
+            const int e = st;
+            x1[e] = u ? prev[1][e] * c : kNegInf;
+            mt1 = __builtin_fmaxf(mt1, x1[e]);
+            pin(mt1);
+        }
+        if (st == 15) {
+            base_of(m[0], mt0, l[0], m0n, b0, s0);
+            pin(s0);
+        }
+        if (st >= 17) {
+            s1 += __builtin_amdgcn_exp2f(x1[st - 17] - b1);
+            pin(s1);
+        }
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    s1 += __builtin_amdgcn_exp2f(x1[15] - b1);
+    m[0] = m0n;
+    l[0] = s0;
+    m[1] = m1n;
+    l[1] = s1;
+}
+
 // Online update of one lane's (m, l) -- base-2 running maximum and sum of
 // 2^(x - m) -- with its 16 scores of a tile, x = acc * c. Bit
 // 8*(e/4) + e%4 of `used` says whether element e is a used entry.
@@ -743,8 +838,13 @@ __global__ __launch_bounds__(64 * WAVES, 2) void smla_lse_kernel(KernelArgs a) {
             // slot kk of the tile is used: bit kk (lanes kk and kk + 32 agree)
             const uint32_t mask =
                 (uint32_t)__builtin_amdgcn_ballot_w64(used(tile, col, key_cur));
-            kq_tile<BF16, NB>(cur, qa, col, half, acc, epilogue);
-            settle();
+            if constexpr (NB == 2) {
+                kq_tile_exact2<BF16>(cur, qa, col, half, acc, acc_prev, slots_prev >> (4 * half),
+                                     a.c_scale, m, l);
+            } else {
+                kq_tile<BF16, NB>(cur, qa, col, half, acc, epilogue);
+                settle();
+            }
 #pragma unroll
             for (int nb = 0; nb < NB; ++nb) acc_prev[nb] = acc[nb];
             slots_prev = mask;
@@ -823,23 +923,6 @@ __device__ __forceinline__ void barrier_after_vmcnt(int n) {
 __device__ __forceinline__ void lds_barrier() {
     waitcnt_vm_lgkm0<63>();
     asm volatile("s_barrier" ::: "memory");
-}
-
-// Marks a loaded register as used here, on every path: the compiler then
-// waits for its load at this point instead of before a later reuse of the
-// register, where the wait would also cover the loads in flight since.
-__device__ __forceinline__ void consume(int32_t v) { asm volatile("" ::"v"(v)); }
-// Keeps a value's computation at this point of the instruction stream (pure
-// arithmetic is otherwise free to move to its first use).
-__device__ __forceinline__ void pin(float& v) { asm volatile("" : "+v"(v)); }
-// The same for an integer kept in a vector register.
-__device__ __forceinline__ void pin_v(int32_t& v) { asm volatile("" : "+v"(v)); }
-// The same for a wave-uniform value kept in a scalar register (the
-// readfirstlane costs nothing where the compiler already knows the value is
-// uniform, and makes it legal where it cannot prove it).
-__device__ __forceinline__ void pin_s(int32_t& v) {
-    v = __builtin_amdgcn_readfirstlane(v);
-    asm volatile("" : "+s"(v));
 }
 
 // Buffer descriptor as four dwords (base, range in bytes, gfx9 untyped
