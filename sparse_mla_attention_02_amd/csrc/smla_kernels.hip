@@ -589,11 +589,14 @@ __device__ __forceinline__ void kq_tile(const uint4* __restrict__ src, const uin
 // first gap, block 1 in the second), steps 15..16 the new bases, and steps
 // 16..31 add each element's exp2 to the rescaled sum. Bit
 // 8*(e/4) + e%4 of `used` says whether element e is a used entry.
-template <bool BF16>
+// `gstep(i)`, called in the second gap of steps 0..15, issues the next
+// tile's gather loads one at a time.
+template <bool BF16, typename GStep>
 __device__ __forceinline__ void kq_tile_exact2(const uint4* __restrict__ src,
                                                const uint4 (*qa)[kChunks / 2], int col, int half,
                                                f32x16_t* acc, const f32x16_t* prev,
-                                               uint32_t used, float c, float* m, float* l) {
+                                               uint32_t used, float c, float* m, float* l,
+                                               GStep&& gstep) {
     constexpr float kNegInf = -__builtin_inff();
     constexpr int kSteps = kChunks / 2;
     constexpr int kLead = 4;
@@ -634,6 +637,7 @@ __device__ __forceinline__ void kq_tile_exact2(const uint4* __restrict__ src,
         acc[1] = mfma_32x32x16<BF16>(ring[st % kLead], qa[1][st], acc[1]);
         asm volatile("" ::"a"(acc[1]));
         if (st + kLead < kSteps) ring[st % kLead] = row[2 * (st + kLead)];
+        if (st < 16) gstep(st);
         if (st < 16) {
             const int e = st;
             x1[e] = u ? prev[1][e] * c : kNegInf;
@@ -833,14 +837,24 @@ __global__ __launch_bounds__(64 * WAVES, 2) void smla_lse_kernel(KernelArgs a) {
             // gathers of this tile landed; every wave is done reading `nxt`
             __builtin_amdgcn_s_waitcnt(0);
             __syncthreads();
-            if (tile + 1 < ntiles) gather(nxt, tile + 1, key_nxt);
+            if (NB != 2 && tile + 1 < ntiles) gather(nxt, tile + 1, key_nxt);
             const int32_t key_nn = tile_idx(tile + 2);
             // slot kk of the tile is used: bit kk (lanes kk and kk + 32 agree)
             const uint32_t mask =
                 (uint32_t)__builtin_amdgcn_ballot_w64(used(tile, col, key_cur));
             if constexpr (NB == 2) {
-                kq_tile_exact2<BF16>(cur, qa, col, half, acc, acc_prev, slots_prev >> (4 * half),
-                                     a.c_scale, m, l);
+                // the next tile's rows (row 0 where it has none: the buffer is
+                // then not read again, and each slot is always loaded by the
+                // same wave, in order) are gathered one per step
+                const int32_t rows = used(tile + 1, col, key_nxt) ? key_nxt : 0;
+                kq_tile_exact2<BF16>(
+                    cur, qa, col, half, acc, acc_prev, slots_prev >> (4 * half), a.c_scale, m, l,
+                    [&](int i) {
+                        const int kk = wave + i * WAVES;
+                        const int32_t j = __builtin_amdgcn_readlane(rows, kk);
+                        __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                            krs, SMLA_LDS(nxt + kk * kPitch), 16, lane << 4, j << 10, 0, 0);
+                    });
             } else {
                 kq_tile<BF16, NB>(cur, qa, col, half, acc, epilogue);
                 settle();
@@ -885,6 +899,9 @@ __global__ __launch_bounds__(64 * WAVES, 2) void smla_lse_kernel(KernelArgs a) {
         // every wave is done with kbuf0 before the next row gathers into it
         __syncthreads();
     }
+    // loads into LDS (the last tile's gathers of row 0) must land before the
+    // workgroup's LDS is released
+    __builtin_amdgcn_s_waitcnt(0);
 }
 
 #endif  // SMLA_LSE_TU
