@@ -556,9 +556,12 @@ __global__ __launch_bounds__(64 * HT, 2) void smla_l1norm_kernel(KernelArgs a) {
 // One 32-key tile, S = K_tile . Q_tile^T for this wave's NB blocks of 32
 // heads (each K operand read feeds NB MFMAs), with the previous tile's
 // epilogue `epi` scheduled between the MFMAs.
-template <bool BF16, int NB, typename Epi>
+// `gstep(i)`, called after the MFMAs of step i (the gathers of the next
+// tile, at most one load each), keeps its place by a scheduling barrier.
+template <bool BF16, int NB, typename Epi, typename GStep>
 __device__ __forceinline__ void kq_tile(const uint4* __restrict__ src, const uint4 (*qa)[kChunks / 2],
-                                        int col, int half, f32x16_t* acc, Epi&& epi) {
+                                        int col, int half, f32x16_t* acc, Epi&& epi,
+                                        GStep&& gstep) {
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb) acc[nb] = f32x16_t{};
     const uint4* row = src + col * kPitch + half;
@@ -567,6 +570,7 @@ __device__ __forceinline__ void kq_tile(const uint4* __restrict__ src, const uin
         const uint4 b = row[2 * s];
 #pragma unroll
         for (int nb = 0; nb < NB; ++nb) acc[nb] = mfma_32x32x16<BF16>(b, qa[nb][s], acc[nb]);
+        gstep(s);
     }
     epi();
     constexpr int kLead = 4;
@@ -575,6 +579,7 @@ __device__ __forceinline__ void kq_tile(const uint4* __restrict__ src, const uin
     for (int s = 0; s < kChunks / 2; ++s) {
         __builtin_amdgcn_sched_group_barrier(0x008, NB, 0);
         if (s < kChunks / 2 - kLead) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
         __builtin_amdgcn_sched_group_barrier(0x002, 3 * NB, 0);
     }
 }
@@ -837,26 +842,27 @@ __global__ __launch_bounds__(64 * WAVES, 2) void smla_lse_kernel(KernelArgs a) {
             // gathers of this tile landed; every wave is done reading `nxt`
             __builtin_amdgcn_s_waitcnt(0);
             __syncthreads();
-            if (NB != 2 && tile + 1 < ntiles) gather(nxt, tile + 1, key_nxt);
             const int32_t key_nn = tile_idx(tile + 2);
             // slot kk of the tile is used: bit kk (lanes kk and kk + 32 agree)
             const uint32_t mask =
                 (uint32_t)__builtin_amdgcn_ballot_w64(used(tile, col, key_cur));
+            // the next tile's rows (row 0 where it has none: the buffer is
+            // then not read again, and each slot is always loaded by the same
+            // wave, in order) are gathered one per step, 32 / WAVES of them
+            const int32_t rows = used(tile + 1, col, key_nxt) ? key_nxt : 0;
+            auto gstep = [&](int i) {
+                if (i < kTile / WAVES) {
+                    const int kk = wave + i * WAVES;
+                    const int32_t j = __builtin_amdgcn_readlane(rows, kk);
+                    __builtin_amdgcn_raw_ptr_buffer_load_lds(krs, SMLA_LDS(nxt + kk * kPitch), 16,
+                                                             lane << 4, j << 10, 0, 0);
+                }
+            };
             if constexpr (NB == 2) {
-                // the next tile's rows (row 0 where it has none: the buffer is
-                // then not read again, and each slot is always loaded by the
-                // same wave, in order) are gathered one per step
-                const int32_t rows = used(tile + 1, col, key_nxt) ? key_nxt : 0;
-                kq_tile_exact2<BF16>(
-                    cur, qa, col, half, acc, acc_prev, slots_prev >> (4 * half), a.c_scale, m, l,
-                    [&](int i) {
-                        const int kk = wave + i * WAVES;
-                        const int32_t j = __builtin_amdgcn_readlane(rows, kk);
-                        __builtin_amdgcn_raw_ptr_buffer_load_lds(
-                            krs, SMLA_LDS(nxt + kk * kPitch), 16, lane << 4, j << 10, 0, 0);
-                    });
+                kq_tile_exact2<BF16>(cur, qa, col, half, acc, acc_prev, slots_prev >> (4 * half),
+                                     a.c_scale, m, l, gstep);
             } else {
-                kq_tile<BF16, NB>(cur, qa, col, half, acc, epilogue);
+                kq_tile<BF16, NB>(cur, qa, col, half, acc, epilogue, gstep);
                 settle();
             }
 #pragma unroll
