@@ -146,6 +146,13 @@ __device__ __forceinline__ void pin_s(int32_t& v) {
     asm volatile("" : "+s"(v));
 }
 
+// A compile-time integer (a tile parity, tile & 1, so that the buffer
+// addresses of a tile fold into constants; or a flag).
+template <int P>
+struct Par {
+    static constexpr int value = P;
+};
+
 // Row -> (batch, position) decode, mask limit and entry count.
 // Right-down causal with compression ratio r and residual res: the query at
 // position i of a sequence with s1 queries and s2 compressed keys is at
@@ -450,17 +457,19 @@ __global__ __launch_bounds__(64 * HT, 2) void smla_l1norm_kernel(KernelArgs a) {
         int32_t key_p1 = -1, key_p2 = -1;  // raw indices of tiles t-1 and t-2
         // One tile: finish tile-2's head sum, gather tile+1, QK^T of this
         // tile with tile-1's epilogue.
-        auto body = [&](int tile, const uint4* cur, uint4* nxt) {
+        // A tile with a next tile (GATHER) issues that tile's rows between its
+        // MFMAs; the last tile of a row gathers nothing (kbuf0 is the row
+        // stage at the end of the row, so no load may land there late).
+        auto body = [&](auto GATHER, int tile, const uint4* cur, uint4* nxt) {
             // gathers of this tile landed, partial sums of tile-1 visible
             __builtin_amdgcn_s_waitcnt(0);
             __syncthreads();
             reduce(tile - 2, key_p2);
-            if (tile + 1 < ntiles) gather(nxt, tile + 1, key_nxt);
             const int32_t key_nn = tile_idx(tile + 2);
             float sum_prev;
-            const f32x16_t acc = qk_tile<BF16, false, HT>(cur, qa, col, half, acc_prev, l2,
-                                                          a.c_scale, &sum_prev, nullptr, krs, 0,
-                                                          wave, lane);
+            const f32x16_t acc = qk_tile<BF16, decltype(GATHER)::value != 0, HT>(
+                cur, qa, col, half, acc_prev, l2, a.c_scale, &sum_prev, nxt, krs,
+                decltype(GATHER)::value ? gather_row(tile + 1, key_nxt) : 0, wave, lane);
             red[(tile - 1) & 1][2 * wave + half][col] = sum_prev;  // tile 0: unused slot
             acc_prev = acc;
             key_p2 = key_p1;
@@ -468,9 +477,16 @@ __global__ __launch_bounds__(64 * HT, 2) void smla_l1norm_kernel(KernelArgs a) {
             key_cur = key_nxt;
             key_nxt = key_nn;
         };
-        for (int tile = 0; tile < ntiles; tile += 2) {
-            body(tile, kbuf0, kbuf1);
-            if (tile + 1 < ntiles) body(tile + 1, kbuf1, kbuf0);
+        int tile = 0;
+        for (; tile + 2 < ntiles; tile += 2) {
+            body(Par<1>{}, tile, kbuf0, kbuf1);
+            body(Par<1>{}, tile + 1, kbuf1, kbuf0);
+        }
+        if (tile + 1 < ntiles) {
+            body(Par<1>{}, tile, kbuf0, kbuf1);
+            body(Par<0>{}, tile + 1, kbuf1, kbuf0);
+        } else if (tile < ntiles) {
+            body(Par<0>{}, tile, kbuf0, kbuf1);
         }
         if (ntiles > 0)
             red[(ntiles - 1) & 1][2 * wave + half][col] = head_sum(acc_prev, l2, a.c_scale);
@@ -1176,12 +1192,6 @@ __device__ __forceinline__ void wide_tile(const uint4* __restrict__ cur,
     psum = sum;
 }
 
-// A compile-time tile parity (tile & 1), so that the buffer addresses of a
-// tile fold into constants.
-template <int P>
-struct Par {
-    static constexpr int value = P;
-};
 
 // ROWBUF (output rows of at most kRowCap columns): each row is assembled in
 // LDS (zeroed at the row start, values written as they are finished) and
