@@ -288,12 +288,31 @@ __device__ __forceinline__ f32x16_t qk_tile(const uint4* __restrict__ src, const
                                             int wave, int lane) {
     constexpr int kSlots = kTile / HT;                 // rows this wave gathers
     constexpr int kGap = kSlots >= 16 ? 1 : 16 / kSlots;  // MFMAs between gathers
+    constexpr int kSteps = kChunks / 2;
+    // Laid out step by step (one wave per SIMD issues one instruction per 4
+    // cycles, and the MFMA keeps the matrix core busy for 32): each step
+    // holds its MFMA, the operand read LEAD steps ahead, half an element of
+    // the previous tile's epilogue (the fma in even steps, the exp and the
+    // add in odd ones) and at most one gather load.
     f32x16_t acc = {};
     const uint4* row = src + col * kPitch + half;
+    uint4 ring[LEAD];
 #pragma unroll
-    for (int s = 0; s < kChunks / 2; ++s) {
-        const uint4 b = row[2 * s];
-        acc = mfma_32x32x16<BF16>(qa[s], b, acc);
+    for (int i = 0; i < LEAD; ++i) ring[i] = row[2 * i];
+    float sum = 0.0f, t = 0.0f;
+#pragma unroll
+    for (int s = 0; s < kSteps; ++s) {
+        __builtin_amdgcn_sched_barrier(0);
+        acc = mfma_32x32x16<BF16>(qa[s], ring[s % LEAD], acc);
+        asm volatile("" ::"v"(acc));
+        if (s + LEAD < kSteps) ring[s % LEAD] = row[2 * (s + LEAD)];
+        if ((s & 1) == 0) {
+            t = __builtin_fmaf(prev[s >> 1], c, -l2[s >> 1]);
+            pin(t);
+        } else {
+            sum += __builtin_amdgcn_exp2f(t);
+            pin(sum);
+        }
         if constexpr (GATHER) {
             if (s % kGap == 0 && s / kGap < kSlots) {
                 const int kk = wave + (s / kGap) * HT;
@@ -303,19 +322,8 @@ __device__ __forceinline__ f32x16_t qk_tile(const uint4* __restrict__ src, const
             }
         }
     }
-    *prev_sum = head_sum(prev, l2, c);
-    // kLead operand reads ahead of the MFMAs; between MFMAs one read, two
-    // VALU instructions of the previous tile's epilogue, and the gathers
-    constexpr int kLead = LEAD;
-    __builtin_amdgcn_sched_group_barrier(0x100, kLead, 0);
-#pragma unroll
-    for (int s = 0; s < kChunks / 2; ++s) {
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-        if (s < kChunks / 2 - kLead) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-        __builtin_amdgcn_sched_group_barrier(0x002, 2, 0);
-        if (GATHER && s % kGap == 0 && s / kGap < kSlots)
-            __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
-    }
+    __builtin_amdgcn_sched_barrier(0);
+    *prev_sum = sum;
     return acc;
 }
 
