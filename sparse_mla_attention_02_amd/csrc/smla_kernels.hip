@@ -577,36 +577,6 @@ __global__ __launch_bounds__(64 * HT, 2) void smla_l1norm_kernel(KernelArgs a) {
 // online maximum and rescaled sum (base 2); the two half-waves of a head
 // meet once at the end of the row.
 
-// One 32-key tile, S = K_tile . Q_tile^T for this wave's NB blocks of 32
-// heads (each K operand read feeds NB MFMAs), with the previous tile's
-// epilogue `epi` scheduled between the MFMAs.
-// `gstep(i)`, called after the MFMAs of step i (the gathers of the next
-// tile, at most one load each), keeps its place by a scheduling barrier.
-template <bool BF16, int NB, typename Epi, typename GStep>
-__device__ __forceinline__ void kq_tile(const uint4* __restrict__ src, const uint4 (*qa)[kChunks / 2],
-                                        int col, int half, f32x16_t* acc, Epi&& epi,
-                                        GStep&& gstep) {
-#pragma unroll
-    for (int nb = 0; nb < NB; ++nb) acc[nb] = f32x16_t{};
-    const uint4* row = src + col * kPitch + half;
-#pragma unroll
-    for (int s = 0; s < kChunks / 2; ++s) {
-        const uint4 b = row[2 * s];
-#pragma unroll
-        for (int nb = 0; nb < NB; ++nb) acc[nb] = mfma_32x32x16<BF16>(b, qa[nb][s], acc[nb]);
-        gstep(s);
-    }
-    epi();
-    constexpr int kLead = 4;
-    __builtin_amdgcn_sched_group_barrier(0x100, kLead, 0);
-#pragma unroll
-    for (int s = 0; s < kChunks / 2; ++s) {
-        __builtin_amdgcn_sched_group_barrier(0x008, NB, 0);
-        if (s < kChunks / 2 - kLead) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-        __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
-        __builtin_amdgcn_sched_group_barrier(0x002, 3 * NB, 0);
-    }
-}
 
 // One 32-key tile for two blocks of 32 heads (S = K_tile . Q_tile^T, each K
 // operand read feeding both MFMAs), with the previous tile's exact online
@@ -752,6 +722,48 @@ __device__ __forceinline__ void lse_lazy(const f32x16_t& acc, uint32_t slots, fl
     }
 }
 
+// One 32-key tile for one block of 32 heads with the previous tile's lazy
+// step (lse_lazy, same arithmetic and order) laid out step by step: each
+// step holds its MFMA, the operand read four steps ahead, half an element of
+// the lazy step (the masked shifted score in even steps, the maximum, the
+// exp2 and the sum in odd ones) and `gstep(s)`, at most one gather load.
+template <bool BF16, typename GStep>
+__device__ __forceinline__ void kq_tile_lazy(const uint4* __restrict__ src, const uint4* qa,
+                                             int col, int half, f32x16_t& acc,
+                                             const f32x16_t& prev, uint32_t slots, float c,
+                                             float b, float& ymax, float& sum, GStep&& gstep) {
+    constexpr int kSteps = kChunks / 2;
+    constexpr int kLead = 4;
+    acc = f32x16_t{};
+    const uint4* row = src + col * kPitch + half;
+    uint4 ring[kLead];
+#pragma unroll
+    for (int i = 0; i < kLead; ++i) ring[i] = row[2 * i];
+    const float nb = -b;
+    float y = 0.0f;
+    ymax = -__builtin_inff();
+    sum = 0.0f;
+#pragma unroll
+    for (int s = 0; s < kSteps; ++s) {
+        __builtin_amdgcn_sched_barrier(0);
+        acc = mfma_32x32x16<BF16>(ring[s % kLead], qa[s], acc);
+        asm volatile("" ::"a"(acc));
+        if (s + kLead < kSteps) ring[s % kLead] = row[2 * (s + kLead)];
+        const int e = s >> 1;
+        if ((s & 1) == 0) {
+            y = select_lanes(used_lanes(slots, e), __builtin_fmaf(prev[e], c, nb),
+                             -__builtin_inff());
+            pin(y);
+        } else {
+            ymax = __builtin_fmaxf(ymax, y);
+            sum += __builtin_amdgcn_exp2f(y);
+            pin(sum);
+        }
+        gstep(s);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+}
+
 // WAVES waves per workgroup, each with NB blocks of 32 heads (1 x 1 for up
 // to 32 heads, 2 x 1 for up to 64, 2 x 2 for up to 128). One wave per SIMD
 // at two workgroups per CU, so each wave has the whole register file: Q
@@ -885,8 +897,9 @@ __global__ __launch_bounds__(64 * WAVES, 2) void smla_lse_kernel(KernelArgs a) {
             if constexpr (NB == 2) {
                 kq_tile_exact2<BF16>(cur, qa, col, half, acc, acc_prev, slots_prev >> (4 * half),
                                      a.c_scale, m, l, gstep);
-            } else {
-                kq_tile<BF16, NB>(cur, qa, col, half, acc, epilogue, gstep);
+            } else if constexpr (NB == 1) {
+                kq_tile_lazy<BF16>(cur, qa[0], col, half, acc[0], acc_prev[0], slots_prev,
+                                   a.c_scale, m[0], ymax[0], lsum[0], gstep);
                 settle();
             }
 #pragma unroll
