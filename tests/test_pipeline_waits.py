@@ -15,9 +15,12 @@ of random tile counts, in the kernel's order:
     for everything and the barrier (after which the operands of tile t+1
     are read); steps 25..31: rows 0..6 of tile t+2 (stream B), then the
     value store of the step sequence;
-  * row end: the value stores of the last two tiles, the zero-fill of the
-    next row's output, its index list (8), the rest of its Q and lse (1), a
-    wait for everything, then the next row's start.
+  * before the last two or three tiles of a row (where the steady tiles
+    end): an L2 prefetch of the next row's index list (1 load);
+  * row end: as the tile loop ends, the rest of the next row's Q (32 in the
+    model) and its lse (1); then the value stores of the last two tiles, the
+    zero-fill of the next row's output, its index list (8), a wait for
+    everything, then the next row's start.
 
 With rows assembled in LDS (output rows of at most 4096 columns) the values
 go to LDS instead: no store in the tile loop and no zero-fill; the row end
@@ -84,13 +87,24 @@ def replay(rows, switch, rng, row_start_later=ROW_START_LATER, bar_later=0, rowb
         more = r + 1 < len(rows)
         assert landed(("index list", r)), (rows, r)
         assert rowbuf or landed(("zero fill", r)), (rows, r)
+        # the steady pairs run while tile + 3 < nt; the rest form the tail
+        tail = 0
+        while tail + 3 < nt:
+            tail += 2
         for t in range(nt):
+            if t == tail and more:
+                issue(("prefetch", r + 1))
             gather(r, t + 1, 7, 16, nt)                  # steps 1..9
             wait(bar_later)                              # step 24
             assert landed(("gather", r, t + 1)), (rows, r, t)
             gather(r, t + 2, 0, 7, nt)                   # steps 25..31
             if not rowbuf:
                 issue(("store", r))                      # step 31
+        if nt == 0 and more:
+            issue(("prefetch", r + 1))
+        if more:
+            issue(("q", r + 1), 32)
+            issue(("lse", r + 1))
         if rowbuf:
             issue(("row", r), rng.randint(1, 4))
         else:
@@ -99,9 +113,8 @@ def replay(rows, switch, rng, row_start_later=ROW_START_LATER, bar_later=0, rowb
                 issue(("zero fill", r + 1), rng.randint(0, 12))
         issue(("index list", r + 1), IDX_OPS)
         if more:
-            issue(("q", r + 1), 32)
-            issue(("lse", r + 1))
             wait(0)
+            assert landed(("q", r + 1)) and landed(("lse", r + 1)), (rows, r)
             row_start(r + 1)
 
 
