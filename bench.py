@@ -15,9 +15,17 @@ workload; its duration is measured with HIP events on the stream the kernel
 is launched on. ``cpu_baseline`` times the CPU oracle (the test checker, as
 it stands) on a bounded sample of the same workload's rows.
 
-softmax_lse: timing runs use a stand-in of the right shape and magnitude
-(log n + D*scale^2/2 per row), not the oracle's exact values; the work done
-does not depend on the values.
+softmax_lse: computed on the GPU by the library's own lse call
+(smla_softmax_lse) before the timed region, so the timed main call runs on
+real inputs and its output is a proper distribution per row.
+
+The line checks itself: after timing, the timed output is compared with the
+CPU oracle (fed the same lse) on the rows the CPU baseline evaluates, every
+row's sum is checked against 1, and the GPU lse against the oracle's lse on
+a row sample; ``parity`` reports the result and a mismatch makes the run
+exit with status 1. ``kernel_ms`` is the median of the per-launch HIP event
+times; ``clock_mhz`` is the GPU's graphics clock sampled with amdsmi during
+the timed region (null where amdsmi cannot read it).
 """
 
 from __future__ import annotations
@@ -27,6 +35,7 @@ import hashlib
 import json
 import os
 import sys
+import threading
 import time
 
 import numpy as np
@@ -84,21 +93,26 @@ def measured_traffic(kernel, workload):
         return None
 
 
-def cpu_baseline(p, target_s, op="l1norm"):
+def cpu_baseline(p, target_s, op="l1norm", timed=True):
     """Time the CPU oracle (oracle_l1norm given lse, or oracle_lse) on evenly
-    spaced rows of the workload."""
+    spaced rows of the workload. Returns (baseline dict or None, rows, the
+    oracle's outputs on those rows); with ``timed`` False only a small sample
+    is evaluated, for the parity check."""
     import oracle
     R = p.rows
     n = p.row_entries.reshape(R).astype(np.int64)
-    # calibrate on a few rows per thread, then size the sample for ~target_s
     threads = oracle.num_threads()
-    cal = np.linspace(0, R - 1, min(R, 4 * threads)).astype(np.int64)
+
     def run(rows):
         if op == "lse":
-            oracle.lse(p, rows=rows)
-        else:
-            oracle.l1norm(p, rows=rows)
+            return oracle.lse(p, rows=rows)[0]
+        return oracle.l1norm(p, rows=rows)
 
+    if not timed:
+        rows = np.unique(np.linspace(0, R - 1, min(R, 2 * threads)).astype(np.int64))
+        return None, rows, run(rows)
+    # calibrate on a few rows per thread, then size the sample for ~target_s
+    cal = np.linspace(0, R - 1, min(R, 4 * threads)).astype(np.int64)
     run(cal[:threads])       # warm the thread pool
     t0 = time.perf_counter()
     run(cal)
@@ -109,15 +123,130 @@ def cpu_baseline(p, target_s, op="l1norm"):
     rows = np.linspace(0, R - 1, count).astype(np.int64)
     log(f"cpu baseline: oracle on {count} rows (~{count * n.mean() * per_pair:.1f} s)")
     t0 = time.perf_counter()
-    run(rows)
+    out = run(rows)
     t = time.perf_counter() - t0
     pairs = int(n[rows].sum())
     flops = 2.0 * p.heads_q * p.head_dim * pairs
-    return {"value": flops / t / 1e12, "unit": "TFLOP/s", "cores": threads,
-            "kind": "oracle",
+    base = {"value": flops / t / 1e12, "unit": "TFLOP/s", "cores": threads,
+            "kind": "oracle", "cpu_model": cpu_model(),
             "sample": f"{count} evenly spaced rows of {R} ({pairs} valid pairs), "
                       + ("oracle_lse" if op == "lse" else "oracle_l1norm given lse")
                       + f", {t:.1f} s wall"}
+    return base, rows, out
+
+
+def cpu_model():
+    """The host CPU's model name (from /proc/cpuinfo), or None."""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
+
+
+class ClockSampler:
+    """Samples the GPU's graphics clock (MHz) with amdsmi from a thread while
+    the timed region runs. Every failure leaves the figures null: the clock
+    is reported, never required."""
+
+    def __init__(self, torch, dev_index=0, period_s=0.005):
+        self.samples = []
+        self.error = None
+        self.period = period_s
+        self._stop = threading.Event()
+        self._thread = None
+        self._smi = None
+        self._h = None
+        try:
+            import amdsmi
+            amdsmi.amdsmi_init()
+            props = torch.cuda.get_device_properties(dev_index)
+            want = (int(getattr(props, "pci_domain_id", 0)), int(props.pci_bus_id),
+                    int(getattr(props, "pci_device_id", 0)))
+            handles = amdsmi.amdsmi_get_processor_handles()
+            for h in handles:
+                bdf = amdsmi.amdsmi_get_gpu_device_bdf(h)      # "dddd:bb:dd.f"
+                dom, bus, rest = bdf.split(":")
+                if (int(dom, 16), int(bus, 16), int(rest.split(".")[0], 16)) == want:
+                    self._h = h
+            if self._h is None and len(handles) == 1:
+                self._h = handles[0]
+            if self._h is None:
+                raise RuntimeError("no amdsmi handle matches the device's PCI address")
+            self._smi = amdsmi
+            self._read()
+        except Exception as e:  # noqa: BLE001 (reporting only)
+            self.error = f"{type(e).__name__}: {e}"
+            self._smi = None
+
+    def _read(self):
+        info = self._smi.amdsmi_get_clock_info(self._h, self._smi.AmdSmiClkType.GFX)
+        return float(info["clk"])
+
+    def _loop(self):
+        while not self._stop.is_set():
+            try:
+                self.samples.append(self._read())
+            except Exception as e:  # noqa: BLE001
+                self.error = f"{type(e).__name__}: {e}"
+                return
+            self._stop.wait(self.period)
+
+    def __enter__(self):
+        if self._smi is not None:
+            self._thread = threading.Thread(target=self._loop, daemon=True)
+            self._thread.start()
+        return self
+
+    def __exit__(self, *exc):
+        self._stop.set()
+        if self._thread is not None:
+            self._thread.join()
+
+    def summary(self):
+        if not self.samples:
+            return {"median": None, "min": None, "max": None, "samples": 0,
+                    "source": "amdsmi gfx clock", "error": self.error}
+        a = np.array(self.samples)
+        return {"median": float(np.median(a)), "min": float(a.min()), "max": float(a.max()),
+                "samples": int(a.size), "source": "amdsmi gfx clock"}
+
+
+TOL = 2e-5          # per element, and per lse value
+ROWSUM_TOL = 1e-4   # per row with a used entry
+
+
+def parity_check(p, op, out_rows, lse_rows, rows, expect, lse_sample):
+    """The timed output against the oracle. ``out_rows``: (R, W) output (main
+    call) or (R, G) lse (lse call) as numpy; ``expect``: the oracle on
+    ``rows``; ``lse_sample``: (rows, oracle lse) for the main call's lse."""
+    res = {"rows_checked": int(len(rows))}
+    err = np.abs(out_rows[rows].astype(np.float64) - expect.astype(np.float64))
+    if op == "lse":
+        dead = np.isneginf(expect)
+        ok_inf = bool(np.array_equal(np.isneginf(out_rows[rows]), dead))
+        e = err[~dead]
+        res["max_abs_err"] = float(e.max()) if e.size else 0.0
+        res["ok"] = ok_inf and res["max_abs_err"] <= TOL
+        return res
+    res["max_abs_err"] = float(err.max()) if err.size else 0.0
+    live = p.row_entries.reshape(p.rows) > 0
+    sums = out_rows.astype(np.float64).sum(axis=1)
+    res["max_rowsum_dev"] = float(np.abs(sums[live] - 1.0).max()) if live.any() else 0.0
+    res["empty_rows_zero"] = bool(not out_rows[~live].any())
+    lrows, lwant = lse_sample
+    got = lse_rows[lrows]
+    dead = np.isneginf(lwant)
+    lerr = np.abs(got[~dead].astype(np.float64) - lwant[~dead].astype(np.float64))
+    res["lse_rows_checked"] = int(len(lrows))
+    res["lse_max_abs_err"] = float(lerr.max()) if lerr.size else 0.0
+    res["ok"] = bool(res["max_abs_err"] <= TOL and res["max_rowsum_dev"] <= ROWSUM_TOL
+                     and res["empty_rows_zero"] and res["lse_max_abs_err"] <= TOL
+                     and np.array_equal(np.isneginf(got), dead))
+    return res
 
 
 def main():
@@ -174,14 +303,11 @@ def main():
     p = workloads.generate(args.workload)
     p.kwide = args.kwide and args.op == "l1norm"
     flops, nbytes, pairs = algorithmic(p, args.op)
-    lse = workloads.lse_standin(p)
-    p.softmax_lse = lse
 
     def t(a):
         return None if a is None else torch.from_numpy(np.ascontiguousarray(a)).to(dev)
 
     q, k = p.q.to(dev), p.k.to(dev)
-    lse_d = t(lse)
     idx, tlen = t(p.sparse_indices), t(p.topk_length)
     cu_q, cu_k, res = t(p.cu_seqlens_q), t(p.cu_seqlens_k), t(p.cmp_residual_k)
     cu_q_h = None if p.cu_seqlens_q is None else torch.from_numpy(p.cu_seqlens_q)
@@ -192,17 +318,31 @@ def main():
         out = torch.empty(p.out_shape(), dtype=torch.float32, device=dev)
     stream = torch.cuda.current_stream(dev)
 
-    def step(before=None, after=None):
-        md = smla.smla_l1norm_metadata(
+    def metadata():
+        return smla.smla_l1norm_metadata(
             p.heads_q, p.heads_k, p.head_dim, cu_seqlens_q=cu_q_h, cu_seqlens_k=cu_k_h,
             batch_size=p.batch, max_seqlen_q=p.max_seqlen_q, max_seqlen_k=p.max_seqlen_k,
             topk=p.topk, layout_q=p.layout, layout_k=p.layout, mask_mode=p.mask_mode,
             cmp_ratio=p.cmp_ratio, device=0)
-        kw = dict(sparse_indices=idx, cu_seqlens_q=cu_q, cu_seqlens_k=cu_k,
-                  cmp_residual_k=res, topk_length=tlen, metadata=md,
-                  softmax_scale=p.softmax_scale, max_seqlen_k=p.max_seqlen_k,
-                  cmp_ratio=p.cmp_ratio, mask_mode=p.mask_mode, layout_q=p.layout,
-                  layout_k=p.layout, out=out)
+
+    def call_args(md, o):
+        return dict(sparse_indices=idx, cu_seqlens_q=cu_q, cu_seqlens_k=cu_k,
+                    cmp_residual_k=res, topk_length=tlen, metadata=md,
+                    softmax_scale=p.softmax_scale, max_seqlen_k=p.max_seqlen_k,
+                    cmp_ratio=p.cmp_ratio, mask_mode=p.mask_mode, layout_q=p.layout,
+                    layout_k=p.layout, out=o)
+
+    # the main call's softmax_lse input, computed untimed by the GPU lse call
+    lse_d = None
+    if args.op == "l1norm":
+        lse_d = torch.empty(p.lse_shape(), dtype=torch.float32, device=dev)
+        smla.smla_softmax_lse(q, k, **call_args(metadata(), lse_d))
+        torch.cuda.synchronize()
+        p.softmax_lse = lse_d.cpu().numpy()
+
+    def step(before=None, after=None):
+        md = metadata()
+        kw = call_args(md, out)
         if before is not None:
             before.record(stream)
         if args.op == "lse":
@@ -229,15 +369,17 @@ def main():
     ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
           for _ in range(args.steps)]
     log(f"timing {args.steps} steps")
+    clock = ClockSampler(torch, 0)
     torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for i in range(args.steps):
-        md = step(ev[i][0], ev[i][1])
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
+    with clock:
+        t0 = time.perf_counter()
+        for i in range(args.steps):
+            md = step(ev[i][0], ev[i][1])
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t0
     kernel_ms = [a.elapsed_time(b) for a, b in ev]
     ms_step = wall * 1e3 / args.steps
-    kms = float(np.mean(kernel_ms))
+    kms = float(np.median(kernel_ms))
 
     tflops = flops / (ms_step * 1e-3) / 1e12
     gbps = nbytes / (ms_step * 1e-3) / 1e9
@@ -257,6 +399,8 @@ def main():
     roof["traffic"] = None if p.kwide else measured_traffic(kernel, p.name)
     roof["kernel"] = kernel
     roof["kernel_ms"] = round(kms, 4)
+    roof["kernel_ms_mean"] = round(float(np.mean(kernel_ms)), 4)
+    roof["kernel_ms_min"] = round(float(np.min(kernel_ms)), 4)
     roof["algorithmic_flops"] = flops
     roof["algorithmic_bytes"] = nbytes
 
@@ -278,13 +422,30 @@ def main():
                    "mask_mode": p.mask_mode, "cmp_ratio": p.cmp_ratio,
                    "valid_pairs": pairs, "op": args.op, "kwide": p.kwide,
                    "workgroups": int(md[4]) if args.op == "l1norm" else None,
-                   "lse": "stand-in" if args.op == "l1norm" else "computed"},
+                   "lse": "computed (smla_softmax_lse, untimed)" if args.op == "l1norm"
+                          else "output"},
         "roofline": roof,
+        "clock_mhz": clock.summary(),
         "cpu_baseline": None,
+        "parity": None,
     }
-    if not args.no_cpu_baseline:
-        line["cpu_baseline"] = cpu_baseline(p, args.cpu_seconds, args.op)
+    # the timed output (every step wrote the same values) against the oracle
+    out_rows = out.reshape(p.rows, -1).cpu().numpy()
+    base, rows, expect = cpu_baseline(p, args.cpu_seconds, args.op,
+                                      timed=not args.no_cpu_baseline)
+    line["cpu_baseline"] = base
+    lse_sample = None
+    lse_rows = None
+    if args.op == "l1norm":
+        import oracle
+        lrows = np.unique(np.linspace(0, p.rows - 1, min(p.rows, 64)).astype(np.int64))
+        lse_sample = (lrows, oracle.lse(p, rows=lrows)[0])
+        lse_rows = p.softmax_lse.reshape(p.rows, p.groups)
+    line["parity"] = parity_check(p, args.op, out_rows, lse_rows, rows, expect, lse_sample)
     print(json.dumps(line), flush=True)
+    if not line["parity"]["ok"]:
+        log(f"PARITY FAILED: {line['parity']}")
+        sys.exit(1)
 
 
 if __name__ == "__main__":

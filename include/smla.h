@@ -47,8 +47,13 @@ enum {
     SMLA_SUCCESS = 0,
     SMLA_ERR_PARAM_NULLPTR = 161001,
     SMLA_ERR_PARAM_INVALID = 161002,
-    SMLA_ERR_UNSUPPORTED = 161101, /* valid on the page, not built here
-                                      (no call returns it at present) */
+    SMLA_ERR_UNSUPPORTED = 161101, /* valid on the page, beyond this
+                                      library's limits: a key sequence of
+                                      more than 2^21 rows, topk above 2^24,
+                                      or output rows wider than 0x1FFFFFFC
+                                      columns (the kernels address key rows,
+                                      index lists and output rows with
+                                      32-bit byte offsets) */
     SMLA_ERR_RUNTIME = 561001      /* a HIP runtime call failed */
 };
 
@@ -79,7 +84,9 @@ enum { SMLA_MASK_NONE = 0, SMLA_MASK_RIGHT_DOWN_CAUSAL = 3 };
  *        per CU), 1 = pipelined (65..128 heads with topk <= 2048 or the
  *        dense case: one 4-wave workgroup per CU, 64 heads per wave,
  *        64-key tiles);
- *        [25..63] zero.
+ *   [25] the longest key sequence (BSND: S2; TND: the longest
+ *        cu_seqlens_k step);
+ *        [26..63] zero.
  */
 #define SMLA_META_MAGIC 0x534D4C41
 
@@ -116,8 +123,16 @@ enum { SMLA_MASK_NONE = 0, SMLA_MASK_RIGHT_DOWN_CAUSAL = 3 };
  *
  * Errors: SMLA_ERR_PARAM_NULLPTR (metadata_host NULL, TND without
  * cu_seqlens), SMLA_ERR_PARAM_INVALID (out-of-range value, layout mismatch,
- * inconsistent cu_seqlens),
+ * inconsistent cu_seqlens), SMLA_ERR_UNSUPPORTED (a key sequence longer than
+ * 2^21 rows, topk above 2^24, more than 0x1FFFFFFC key rows),
  * SMLA_ERR_RUNTIME (device query failed; only when core_budget == 0).
+ *
+ * Core budget: not a page parameter. The page's metadata operator caps the
+ * split at the device's core count; core_budget lets a caller (tests, or a
+ * caller sharing the GPU) split over fewer workgroups instead.
+ *
+ * Environment: SMLA_LOG=1 prints one line per metadata call and per launch
+ * (shapes, kernel, grid) on stderr.
  */
 smla_status_t smla_l1norm_metadata(
     int64_t num_heads_q, int64_t num_heads_k, int64_t head_dim,
@@ -146,7 +161,15 @@ smla_status_t smla_l1norm_metadata(
  *                  its position is < the row's entry count (topk_length
  *                  below), it lies in [0, S2_b) and
  *                  the mask lets the key through. Used entries of one row
- *                  must be distinct (duplicates are not supported).
+ *                  must be distinct: the kernels write each entry's value
+ *                  to its key's column, so with a repeated key one write
+ *                  wins and the row loses both its sum of 1 and its
+ *                  run-to-run determinism. Nothing checks this by default;
+ *                  smla_check_indices checks host copies, and with
+ *                  SMLA_CHECK_INDICES=1 in the environment every main call
+ *                  copies its index lists to the host (synchronising the
+ *                  stream) and fails with SMLA_ERR_PARAM_INVALID on a row
+ *                  that repeats a key.
  *   cu_seqlens_q, cu_seqlens_k  int32 (B+1) device, required for TND
  *   seqused_q, seqused_k        int32 (B) device, optional (parameter
  *                  table: the q / k tokens of each batch that take part):
@@ -184,6 +207,7 @@ smla_status_t smla_l1norm_metadata(
  * match the metadata; SMLA_ERR_PARAM_NULLPTR when a conditionally required
  * pointer is NULL (metadata, cu_seqlens for TND, cmp_residual_k,
  * topk_length);
+ * SMLA_ERR_UNSUPPORTED beyond the limits listed with the status codes;
  * SMLA_ERR_RUNTIME if the launch fails. An empty q (R == 0) or an empty
  * output (S2/T2 == 0) returns SMLA_SUCCESS once the attributes are checked,
  * before any pointer or the metadata is looked at, and launches nothing.
@@ -272,6 +296,31 @@ smla_status_t smla_softmax_lse(
     int64_t topk, double softmax_scale, int64_t max_seqlen_k, int64_t cmp_ratio,
     int64_t mask_mode, int32_t layout_q, int32_t layout_k, float* softmax_lse,
     void* stream);
+
+/*
+ * smla_check_indices - host check of the distinct-entries precondition of
+ * the main calls (parameter table, sparse_indices: the selected key blocks
+ * of a row; a selection names each key once).
+ *
+ *   sparse_indices_host  int32 (rows, topk) in host memory
+ *   topk_length_host     int32 (rows) in host memory, or NULL (then every
+ *                        one of the topk entries is looked at)
+ *   rows, topk           the list's shape (>= 0)
+ *   first_bad_row        out, may be NULL: the first row that repeats a key,
+ *                        -1 when none does
+ *
+ * Looks at entries t < n (n = topk_length[row] clamped to [0, topk]) with a
+ * non-negative index, and fails on the first row in which two of them name
+ * the same key. This is stricter than the kernels need: a repeated key that
+ * lies past S2_b or that the mask hides is never used, but is flagged too.
+ *
+ * Errors: SMLA_ERR_PARAM_INVALID (negative sizes, or a repeated key: the
+ * message names the row, the key and both entries), SMLA_ERR_PARAM_NULLPTR
+ * (sparse_indices_host NULL with rows and topk > 0). Host only.
+ */
+smla_status_t smla_check_indices(const int32_t* sparse_indices_host,
+                                 const int32_t* topk_length_host, int64_t rows, int64_t topk,
+                                 int64_t* first_bad_row);
 
 /* Elements of the output for the given shapes: B*S1*N2*S2 (BSND) or
  * T1*N2*T2 (TND); -1 for an unknown layout or a negative size. Host only. */

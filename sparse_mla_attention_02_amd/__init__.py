@@ -30,7 +30,7 @@ __all__ = [
     "SmlaError", "library_path", "smla_l1norm_metadata", "smla_softmax_l1norm",
     "smla_softmax_lse", "sparse_flash_mla_softmax_l1_norm_metadata",
     "sparse_flash_mla_softmax_l1_norm", "sparse_flash_mla_softmax_lse",
-    "output_shape", "SMLA_METADATA_SIZE",
+    "output_shape", "smla_check_indices", "SMLA_METADATA_SIZE",
 ]
 
 SMLA_METADATA_SIZE = 64
@@ -82,6 +82,8 @@ def _load():
     lib.smla_last_error.restype = ctypes.c_char_p
     lib.smla_version.argtypes = []
     lib.smla_version.restype = i32
+    lib.smla_check_indices.argtypes = [p, p, i64, i64, ctypes.POINTER(i64)]
+    lib.smla_check_indices.restype = i32
     return lib
 
 
@@ -111,6 +113,21 @@ def _host_i32(t) -> Optional[torch.Tensor]:
 
 def _ptr(t: Optional[torch.Tensor]):
     return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def smla_check_indices(sparse_indices, topk_length=None) -> None:
+    """Check the distinct-entries precondition of the main calls on host
+    copies (``smla_check_indices`` of the C ABI): raises ``SmlaError`` naming
+    the first row whose used entries (t < topk_length, index >= 0) repeat a
+    key. ``sparse_indices`` is int32 with the rows first and K last."""
+    idx = _host_i32(sparse_indices)
+    K = int(idx.shape[-1]) if idx.dim() else 0
+    rows = idx.numel() // K if K else 0
+    tl = _host_i32(topk_length)
+    if tl is not None and tl.numel() != rows:
+        raise SmlaError(SMLA_ERR_PARAM_INVALID, "topk_length must hold one count per row")
+    bad = ctypes.c_int64(-1)
+    _check(_lib.smla_check_indices(_ptr(idx), _ptr(tl), rows, K, ctypes.byref(bad)))
 
 
 def sparse_flash_mla_softmax_l1_norm_metadata(

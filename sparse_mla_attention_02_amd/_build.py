@@ -27,6 +27,8 @@ COMMON = ["--offload-arch=" + ARCH, "-O3", "-std=c++17", "-fPIC",
           "-Wall", "-Wno-unused-command-line-argument", "-I", INCLUDE, "-I", CSRC]
 KERNELS = os.path.join(CSRC, "smla_kernels.hip")
 HOST = os.path.join(CSRC, "smla_host.cpp")
+EXAMPLE_SRC = os.path.join(CSRC, "example", "smla_example.cpp")
+EXAMPLE = os.path.join(PKG, "smla_example")
 
 
 def commands(out: str, tmp: str) -> list:
@@ -46,22 +48,37 @@ def commands(out: str, tmp: str) -> list:
     ]
 
 
+def _run(cmd, verbose):
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    res = subprocess.run(cmd, capture_output=True, text=True)
+    msg = "\n".join(l for l in (res.stdout + res.stderr).splitlines()
+                    if "packed-fp32-ops" not in l)
+    if res.returncode != 0:
+        raise RuntimeError("hipcc failed:\n" + msg)
+    if verbose and msg.strip():
+        print(msg, flush=True)
+
+
+def example_command(out: str) -> list:
+    """The example host program on the C ABI, linked against libsmla.so in
+    the same folder."""
+    return [hipcc(), "-O2", "-std=c++17", "-Wall", "-I", INCLUDE, EXAMPLE_SRC, "-L", PKG,
+            "-lsmla", "-Wl,-rpath,$ORIGIN", "-o", out]
+
+
 def build(verbose: bool = False) -> str:
-    """Compile every source into ``libsmla.so`` (always recompiles)."""
+    """Compile every source into ``libsmla.so`` and the example program
+    (always recompiles)."""
     import tempfile
     out = LIB + ".tmp%d" % os.getpid()
     with tempfile.TemporaryDirectory(prefix="smla_build_") as tmp:
         for cmd in commands(out, tmp):
-            if verbose:
-                print(" ".join(cmd), flush=True)
-            res = subprocess.run(cmd, capture_output=True, text=True)
-            msg = "\n".join(l for l in (res.stdout + res.stderr).splitlines()
-                            if "packed-fp32-ops" not in l)
-            if res.returncode != 0:
-                raise RuntimeError("hipcc failed:\n" + msg)
-            if verbose and msg.strip():
-                print(msg, flush=True)
+            _run(cmd, verbose)
     os.replace(out, LIB)
+    exe = EXAMPLE + ".tmp%d" % os.getpid()
+    _run(example_command(exe), verbose)
+    os.replace(exe, EXAMPLE)
     return LIB
 
 

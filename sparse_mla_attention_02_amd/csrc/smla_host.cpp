@@ -7,14 +7,17 @@
 // codes (section 调用方式一 aclnn API).
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
+#include <cstdlib>
 #include <cstring>
 #include <map>
 #include <mutex>
 #include <string>
 #include <tuple>
+#include <vector>
 
 #include "smla.h"
 #include "smla_internal.h"
@@ -73,8 +76,32 @@ hipError_t device_capacity(int device, int ht, bool tnd, int64_t topk, int* cus,
     return hipSuccess;
 }
 
-constexpr int32_t kVersion = 1;
+constexpr int32_t kVersion = 2;
 constexpr int64_t kHeadDim = 512;
+// Limits of the kernels' 32-bit buffer offsets: a key row is addressed as
+// key * 1024 bytes from its sequence's first row, an index list as entry * 4
+// bytes, an output row as column * 4 bytes (signed 32-bit range).
+constexpr int64_t kMaxKeysPerSeq = int64_t(1) << 21;
+constexpr int64_t kMaxTopk = int64_t(1) << 24;
+constexpr int64_t kMaxWidth = 0x1FFFFFFC;
+
+// SMLA_LOG=1: one line on stderr per metadata call and per launch.
+bool log_on() {
+    static const bool on = [] {
+        const char* v = std::getenv("SMLA_LOG");
+        return v && *v && std::strcmp(v, "0") != 0;
+    }();
+    return on;
+}
+// SMLA_CHECK_INDICES=1: the main calls copy the index lists to the host and
+// reject a row whose used entries repeat a key (see smla_check_indices).
+bool check_indices_on() {
+    static const bool on = [] {
+        const char* v = std::getenv("SMLA_CHECK_INDICES");
+        return v && *v && std::strcmp(v, "0") != 0;
+    }();
+    return on;
+}
 
 // Shared checks of the scalar attributes of both calls.
 smla_status_t check_common(int64_t n1, int64_t n2, int64_t d, int32_t layout_q,
@@ -119,11 +146,55 @@ smla_status_t check_cu(const int32_t* cu, int64_t B, const char* name, int64_t* 
     return SMLA_SUCCESS;
 }
 
+// Rows [0, rows) of a host index list: the first row whose entries t < n
+// (n = topk_length[r] clamped to [0, K], or K) repeat a non-negative key.
+// Returns -1 when every row is fine; *t0/*t1 get the two entry positions.
+int64_t first_repeat(const int32_t* idx, const int32_t* tlen, int64_t rows, int64_t K,
+                     int64_t* t0, int64_t* t1) {
+    std::vector<std::pair<int32_t, int32_t>> v;
+    v.reserve((size_t)K);
+    for (int64_t r = 0; r < rows; ++r) {
+        int64_t n = K;
+        if (tlen) n = std::min<int64_t>(std::max<int64_t>(tlen[r], 0), K);
+        v.clear();
+        const int32_t* row = idx + r * K;
+        for (int64_t t = 0; t < n; ++t)
+            if (row[t] >= 0) v.emplace_back(row[t], (int32_t)t);
+        std::sort(v.begin(), v.end());
+        for (size_t i = 1; i < v.size(); ++i)
+            if (v[i].first == v[i - 1].first) {
+                *t0 = v[i - 1].second;
+                *t1 = v[i].second;
+                return r;
+            }
+    }
+    return -1;
+}
+
 }  // namespace
 
 extern "C" {
 
-int32_t smla_version(void) { return 10000 * 0 + 100 * 1 + 0; }
+int32_t smla_version(void) { return 10000 * 0 + 100 * 2 + 0; }
+
+smla_status_t smla_check_indices(const int32_t* sparse_indices_host,
+                                 const int32_t* topk_length_host, int64_t rows, int64_t topk,
+                                 int64_t* first_bad_row) {
+    if (first_bad_row) *first_bad_row = -1;
+    if (rows < 0 || topk < 0) return fail(SMLA_ERR_PARAM_INVALID, "rows and topk must be >= 0");
+    if (rows == 0 || topk == 0) return ok();
+    if (!sparse_indices_host) return fail(SMLA_ERR_PARAM_NULLPTR, "sparse_indices_host is NULL");
+    int64_t t0 = 0, t1 = 0;
+    const int64_t r = first_repeat(sparse_indices_host, topk_length_host, rows, topk, &t0, &t1);
+    if (r >= 0) {
+        if (first_bad_row) *first_bad_row = r;
+        return fail(SMLA_ERR_PARAM_INVALID,
+                    "row %lld repeats key %d at entries %lld and %lld (used entries of a row "
+                    "must be distinct)", (long long)r, sparse_indices_host[r * topk + t0],
+                    (long long)t0, (long long)t1);
+    }
+    return ok();
+}
 
 const char* smla_last_error(void) { return g_last_error.c_str(); }
 
@@ -186,6 +257,24 @@ smla_status_t smla_l1norm_metadata(
     }
     if (R > INT32_MAX || rows_k > INT32_MAX || B > INT32_MAX)
         return fail(SMLA_ERR_PARAM_INVALID, "sizes exceed the int32 metadata fields");
+    // the longest key sequence (BSND: S2; TND: the longest cu_seqlens_k step)
+    int64_t longest_k = mk;
+    if (layout_q == SMLA_LAYOUT_TND) {
+        int64_t tk, mxk;
+        (void)check_cu(cu_seqlens_k_host, B, "cu_seqlens_k", &tk, &mxk);
+        longest_k = mxk;
+    }
+    if (longest_k > kMaxKeysPerSeq)
+        return fail(SMLA_ERR_UNSUPPORTED,
+                    "a key sequence of %lld rows exceeds the supported %lld (32-bit key "
+                    "offsets)", (long long)longest_k, (long long)kMaxKeysPerSeq);
+    if (topk > kMaxTopk)
+        return fail(SMLA_ERR_UNSUPPORTED, "topk %lld exceeds the supported %lld",
+                    (long long)topk, (long long)kMaxTopk);
+    if (rows_k > kMaxWidth)
+        return fail(SMLA_ERR_UNSUPPORTED,
+                    "%lld key rows (the output row width) exceed the supported %lld "
+                    "(32-bit output offsets)", (long long)rows_k, (long long)kMaxWidth);
 
     const int ht = smla::head_tiles_for(num_heads_q / num_heads_k);
     int cus = 0, per_cu = 0;
@@ -231,6 +320,16 @@ smla_status_t smla_l1norm_metadata(
     m[22] = cus;
     m[23] = per_cu;
     m[24] = smla::uses_pipe(ht, topk) ? 1 : 0;  // kernel variant
+    m[25] = (int32_t)longest_k;
+    if (log_on())
+        std::fprintf(stderr,
+                     "smla: metadata layout=%s R=%lld N1=%lld K=%lld mask=%lld cmp=%lld "
+                     "rows_k=%lld longest_k=%lld cores=%d rows/core=%d/%d tail=%d "
+                     "kernel=%s cus=%d per_cu=%d\n",
+                     layout_q == SMLA_LAYOUT_TND ? "TND" : "BSND", (long long)R,
+                     (long long)num_heads_q, (long long)topk, (long long)mask_mode,
+                     (long long)cmp_ratio, (long long)rows_k, (long long)longest_k, m[4],
+                     m[1], m[2], m[3], m[24] ? "pipelined" : "general", cus, per_cu);
     return ok();
 }
 
@@ -306,6 +405,13 @@ smla_status_t prepare(const void* q, const void* k, const int32_t* sparse_indice
                     "topk_length is required when mask_mode == 0 with sparse_indices");
     if (R > INT32_MAX || rows_k > INT32_MAX || topk > INT32_MAX)
         return fail(SMLA_ERR_PARAM_INVALID, "sizes exceed the supported range");
+    if (topk > kMaxTopk)
+        return fail(SMLA_ERR_UNSUPPORTED, "topk %lld exceeds the supported %lld",
+                    (long long)topk, (long long)kMaxTopk);
+    if (W > kMaxWidth)
+        return fail(SMLA_ERR_UNSUPPORTED,
+                    "output rows of %lld columns exceed the supported %lld (32-bit output "
+                    "offsets)", (long long)W, (long long)kMaxWidth);
 
     const int32_t* m = metadata_host;
     if (m[5] != SMLA_META_MAGIC || m[6] != kVersion)
@@ -323,6 +429,8 @@ smla_status_t prepare(const void* q, const void* k, const int32_t* sparse_indice
                     "metadata's max_seqlen_k");
     if (m[4] < 1 || m[4] > m[0])
         return fail(SMLA_ERR_PARAM_INVALID, "metadata core count is out of range");
+    if (m[25] < 0 || m[25] > kMaxKeysPerSeq || (!tnd && m[25] != seqlen_k))
+        return fail(SMLA_ERR_PARAM_INVALID, "metadata longest key sequence is out of range");
 
     smla::KernelArgs& a = *out_args;
     a = smla::KernelArgs{};
@@ -357,6 +465,62 @@ smla_status_t prepare(const void* q, const void* k, const int32_t* sparse_indice
     a.num_wg = m[4];
     a.snake = m[19];
     return SMLA_SUCCESS;
+}
+
+// SMLA_CHECK_INDICES: copies the index lists (and topk_length) of a main
+// call to the host on its stream, waits, and checks them.
+smla_status_t check_device_indices(const smla::KernelArgs& a, hipStream_t stream) {
+    if (a.dense || !a.idx) return SMLA_SUCCESS;
+    std::vector<int32_t> idx((size_t)(a.R * a.K)), tl;
+    hipError_t e = hipMemcpyAsync(idx.data(), a.idx, idx.size() * 4, hipMemcpyDeviceToHost,
+                                  stream);
+    if (e == hipSuccess && a.topk_len) {
+        tl.resize((size_t)a.R);
+        e = hipMemcpyAsync(tl.data(), a.topk_len, tl.size() * 4, hipMemcpyDeviceToHost,
+                           stream);
+    }
+    if (e == hipSuccess) e = hipStreamSynchronize(stream);
+    if (e != hipSuccess)
+        return fail(SMLA_ERR_RUNTIME, "index check copy failed: %s", hipGetErrorString(e));
+    int64_t t0 = 0, t1 = 0;
+    const int64_t r = first_repeat(idx.data(), a.topk_len ? tl.data() : nullptr, a.R, a.K,
+                                   &t0, &t1);
+    if (r >= 0)
+        return fail(SMLA_ERR_PARAM_INVALID,
+                    "row %lld repeats key %d at entries %lld and %lld (used entries of a row "
+                    "must be distinct)", (long long)r, idx[(size_t)(r * a.K + t0)],
+                    (long long)t0, (long long)t1);
+    return SMLA_SUCCESS;
+}
+
+void log_launch(const char* call, const smla::KernelArgs& a, int ht, int32_t dtype,
+                const char* kernel, int32_t grid, int32_t block, void* stream) {
+    if (!log_on()) return;
+    std::fprintf(stderr,
+                 "smla: %s kernel=%s grid=%d block=%d R=%lld W=%lld G=%d K=%d head_tiles=%d "
+                 "dtype=%s dense=%d kwide=%d mask=%d cmp=%d stream=%p\n",
+                 call, kernel, grid, block, (long long)a.R, (long long)a.W, a.G, a.K, ht,
+                 dtype == SMLA_DTYPE_BF16 ? "bf16" : "fp16", a.dense, a.kwide, a.mask_mode,
+                 a.cmp_ratio, stream);
+}
+
+// Enqueues the main kernel for prepared arguments (both main calls).
+smla_status_t run_main(const char* call, const smla::KernelArgs& a, int32_t dtype,
+                       int32_t layout_q, void* stream) {
+    const hipStream_t s = static_cast<hipStream_t>(stream);
+    if (check_indices_on()) {
+        smla_status_t st = check_device_indices(a, s);
+        if (st != SMLA_SUCCESS) return st;
+    }
+    const int ht = smla::head_tiles_for(a.G);
+    const bool pipe = smla::uses_pipe(ht, a.dense ? 0 : a.K);
+    log_launch(call, a, ht, dtype, pipe ? "smla_wide_kernel" : "smla_l1norm_kernel",
+               a.num_wg, pipe ? 256 : 64 * ht, stream);
+    hipError_t e = smla::launch(a, ht, dtype == SMLA_DTYPE_BF16, layout_q == SMLA_LAYOUT_TND,
+                                s);
+    if (e != hipSuccess)
+        return fail(SMLA_ERR_RUNTIME, "kernel launch failed: %s", hipGetErrorString(e));
+    return ok();
 }
 
 // Co-resident workgroups per CU of the lse kernel, queried once per variant.
@@ -403,12 +567,7 @@ smla_status_t smla_softmax_l1norm(
                                softmax_l1_norm, &a, &nothing);
     if (st != SMLA_SUCCESS) return st;
     if (nothing) return ok();
-    const int ht = smla::head_tiles_for(a.G);
-    hipError_t e = smla::launch(a, ht, dtype == SMLA_DTYPE_BF16, layout_q == SMLA_LAYOUT_TND,
-                                static_cast<hipStream_t>(stream));
-    if (e != hipSuccess)
-        return fail(SMLA_ERR_RUNTIME, "kernel launch failed: %s", hipGetErrorString(e));
-    return ok();
+    return run_main("smla_softmax_l1norm", a, dtype, layout_q, stream);
 }
 
 smla_status_t smla_softmax_l1norm_kwide(
@@ -431,12 +590,7 @@ smla_status_t smla_softmax_l1norm_kwide(
                                softmax_l1_norm, &a, &nothing);
     if (st != SMLA_SUCCESS) return st;
     if (nothing) return ok();
-    const int ht = smla::head_tiles_for(a.G);
-    hipError_t e = smla::launch(a, ht, dtype == SMLA_DTYPE_BF16, layout_q == SMLA_LAYOUT_TND,
-                                static_cast<hipStream_t>(stream));
-    if (e != hipSuccess)
-        return fail(SMLA_ERR_RUNTIME, "kernel launch failed: %s", hipGetErrorString(e));
-    return ok();
+    return run_main("smla_softmax_l1norm_kwide", a, dtype, layout_q, stream);
 }
 
 smla_status_t smla_softmax_lse(
@@ -472,6 +626,8 @@ smla_status_t smla_softmax_lse(
         const int64_t cap = (int64_t)m[22] * per_cu;
         a.num_wg = (int32_t)(a.R < cap ? a.R : cap);
     }
+    log_launch("smla_softmax_lse", a, ht, dtype, "smla_lse_kernel", a.num_wg,
+               64 * (ht == 4 ? 2 : ht), stream);
     hipError_t e = smla::launch_lse(a, ht, bf16, tnd, static_cast<hipStream_t>(stream));
     if (e != hipSuccess)
         return fail(SMLA_ERR_RUNTIME, "kernel launch failed: %s", hipGetErrorString(e));

@@ -337,6 +337,7 @@ __global__ __launch_bounds__(64 * HT, 2) void smla_l1norm_kernel(KernelArgs a) {
     __shared__ uint4 kbuf0[kTile * kPitch];
     __shared__ uint4 kbuf1[kTile * kPitch];
     __shared__ float red[2][2 * HT][kTile];   // half-wave partial sums, last two tiles
+    __shared__ float redl[2 * HT][kTile];     // the same for a row's last tile
     __shared__ float vals[kVcap + 64];        // the row's values by entry; then a sink
 
     const int tid = threadIdx.x;
@@ -444,12 +445,11 @@ __global__ __launch_bounds__(64 * HT, 2) void smla_l1norm_kernel(KernelArgs a) {
         // lanes. `key` is the tile's raw index register. The staged version
         // has no branch: other lanes (and tiles < 0) write to the sink.
         constexpr int kSlotsPerWave = kTile / HT;
-        auto reduce = [&](int tile, int32_t key) {
+        auto reduce_from = [&](const float (*pr)[kTile], int tile, int32_t key) {
             const int slot = (wave * kSlotsPerWave + lane) & (kTile - 1);
-            const int pb = tile & 1;
-            float tot = red[pb][0][slot];
+            float tot = pr[0][slot];
 #pragma unroll
-            for (int w = 1; w < 2 * HT; ++w) tot += red[pb][w][slot];
+            for (int w = 1; w < 2 * HT; ++w) tot += pr[w][slot];
             const float v = tot * a.inv_g;
             if constexpr (STAGED) {
                 const bool mine = lane < kSlotsPerWave && tile >= 0;
@@ -460,6 +460,7 @@ __global__ __launch_bounds__(64 * HT, 2) void smla_l1norm_kernel(KernelArgs a) {
                     orow[a.kwide ? tile * kTile + slot : ri.col0 + j] = v;
             }
         };
+        auto reduce = [&](int tile, int32_t key) { reduce_from(red[tile & 1], tile, key); };
 
         f32x16_t acc_prev = {};
         int32_t key_p1 = -1, key_p2 = -1;  // raw indices of tiles t-1 and t-2
@@ -496,8 +497,9 @@ __global__ __launch_bounds__(64 * HT, 2) void smla_l1norm_kernel(KernelArgs a) {
         } else if (tile < ntiles) {
             body(Par<0>{}, tile, kbuf0, kbuf1);
         }
-        if (ntiles > 0)
-            red[(ntiles - 1) & 1][2 * wave + half][col] = head_sum(acc_prev, l2, a.c_scale);
+        // (the last tile's sums go to their own buffer: a slower wave may
+        // still be reading red[(ntiles - 1) & 1] in the last tile's reduce)
+        if (ntiles > 0) redl[2 * wave + half][col] = head_sum(acc_prev, l2, a.c_scale);
 
         // indices for the row assembly, then the next row's Q and lse: all
         // in flight together; waits below cover only the indices
@@ -516,7 +518,7 @@ __global__ __launch_bounds__(64 * HT, 2) void smla_l1norm_kernel(KernelArgs a) {
 
         __syncthreads();  // partial sums in LDS (the barrier waits for LDS writes)
         if (ntiles >= 2) reduce(ntiles - 2, key_p2);
-        if (ntiles >= 1) reduce(ntiles - 1, key_p1);
+        if (ntiles >= 1) reduce_from(redl, ntiles - 1, key_p1);
 
         if (staged) {
             // assemble columns [seg0, seg1) in LDS and write them once. Stage

@@ -106,7 +106,8 @@ def test_metadata_fields_follow_page_formulas(total, budget):
     assert 0 <= m[3] < max(m[4], 1)
     assert m[5] == 0x534D4C41 and m[8] == 128 and m[9] == 1 and m[10] == 512
     assert m[24] == 1                          # 128 heads, topk 2048: pipelined kernel
-    assert (m[25:] == 0).all()
+    assert m[25] == 4096                       # the longest key sequence (S2)
+    assert (m[26:] == 0).all()
 
 
 @pytest.mark.parametrize("heads,topk,variant", [(128, 2048, 1), (65, 64, 1), (64, 2048, 0),
@@ -198,8 +199,8 @@ def base_args(layout=0, G=128, K=2048, mask=3, ratio=1, B=1, S1=64, S2=64):
     md = np.zeros(64, dtype=np.int32)
     R = B * S1 if layout == 0 else S1
     rows_k = B * S2 if layout == 0 else S2
-    md[[0, 4, 5, 6, 7, 8, 9, 10, 11, 12, 13, 14, 15, 16, 17, 18, 19]] = [
-        R, 0, 0x534D4C41, 1, layout, G, 1, 512, B, S1, S2, K, mask, ratio, R, rows_k, 1]
+    md[[0, 4, 5, 6, 7, 8, 9, 10, 11, 12, 13, 14, 15, 16, 17, 18, 19, 25]] = [
+        R, 0, 0x534D4C41, 2, layout, G, 1, 512, B, S1, S2, K, mask, ratio, R, rows_k, 1, S2]
     a = dict(q=FAKE, k=FAKE, lse=FAKE, idx=FAKE, cu_q=None, cu_k=None, sq=None, sk=None,
              res=None, tlen=FAKE, meta=md, dtype=1, B=B, S1=S1, S2=S2, N1=G, N2=1, D=512,
              K=K, scale=0.044, maxk=0, ratio=ratio, mask=mask, lq=layout, lk=layout,
@@ -401,3 +402,104 @@ def test_kwide_dense_tnd_width_is_max_seqlen_k():
     a["maxk"] = 0
     a["out"] = None
     assert call_kwide(a) == 0
+
+
+# ---------------------------------------------------------------- limits
+
+def test_metadata_rejects_sizes_past_the_32bit_offsets():
+    """Key rows are addressed as key * 1024 bytes, index lists as entry * 4
+    bytes and output rows as column * 4 bytes, all in 32 bits: the metadata
+    call refuses what would overflow them, with SMLA_ERR_UNSUPPORTED."""
+    import torch
+    for kw in (dict(max_seqlen_k=(1 << 21) + 1), dict(topk=(1 << 24) + 1)):
+        with pytest.raises(smla.SmlaError) as e:
+            meta(**kw)
+        assert e.value.status == smla.SMLA_ERR_UNSUPPORTED, kw
+    # exactly 2^21 keys per sequence is still addressable
+    m = meta(max_seqlen_k=1 << 21).numpy()
+    assert m[25] == 1 << 21
+    # TND: the longest sequence decides, not the total
+    cu_q = torch.tensor([0, 3, 6], dtype=torch.int32)
+    ok_k = torch.tensor([0, 1 << 20, (1 << 21) + (1 << 20)], dtype=torch.int32)
+    m = smla.smla_l1norm_metadata(128, 1, 512, cu_seqlens_q=cu_q, cu_seqlens_k=ok_k,
+                                  topk=16, layout_q="TND", layout_k="TND",
+                                  core_budget=8).numpy()
+    assert m[25] == 1 << 21 and m[18] == (1 << 21) + (1 << 20)
+    bad_k = torch.tensor([0, 5, (1 << 21) + 6], dtype=torch.int32)
+    with pytest.raises(smla.SmlaError) as e:
+        smla.smla_l1norm_metadata(128, 1, 512, cu_seqlens_q=cu_q, cu_seqlens_k=bad_k,
+                                  topk=16, layout_q="TND", layout_k="TND", core_budget=8)
+    assert e.value.status == smla.SMLA_ERR_UNSUPPORTED
+    assert "2097152" in str(e.value)
+
+
+@pytest.mark.parametrize("kw,msg", [
+    (dict(S2=0x1FFFFFFD), b"output rows"), (dict(K=(1 << 24) + 1), b"topk"),
+])
+def test_main_call_rejects_sizes_past_the_32bit_offsets(kw, msg):
+    a = _with(**kw)
+    assert call(a) == smla.SMLA_ERR_UNSUPPORTED, LIB.smla_last_error()
+    assert msg in LIB.smla_last_error()
+
+
+def test_main_call_checks_the_longest_key_sequence_field():
+    a = base_args()
+    a["meta"][4] = 1            # a valid core count: the field 25 check is the last
+    a["meta"][25] = 65          # S2 is 64
+    assert call(a) == 161002
+    assert b"longest key sequence" in LIB.smla_last_error()
+
+
+# ---------------------------------------------------------------- index check
+
+def test_check_indices_accepts_distinct_rows_and_padding():
+    idx = np.array([[3, 1, -1, -1], [0, 2, 5, -1], [7, 7, 7, 7]], dtype=np.int32)
+    tl = np.array([2, 3, 1], dtype=np.int32)   # row 2 looks at one entry only
+    smla.smla_check_indices(idx, tl)
+    # without topk_length every entry is looked at: row 2 repeats key 7
+    with pytest.raises(smla.SmlaError) as e:
+        smla.smla_check_indices(idx)
+    assert e.value.status == 161002 and "row 2" in str(e.value)
+
+
+def test_check_indices_names_the_first_bad_row_and_entries():
+    idx = np.zeros((4, 6), dtype=np.int32)
+    idx[:] = np.arange(6)
+    idx[1, 4] = 1                       # row 1 repeats key 1 at entries 1 and 4
+    idx[3, 5] = 0
+    bad = ctypes.c_int64(0)
+    st = LIB.smla_check_indices(idx.ctypes.data, None, 4, 6, ctypes.byref(bad))
+    assert st == 161002 and bad.value == 1
+    err = LIB.smla_last_error()
+    assert b"row 1" in err and b"key 1" in err and b"entries 1 and 4" in err
+    # a repeat past the row's entry count is never used
+    tl = np.array([6, 4, 6, 5], dtype=np.int32)
+    assert LIB.smla_check_indices(idx.ctypes.data, tl.ctypes.data, 4, 6,
+                                  ctypes.byref(bad)) == 0
+    assert bad.value == -1
+    # sizes and null pointers
+    assert LIB.smla_check_indices(None, None, 0, 6, None) == 0
+    assert LIB.smla_check_indices(None, None, 2, 6, None) == 161001
+    assert LIB.smla_check_indices(idx.ctypes.data, None, -1, 6, None) == 161002
+
+
+def test_check_indices_on_a_generated_workload():
+    import workloads
+    p = workloads.generate("bsnd_causal", batch=1, seqlen_q=64)
+    smla.smla_check_indices(p.sparse_indices, p.topk_length)
+
+
+def test_log_lines_on_stderr():
+    code = ("import sparse_mla_attention_02_amd as s;"
+            "s.smla_l1norm_metadata(128, 1, 512, batch_size=1, max_seqlen_q=8, "
+            "max_seqlen_k=8, topk=4, core_budget=4)")
+    env = dict(os.environ, SMLA_LOG="1")
+    r = subprocess.run([os.sys.executable, "-c", code], cwd=ROOT, env=env,
+                       capture_output=True, text=True, timeout=120)
+    assert r.returncode == 0, r.stderr
+    assert "smla: metadata layout=BSND R=8 N1=128 K=4" in r.stderr
+    assert "cores=4" in r.stderr
+    env["SMLA_LOG"] = "0"
+    r = subprocess.run([os.sys.executable, "-c", code], cwd=ROOT, env=env,
+                       capture_output=True, text=True, timeout=120)
+    assert "smla:" not in r.stderr

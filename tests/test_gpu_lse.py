@@ -23,7 +23,7 @@ import oracle
 import workloads
 from tests import cases as C
 from tests.test_gpu_parity import (MEDIUM, ROWSUM_TOL, TINY, TOL, _t, rows_view, run_gpu,
-                                   sample_rows, say)
+                                   say)
 
 pytestmark = pytest.mark.gpu
 
@@ -137,14 +137,13 @@ FULL = ["dsv32", "tnd_varlen", "compressed", "bsnd_causal", "page_example_dense"
 def test_lse_full_size(smla, name):
     say(f"[lse full] {name}: generating inputs")
     p = workloads.generate(name)
-    rows = sample_rows(p)
     say(f"[lse full] {name}: GPU lse (R={p.rows} G={p.groups} K={p.topk})")
     got = run_lse(smla, p)
-    say(f"[lse full] {name}: oracle lse on {len(rows)} sampled rows")
-    want, _ = oracle.lse(p, rows=rows)
-    check_lse(name, got[rows], want)
-    say(f"[lse full] {name}: main call with the GPU lse, every row")
-    check_end_to_end(name, smla, p, got, rows=rows)
+    say(f"[lse full] {name}: oracle lse on all {p.rows} rows")
+    want, _ = oracle.lse(p)
+    check_lse(name, got, want)
+    say(f"[lse full] {name}: main call with the GPU lse, every row against the oracle")
+    check_end_to_end(name, smla, p, got)
 
 
 @pytest.mark.parametrize("heads", [16, 128])

@@ -1,13 +1,26 @@
-"""The pipelined (65..128-head) kernel at every tile-count boundary, through
-the C-ABI binding, against the CPU oracle.
+"""Every kernel variant at every tile-count boundary, through the C-ABI
+binding, against the CPU oracle.
 
-A row of n used entries runs ceil(n / 64) key tiles: tiles with two more after
-them take the steady path, the last two or three form their stream state at
-the tile boundary, a tile's epilogue finishes two tiles later, and the row end
+A row of n used entries runs ceil(n / T) key tiles (T = 64 keys for the
+pipelined kernels, 32 for the general one): tiles with two more after them
+take the steady path, the last two or three form their stream state at the
+tile boundary, a tile's epilogue finishes two tiles later, and the row end
 loads the next row's Q and lse as the tile loop ends. Here every row length
-around a multiple of 64 (0 .. 16 tiles) appears, in a shuffled order, and the
-work is split over a few workgroups (a caller's core budget), so that each
-workgroup walks many rows and meets every transition between row lengths.
+around a multiple of the tile appears, in a shuffled order, and the work is
+split over a few workgroups (a caller's core budget), so that each workgroup
+walks many rows and meets every transition between row lengths.
+
+Cases, by the kernel variant they reach (the constraints section of the
+article allows any B, S1, S2 and S1 != S2; the three-stage formula is the
+same for every head count):
+
+* 65..128 heads, output rows of at most 4096 columns: the pipelined kernel
+  with the row assembled in LDS (sparse and dense);
+* 65..128 heads, rows wider than 4096 columns: the pipelined kernel that
+  zero-fills each row and stores values directly (double-buffered index
+  lists; sparse, dense TND, K-wide dense);
+* up to 64 heads (16, 33, 64), up to 2048 indices per row, and more than
+  2048 (the variant without the LDS row).
 
 Bar: |gpu - oracle| <= 2e-5 per element on every row, and every row with a
 used entry sums to 1 within 1e-4 (the derivation is in test_gpu_parity).
@@ -32,6 +45,12 @@ LENGTHS = sorted({0, 1, 2} | {v for m in range(64, 1025, 64) for v in (m - 1, m,
                               if v <= 1024} | {700, 1000})
 
 
+def lengths(tile, top, extra=()):
+    """Both sides of every multiple of `tile` up to `top`, plus 0, 1, 2."""
+    return sorted({0, 1, 2} | {v for m in range(tile, top + 1, tile)
+                               for v in (m - 1, m, m + 1) if v <= top} | set(extra))
+
+
 @pytest.fixture(scope="module")
 def smla():
     if not torch.cuda.is_available():
@@ -44,11 +63,11 @@ def _t(a, dev="cuda"):
     return None if a is None else torch.from_numpy(np.ascontiguousarray(a)).to(dev)
 
 
-def with_lengths(p, seed):
-    """p with topk_length set to LENGTHS, repeated over the rows and shuffled."""
+def with_lengths(p, seed, lens=LENGTHS):
+    """p with topk_length set to `lens`, repeated over the rows and shuffled."""
     p = C.clone(p)
     rng = np.random.Generator(np.random.PCG64(seed))
-    tl = np.resize(np.array(LENGTHS, dtype=np.int32), p.rows)
+    tl = np.resize(np.array(lens, dtype=np.int32), p.rows)
     rng.shuffle(tl)
     p.topk_length = tl.reshape(p.topk_length.shape)
     return p
@@ -66,6 +85,47 @@ def cases():
     cs.append(("dense_bsnd_g128_causal", C.gen("tiny", heads_q=128, batch=1, seqlen_q=600,
                                                 seqlen_k=600, topk=0, mask_mode=3,
                                                 seed=63)))
+    # rows wider than 4096 columns: zero-filled rows, values stored directly,
+    # the next row's index list loaded into the other buffer
+    cs.append(("bsnd_bf16_g128_w5000", with_lengths(
+        C.gen("tiny", heads_q=128, batch=1, seqlen_q=2 * len(LENGTHS), seqlen_k=5000,
+              topk=1024, mask_mode=0, seed=64), seed=3)))
+    l2k = lengths(64, 2048)
+    cs.append(("tnd_fp16_g100_w6000_k2048", with_lengths(
+        C.gen("tnd_varlen", heads_q=100, topk=2048, mask_mode=0, seqlens_q=(70, 30, 50),
+              seqlens_k=(2100, 2500, 1400), seed=65), seed=4, lens=l2k)))
+    # dense TND rows of a 4700-column output: sequences of different causal
+    # squares, one of them with no visible key for its first rows
+    cs.append(("dense_tnd_g128_w4700", C.gen(
+        "tnd_varlen", heads_q=128, topk=0, mask_mode=3, seqlens_q=(60, 40, 30),
+        seqlens_k=(2000, 2650, 20), cmp_ratio=1, seed=66)))
+    # K-wide dense rows of 5000 entries (entry t at column t)
+    cs.append(("kw_dense_bsnd_g128_w5000", C.as_kwide(C.gen(
+        "tiny", heads_q=128, batch=1, seqlen_q=60, seqlen_k=5000, topk=0, mask_mode=3,
+        seed=73))))
+    # up to 64 heads: 32-key tiles, rows of up to 2048 indices assembled in
+    # LDS, longer rows stored directly
+    l32 = lengths(32, 1024, extra=(1500, 2047, 2048))
+    cs.append(("bsnd_bf16_g16_k2048", with_lengths(
+        C.gen("tiny", heads_q=16, batch=2, seqlen_q=len(l32), seqlen_k=2100, topk=2048,
+              mask_mode=0, seed=67), seed=5, lens=l32)))
+    cs.append(("tnd_fp16_g33_k2048", with_lengths(
+        C.gen("tnd_varlen", heads_q=33, topk=2048, mask_mode=0, seqlens_q=(len(l32), 80),
+              seqlens_k=(2200, 3000), dtype="fp16", seed=68), seed=6, lens=l32)))
+    cs.append(("bsnd_fp16_g64_k2048", with_lengths(
+        C.gen("tiny", heads_q=64, batch=1, seqlen_q=len(l2k), seqlen_k=2048, topk=2048,
+              mask_mode=0, dtype="fp16", seed=69), seed=7, lens=l2k)))
+    l3k = lengths(32, 2600, extra=(2599, 2600)) [::3] + [2600, 2599, 0]
+    cs.append(("bsnd_bf16_g64_k2600", with_lengths(
+        C.gen("tiny", heads_q=64, batch=1, seqlen_q=len(l3k), seqlen_k=2700, topk=2600,
+              mask_mode=0, seed=70), seed=8, lens=sorted(set(l3k)))))
+    cs.append(("tnd_bf16_g16_k3000", with_lengths(
+        C.gen("tnd_varlen", heads_q=16, topk=3000, mask_mode=0, seqlens_q=(90, 60),
+              seqlens_k=(3100, 3500), seed=71), seed=9,
+        lens=lengths(32, 3000)[::4] + [3000])))
+    cs.append(("bsnd_bf16_g128_k2600", with_lengths(
+        C.gen("tiny", heads_q=128, batch=1, seqlen_q=80, seqlen_k=2700, topk=2600,
+              mask_mode=0, seed=72), seed=10, lens=lengths(32, 2600)[::5] + [2600])))
     return cs
 
 
@@ -87,13 +147,13 @@ def test_tile_counts(smla, case, budget):
         topk=p.topk, layout_q=p.layout, layout_k=p.layout, mask_mode=p.mask_mode,
         cmp_ratio=p.cmp_ratio, device=0, core_budget=budget)
     print(f"[tiles] {name} layout={p.layout} R={p.rows} G={p.groups} K={p.topk} "
-          f"workgroups={int(md[4])}", flush=True)
+          f"W={p.out_width} workgroups={int(md[4])}", flush=True)
     o = smla.smla_softmax_l1norm(
         p.q.cuda(), p.k.cuda(), _t(np.asarray(p.softmax_lse, dtype=np.float32)),
         sparse_indices=_t(p.sparse_indices), cu_seqlens_q=_t(p.cu_seqlens_q),
         cu_seqlens_k=_t(p.cu_seqlens_k), topk_length=_t(p.topk_length), metadata=md,
         softmax_scale=p.softmax_scale, max_seqlen_k=p.max_seqlen_k, cmp_ratio=p.cmp_ratio,
-        mask_mode=p.mask_mode, layout_q=p.layout, layout_k=p.layout)
+        mask_mode=p.mask_mode, layout_q=p.layout, layout_k=p.layout, kwide=p.kwide)
     torch.cuda.synchronize()
     o = o.reshape(p.rows, p.out_width).cpu().numpy()
     err = np.abs(o.astype(np.float64) - e.astype(np.float64))
