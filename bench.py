@@ -42,7 +42,7 @@ import numpy as np
 
 PEAK_MFMA_TFLOPS = {"bf16": 2500.0, "fp16": 2500.0}   # MI355X dense, published
 PEAK_HBM_GBPS = 8000.0                                  # MI355X HBM3E, published
-KERNELS = {0: "smla_l1norm_kernel", 1: "smla_wide_kernel"}  # metadata field 24
+KERNELS = {0: "smla_l1norm_kernel", 1: "smla_wide_kernel", 2: "smla_narrow_kernel"}  # field 24
 HERE = os.path.dirname(os.path.abspath(__file__))
 KERNEL_SOURCE = os.path.join(HERE, "sparse_mla_attention_02_amd", "csrc", "smla_kernels.hip")
 

@@ -80,10 +80,12 @@ enum { SMLA_MASK_NONE = 0, SMLA_MASK_RIGHT_DOWN_CAUSAL = 3 };
  *   [19] row order (1 = snake: workgroup w takes rows w, 2C-1-w, 2C+w, ...),
  *   [20] head tiles per row (kernel variant), [21] device, [22] CU count,
  *   [23] resident workgroups per CU,
- *   [24] kernel: 0 = general (one wave per 32-head tile, two workgroups
- *        per CU), 1 = pipelined (65..128 heads with topk <= 2048 or the
- *        dense case: one 4-wave workgroup per CU, 64 heads per wave,
- *        64-key tiles);
+ *   [24] kernel: 0 = general (65..128 heads with topk > 2048: one wave
+ *        per 32-head tile, two workgroups per CU), 1 = pipelined for
+ *        65..128 heads (topk <= 2048 or the dense case: one 4-wave
+ *        workgroup per CU, 64 heads per wave, 64-key tiles), 2 = pipelined
+ *        for up to 64 heads (any topk or the dense case: one 4-wave
+ *        workgroup per CU, every head and 16 keys per wave);
  *   [25] the longest key sequence (BSND: S2; TND: the longest
  *        cu_seqlens_k step);
  *        [26..63] zero.

@@ -41,16 +41,17 @@ smla_status_t ok() {
     return SMLA_SUCCESS;
 }
 
-// Per (device, head tiles, layout, pipelined kernel): CU count and
+// Per (device, head tiles, layout, kernel variant): CU count and
 // co-resident workgroups per CU, queried once.
 std::mutex g_cap_mu;
-std::map<std::tuple<int, int, bool, bool>, std::pair<int, int>> g_cap;
+std::map<std::tuple<int, int, bool, int>, std::pair<int, int>> g_cap;
 
-hipError_t device_capacity(int device, int ht, bool tnd, int64_t topk, int* cus, int* per_cu) {
-    const bool pipe = smla::uses_pipe(ht, topk);
+hipError_t device_capacity(int device, int ht, bool tnd, int64_t G, int64_t topk, int* cus,
+                           int* per_cu) {
+    const int variant = smla::kernel_variant(G, topk);
     {
         std::lock_guard<std::mutex> lk(g_cap_mu);
-        auto it = g_cap.find({device, ht, tnd, pipe});
+        auto it = g_cap.find({device, ht, tnd, variant});
         if (it != g_cap.end()) {
             *cus = it->second.first;
             *per_cu = it->second.second;
@@ -65,12 +66,12 @@ hipError_t device_capacity(int device, int ht, bool tnd, int64_t topk, int* cus,
     if (e != hipSuccess) return e;
     if (cur != device && (e = hipSetDevice(device)) != hipSuccess) return e;
     int occ = 0;
-    e = smla::resident_per_cu(ht, true, tnd, topk, &occ);
+    e = smla::resident_per_cu(ht, true, tnd, G, topk, &occ);
     if (cur != device) (void)hipSetDevice(cur);
     if (e != hipSuccess) return e;
     if (occ <= 0) return hipErrorInvalidConfiguration;
     std::lock_guard<std::mutex> lk(g_cap_mu);
-    g_cap[{device, ht, tnd, pipe}] = {n, occ};
+    g_cap[{device, ht, tnd, variant}] = {n, occ};
     *cus = n;
     *per_cu = occ;
     return hipSuccess;
@@ -84,6 +85,12 @@ constexpr int64_t kHeadDim = 512;
 constexpr int64_t kMaxKeysPerSeq = int64_t(1) << 21;
 constexpr int64_t kMaxTopk = int64_t(1) << 24;
 constexpr int64_t kMaxWidth = 0x1FFFFFFC;
+
+const char* kernel_name(int variant) {
+    return variant == smla::kKernelNarrow ? "smla_narrow_kernel"
+           : variant == smla::kKernelWide ? "smla_wide_kernel"
+                                           : "smla_l1norm_kernel";
+}
 
 // SMLA_LOG=1: one line on stderr per metadata call and per launch.
 bool log_on() {
@@ -280,8 +287,8 @@ smla_status_t smla_l1norm_metadata(
     int cus = 0, per_cu = 0;
     int64_t budget = core_budget;
     if (core_budget == 0) {
-        hipError_t e =
-            device_capacity(device, ht, layout_q == SMLA_LAYOUT_TND, topk, &cus, &per_cu);
+        hipError_t e = device_capacity(device, ht, layout_q == SMLA_LAYOUT_TND,
+                                       num_heads_q / num_heads_k, topk, &cus, &per_cu);
         if (e != hipSuccess)
             return fail(SMLA_ERR_RUNTIME, "device %d capacity query failed: %s", device,
                         hipGetErrorString(e));
@@ -319,7 +326,7 @@ smla_status_t smla_l1norm_metadata(
     m[21] = device;
     m[22] = cus;
     m[23] = per_cu;
-    m[24] = smla::uses_pipe(ht, topk) ? 1 : 0;  // kernel variant
+    m[24] = smla::kernel_variant(num_heads_q / num_heads_k, topk);  // kernel variant
     m[25] = (int32_t)longest_k;
     if (log_on())
         std::fprintf(stderr,
@@ -329,7 +336,7 @@ smla_status_t smla_l1norm_metadata(
                      layout_q == SMLA_LAYOUT_TND ? "TND" : "BSND", (long long)R,
                      (long long)num_heads_q, (long long)topk, (long long)mask_mode,
                      (long long)cmp_ratio, (long long)rows_k, (long long)longest_k, m[4],
-                     m[1], m[2], m[3], m[24] ? "pipelined" : "general", cus, per_cu);
+                     m[1], m[2], m[3], kernel_name(m[24]), cus, per_cu);
     return ok();
 }
 
@@ -513,9 +520,9 @@ smla_status_t run_main(const char* call, const smla::KernelArgs& a, int32_t dtyp
         if (st != SMLA_SUCCESS) return st;
     }
     const int ht = smla::head_tiles_for(a.G);
-    const bool pipe = smla::uses_pipe(ht, a.dense ? 0 : a.K);
-    log_launch(call, a, ht, dtype, pipe ? "smla_wide_kernel" : "smla_l1norm_kernel",
-               a.num_wg, pipe ? 256 : 64 * ht, stream);
+    const int variant = smla::kernel_variant(a.G, a.dense ? 0 : a.K);
+    log_launch(call, a, ht, dtype, kernel_name(variant), a.num_wg,
+               variant == smla::kKernelGeneral ? 64 * ht : 256, stream);
     hipError_t e = smla::launch(a, ht, dtype == SMLA_DTYPE_BF16, layout_q == SMLA_LAYOUT_TND,
                                 s);
     if (e != hipSuccess)

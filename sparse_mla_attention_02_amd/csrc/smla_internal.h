@@ -43,12 +43,18 @@ inline int head_tiles_for(int64_t G) { return G <= 32 ? 1 : (G <= 64 ? 2 : 4); }
 hipError_t launch(const KernelArgs& a, int head_tiles, bool bf16, bool tnd,
                   hipStream_t stream);
 
-// Whether rows of (head_tiles, topk) run on the pipelined one-workgroup-per-CU
-// kernel (otherwise on the general kernel).
-bool uses_pipe(int head_tiles, int64_t topk);
+// The main call's kernels (metadata field 24): the general kernel (one wave
+// per 32-head tile), the pipelined kernel for 65..128 heads (64 heads per
+// wave, 64-key tiles, index list in LDS), the pipelined kernel for up to 64
+// heads (every head per wave, 16 keys per wave).
+enum { kKernelGeneral = 0, kKernelWide = 1, kKernelNarrow = 2 };
 
-// Co-resident workgroups per CU of the variant used for (head_tiles, topk).
-hipError_t resident_per_cu(int head_tiles, bool bf16, bool tnd, int64_t topk, int* out);
+// The kernel that runs rows of G heads with `topk` indices (0: dense).
+int kernel_variant(int64_t G, int64_t topk);
+
+// Co-resident workgroups per CU of the kernel used for (G, topk).
+hipError_t resident_per_cu(int head_tiles, bool bf16, bool tnd, int64_t G, int64_t topk,
+                           int* out);
 
 // The forward softmax_lse kernel: a.out receives (R, G) fp32.
 hipError_t launch_lse(const KernelArgs& a, int head_tiles, bool bf16, bool tnd,

@@ -110,8 +110,9 @@ def test_metadata_fields_follow_page_formulas(total, budget):
     assert (m[26:] == 0).all()
 
 
-@pytest.mark.parametrize("heads,topk,variant", [(128, 2048, 1), (65, 64, 1), (64, 2048, 0),
-                                                (128, 2049, 0), (1, 16, 0)])
+@pytest.mark.parametrize("heads,topk,variant", [(128, 2048, 1), (65, 64, 1), (64, 2048, 2),
+                                                (128, 2049, 0), (1, 16, 2), (64, 5000, 2),
+                                                (16, 0, 2), (100, 0, 1)])
 def test_metadata_names_the_kernel_variant(heads, topk, variant):
     m = meta(num_heads_q=heads, topk=topk).numpy()
     assert m[24] == variant
