@@ -2110,6 +2110,8 @@ __global__ __launch_bounds__(256, 1) void smla_narrow_kernel(KernelArgs a) {
                     // row start's) may be in flight; everything older (tile
                     // t+1's rows among them) has landed
                     waitcnt_vm_lgkm0<kTileLoads>();
+                    if constexpr (more) jg = idx_read(ip & 3);
+                    js = idx_read(kJsSlot0 + ((t - 1) & 3));
                 }
                 // operands of tile t+1: four reads per step in steps 0..3
                 if (s < 4 && more) {
@@ -2155,19 +2157,18 @@ __global__ __launch_bounds__(256, 1) void smla_narrow_kernel(KernelArgs a) {
                     } else if (s == 11) {
                         val = tot * a.inv_g;
                         pin(val);
-                    } else if (s == 12) {
-                        js = idx_read(kJsSlot0 + ((t - 1) & 3));
-                        pin_v(js);
                     }
                 }
-                // row offsets of this tile's load: indices read in step 5,
-                // offsets in step 6; two scalar offsets per step from step 7
-                // on, one step before their loads
+                // the indices of this tile's load and of tile t-1's stores
+                // (landed at the wait of step 0) are read in step 0, before
+                // the operand reads, and used steps later: an index read used
+                // right after it is issued waits for it (and every LDS read
+                // in flight) there (not pinned, for the same reason)
+                // row offsets of this tile's load in step 6; two scalar
+                // offsets per step from step 7 on, one step before their
+                // loads
                 if (more && b == (NB == 4 ? 1 : 3)) {
-                    if (s == 5) {
-                        jg = idx_read(ip & 3);
-                        pin_v(jg);
-                    } else if (s == 6) {
+                    if (s == 6) {
                         ov = elem_off(E, jg);
                         pin_v(ov);
                     }
