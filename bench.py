@@ -31,7 +31,6 @@ the timed region (null where amdsmi cannot read it).
 from __future__ import annotations
 
 import argparse
-import hashlib
 import json
 import os
 import sys
@@ -44,7 +43,6 @@ PEAK_MFMA_TFLOPS = {"bf16": 2500.0, "fp16": 2500.0}   # MI355X dense, published
 PEAK_HBM_GBPS = 8000.0                                  # MI355X HBM3E, published
 KERNELS = {0: "smla_l1norm_kernel", 1: "smla_wide_kernel", 2: "smla_narrow_kernel"}  # field 24
 HERE = os.path.dirname(os.path.abspath(__file__))
-KERNEL_SOURCE = os.path.join(HERE, "sparse_mla_attention_02_amd", "csrc", "smla_kernels.hip")
 
 
 def log(msg):
@@ -71,7 +69,7 @@ def measured_traffic(kernel, workload):
     """HBM bytes per launch from the committed rocprofv3 counter summary
     profiles/<kernel>_<workload>_hbm_traffic.md (FETCH_SIZE + WRITE_SIZE,
     each scaled by the same counter's reading for a copy of known size), or
-    None when there is none or the kernel source has changed since."""
+    None when there is none or the kernel's source files have changed since."""
     path = os.path.join(HERE, "profiles", f"{kernel}_{workload}_hbm_traffic.md")
     if not os.path.exists(path):
         return None
@@ -83,9 +81,8 @@ def measured_traffic(kernel, workload):
                     "kernel_source_sha256", "fetch_bytes_per_launch", "write_bytes_per_launch"):
                 k, v = line.split(":", 1)
                 fields[k] = v.strip()
-    with open(KERNEL_SOURCE, "rb") as f:
-        sha = hashlib.sha256(f.read()).hexdigest()
-    if fields.get("kernel_source_sha256") != sha:
+    from sparse_mla_attention_02_amd import _build
+    if fields.get("kernel_source_sha256") != _build.kernel_source_sha256(kernel):
         return None
     try:
         return int(fields["fetch_bytes_per_launch"]) + int(fields["write_bytes_per_launch"])

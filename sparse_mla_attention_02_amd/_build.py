@@ -25,27 +25,52 @@ COMMON = ["--offload-arch=" + ARCH, "-O3", "-std=c++17", "-fPIC",
           # keep the compiler from forming packed fp32 VALU instructions
           "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
           "-Wall", "-Wno-unused-command-line-argument", "-I", INCLUDE, "-I", CSRC]
-KERNELS = os.path.join(CSRC, "smla_kernels.hip")
-HOST = os.path.join(CSRC, "smla_host.cpp")
+# (source, extra hipcc flags): the pipelined and general kernels keep MFMA
+# results in VGPRs (-amdgpu-mfma-vgpr-form), so that their epilogues read the
+# scores without a copy; the softmax_lse kernel, with one 32-head block per
+# wave, is faster with the compiler's default
+VGPR_FORM = ["-mllvm", "-amdgpu-mfma-vgpr-form"]
+SOURCES = [
+    ("smla_wide.hip", VGPR_FORM),
+    ("smla_narrow.hip", VGPR_FORM),
+    ("smla_general.hip", VGPR_FORM),
+    ("smla_lse.hip", []),
+    ("smla_dispatch.cpp", []),
+    ("smla_host.cpp", []),
+]
+# the source files of each kernel (its own file and the shared device code)
+KERNEL_SOURCES = {
+    "smla_wide_kernel": ("smla_wide.hip", "smla_device.h", "smla_internal.h"),
+    "smla_narrow_kernel": ("smla_narrow.hip", "smla_device.h", "smla_internal.h"),
+    "smla_l1norm_kernel": ("smla_general.hip", "smla_device.h", "smla_internal.h"),
+    "smla_lse_kernel": ("smla_lse.hip", "smla_device.h", "smla_internal.h"),
+}
 EXAMPLE_SRC = os.path.join(CSRC, "example", "smla_example.cpp")
 EXAMPLE = os.path.join(PKG, "smla_example")
 
 
-def commands(out: str, tmp: str) -> list:
-    """The compile and link commands: the kernel file twice (the pipelined and
-    general kernels with MFMA results in VGPRs, so that the pipelined kernel's
-    epilogue reads its scores without a copy; the softmax_lse kernel with the
-    compiler's default), the host code once, then one shared library."""
-    main_o = os.path.join(tmp, "kernels.o")
-    lse_o = os.path.join(tmp, "kernels_lse.o")
-    host_o = os.path.join(tmp, "host.o")
+def kernel_source_sha256(kernel: str) -> str:
+    """sha256 over the source files of one kernel, in a fixed order."""
+    import hashlib
+    h = hashlib.sha256()
+    for name in KERNEL_SOURCES[kernel]:
+        with open(os.path.join(CSRC, name), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
+
+
+def commands(out: str, tmp: str) -> tuple:
+    """The compile commands (independent of each other) and the link
+    command of the shared library."""
     cc = hipcc()
-    return [
-        [cc, *COMMON, "-mllvm", "-amdgpu-mfma-vgpr-form", "-x", "hip", "-c", KERNELS, "-o", main_o],
-        [cc, *COMMON, "-DSMLA_LSE_TU", "-x", "hip", "-c", KERNELS, "-o", lse_o],
-        [cc, *COMMON, "-x", "hip", "-c", HOST, "-o", host_o],
-        [cc, "--offload-arch=" + ARCH, "-shared", "-fPIC", main_o, lse_o, host_o, "-o", out],
-    ]
+    compiles, objs = [], []
+    for src, extra in SOURCES:
+        obj = os.path.join(tmp, os.path.splitext(src)[0] + ".o")
+        compiles.append([cc, *COMMON, *extra, "-x", "hip", "-c", os.path.join(CSRC, src),
+                         "-o", obj])
+        objs.append(obj)
+    link = [cc, "--offload-arch=" + ARCH, "-shared", "-fPIC", *objs, "-o", out]
+    return compiles, link
 
 
 def _run(cmd, verbose):
@@ -72,9 +97,13 @@ def build(verbose: bool = False) -> str:
     (always recompiles)."""
     import tempfile
     out = LIB + ".tmp%d" % os.getpid()
+    from concurrent.futures import ThreadPoolExecutor
     with tempfile.TemporaryDirectory(prefix="smla_build_") as tmp:
-        for cmd in commands(out, tmp):
-            _run(cmd, verbose)
+        compiles, link = commands(out, tmp)
+        with ThreadPoolExecutor(max_workers=min(len(compiles), os.cpu_count() or 1)) as ex:
+            for f in [ex.submit(_run, c, verbose) for c in compiles]:
+                f.result()
+        _run(link, verbose)
     os.replace(out, LIB)
     exe = EXAMPLE + ".tmp%d" % os.getpid()
     _run(example_command(exe), verbose)

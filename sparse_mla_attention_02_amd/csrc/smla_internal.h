@@ -56,6 +56,19 @@ int kernel_variant(int64_t G, int64_t topk);
 hipError_t resident_per_cu(int head_tiles, bool bf16, bool tnd, int64_t G, int64_t topk,
                            int* out);
 
+// Most indices per row that the pipelined kernel for 65..128 heads takes (its
+// index list sits in LDS); longer rows take the general kernel.
+constexpr int kWideIndexCap = 2048;
+
+// The three kernels of the main call, one source file each.
+hipError_t launch_general(const KernelArgs& a, int head_tiles, bool bf16, bool tnd,
+                          hipStream_t stream);
+hipError_t general_resident_per_cu(int head_tiles, bool bf16, bool tnd, int* out);
+hipError_t launch_wide(const KernelArgs& a, bool bf16, bool tnd, hipStream_t stream);
+hipError_t wide_resident_per_cu(bool bf16, bool tnd, int* out);
+hipError_t launch_narrow(const KernelArgs& a, bool bf16, bool tnd, hipStream_t stream);
+hipError_t narrow_resident_per_cu(bool bf16, bool tnd, int* out);
+
 // The forward softmax_lse kernel: a.out receives (R, G) fp32.
 hipError_t launch_lse(const KernelArgs& a, int head_tiles, bool bf16, bool tnd,
                       hipStream_t stream);

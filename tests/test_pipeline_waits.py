@@ -38,7 +38,7 @@ import random
 import re
 
 KERNEL = os.path.join(os.path.dirname(__file__), os.pardir, "sparse_mla_attention_02_amd",
-                      "csrc", "smla_kernels.hip")
+                      "csrc", "smla_device.h")
 IDX_OPS = 8          # loads of one index list per wave
 ROW_START_LATER = 7  # tile 1's first rows, left in flight at a row start
 BAR_STEP = 24
