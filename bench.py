@@ -391,7 +391,12 @@ def main():
     else:
         roof = {"bound": "hbm", "achieved": round(k_gbps, 1), "peak": PEAK_HBM_GBPS,
                 "unit": "GB/s", "frac": round(k_gbps / PEAK_HBM_GBPS, 4)}
-    kernel = "smla_lse_kernel" if args.op == "lse" else KERNELS.get(int(md[24]), "unknown")
+    if args.op == "lse":
+        # 65..128 heads with at most 2048 indices (or dense): the pipelined kernel
+        pipe = p.groups > 64 and (p.sparse_indices is None or p.topk <= 2048)
+        kernel = "smla_lse_wide_kernel" if pipe else "smla_lse_kernel"
+    else:
+        kernel = KERNELS.get(int(md[24]), "unknown")
     # (the committed counter summaries cover the S2-wide main call and the lse call)
     roof["traffic"] = None if p.kwide else measured_traffic(kernel, p.name)
     roof["kernel"] = kernel

@@ -375,6 +375,24 @@ __device__ __forceinline__ void dma_dword(i32x4_t desc, uint32_t m0, int32_t sof
         : "memory", "m0");
 }
 
+// Lanes of accumulator element e that hold a used entry, as a wave mask:
+// lanes 0..31 hold slot k = 8*(e/4) + e%4 of the tile, lanes 32..63 slot
+// k + 4, and bit kk of the wave-uniform `slots` says slot kk is used. The
+// mask is built by the scalar unit.
+__device__ __forceinline__ uint64_t used_lanes(uint32_t slots, int e) {
+    const int k = 8 * (e >> 2) + (e & 3);
+    const uint64_t lo = ((slots >> k) & 1u) ? 0x00000000ffffffffull : 0ull;
+    const uint64_t hi = ((slots >> (k + 4)) & 1u) ? 0xffffffff00000000ull : 0ull;
+    return lo | hi;
+}
+
+// (lane in m) ? a : b, with the lane mask in a scalar register pair
+__device__ __forceinline__ float select_lanes(uint64_t m, float a, float b) {
+    float r;
+    asm("v_cndmask_b32_e64 %0, %1, %2, %3" : "=v"(r) : "v"(b), "v"(a), "s"(m));
+    return r;
+}
+
 constexpr int kRowBytes = kPitch * 16;          // one key row in LDS
 
 }  // namespace

@@ -532,20 +532,21 @@ smla_status_t run_main(const char* call, const smla::KernelArgs& a, int32_t dtyp
 
 // Co-resident workgroups per CU of the lse kernel, queried once per variant.
 std::mutex g_lse_occ_mu;
-std::map<std::tuple<int, bool, bool>, int> g_lse_occ;
+std::map<std::tuple<int, bool, bool, bool>, int> g_lse_occ;  // (ht, bf16, tnd, pipelined)
 
-hipError_t lse_capacity(int ht, bool bf16, bool tnd, int* per_cu) {
+hipError_t lse_capacity(int ht, bool bf16, bool tnd, int64_t G, int64_t topk, int* per_cu) {
     std::lock_guard<std::mutex> lk(g_lse_occ_mu);
-    auto it = g_lse_occ.find({ht, bf16, tnd});
+    const bool pipe = smla::lse_pipelined(G, topk);
+    auto it = g_lse_occ.find({ht, bf16, tnd, pipe});
     if (it != g_lse_occ.end()) {
         *per_cu = it->second;
         return hipSuccess;
     }
     int occ = 0;
-    hipError_t e = smla::lse_resident_per_cu(ht, bf16, tnd, &occ);
+    hipError_t e = smla::lse_resident_per_cu(ht, bf16, tnd, G, topk, &occ);
     if (e != hipSuccess) return e;
     if (occ <= 0) return hipErrorInvalidConfiguration;
-    g_lse_occ[{ht, bf16, tnd}] = occ;
+    g_lse_occ[{ht, bf16, tnd, pipe}] = occ;
     *per_cu = occ;
     return hipSuccess;
 }
@@ -627,14 +628,15 @@ smla_status_t smla_softmax_lse(
     const int32_t* m = metadata_host;
     if (m[22] > 0) {
         int per_cu = 0;
-        hipError_t e = lse_capacity(ht, bf16, tnd, &per_cu);
+        hipError_t e = lse_capacity(ht, bf16, tnd, a.G, a.dense ? 0 : a.K, &per_cu);
         if (e != hipSuccess)
             return fail(SMLA_ERR_RUNTIME, "occupancy query failed: %s", hipGetErrorString(e));
         const int64_t cap = (int64_t)m[22] * per_cu;
         a.num_wg = (int32_t)(a.R < cap ? a.R : cap);
     }
-    log_launch("smla_softmax_lse", a, ht, dtype, "smla_lse_kernel", a.num_wg,
-               64 * (ht == 4 ? 2 : ht), stream);
+    const bool pipe = smla::lse_pipelined(a.G, a.dense ? 0 : a.K);
+    log_launch("smla_softmax_lse", a, ht, dtype, pipe ? "smla_lse_wide_kernel" : "smla_lse_kernel",
+               a.num_wg, pipe ? 256 : 64 * (ht == 4 ? 2 : ht), stream);
     hipError_t e = smla::launch_lse(a, ht, bf16, tnd, static_cast<hipStream_t>(stream));
     if (e != hipSuccess)
         return fail(SMLA_ERR_RUNTIME, "kernel launch failed: %s", hipGetErrorString(e));

@@ -1,5 +1,7 @@
 // Forward softmax_lse kernel for gfx950 (the input the Softmax-L1Norm
-// operation consumes), over the same used entries as the main call.
+// operation consumes), over the same used entries as the main call: the
+// general kernel, for rows the pipelined one (smla_lse_wide.hip) does not
+// take (up to 64 heads, or more than 2048 indices).
 //
 // Built without -amdgpu-mfma-vgpr-form: with one 32-head block per wave it
 // measured 9% slower with MFMA results in VGPRs.
@@ -125,24 +127,6 @@ __device__ __forceinline__ void lse_update(const f32x16_t& acc, uint32_t used, f
     for (int e = 0; e < 16; ++e) sum += __builtin_amdgcn_exp2f(x[e] - base);
     m = mn;
     l = sum;
-}
-
-// Lanes of accumulator element e that hold a used entry, as a wave mask:
-// lanes 0..31 hold slot k = 8*(e/4) + e%4 of the tile, lanes 32..63 slot
-// k + 4, and bit kk of the wave-uniform `slots` says slot kk is used. The
-// mask is built by the scalar unit.
-__device__ __forceinline__ uint64_t used_lanes(uint32_t slots, int e) {
-    const int k = 8 * (e >> 2) + (e & 3);
-    const uint64_t lo = ((slots >> k) & 1u) ? 0x00000000ffffffffull : 0ull;
-    const uint64_t hi = ((slots >> (k + 4)) & 1u) ? 0xffffffff00000000ull : 0ull;
-    return lo | hi;
-}
-
-// (lane in m) ? a : b, with the lane mask in a scalar register pair
-__device__ __forceinline__ float select_lanes(uint64_t m, float a, float b) {
-    float r;
-    asm("v_cndmask_b32_e64 %0, %1, %2, %3" : "=v"(r) : "v"(b), "v"(a), "s"(m));
-    return r;
 }
 
 // Lazy step of the online log-sum-exp: against the lane's current base b
@@ -414,10 +398,12 @@ hipError_t occupancy_lse_t(int* out) {
 }  // namespace
 
 hipError_t launch_lse(const KernelArgs& a, int ht, bool bf16, bool tnd, hipStream_t stream) {
+    if (lse_pipelined(a.G, a.dense ? 0 : a.K)) return launch_lse_wide(a, bf16, tnd, stream);
     SMLA_DISPATCH(launch_lse_t, a, stream);
 }
 
-hipError_t lse_resident_per_cu(int ht, bool bf16, bool tnd, int* out) {
+hipError_t lse_resident_per_cu(int ht, bool bf16, bool tnd, int64_t G, int64_t topk, int* out) {
+    if (lse_pipelined(G, topk)) return lse_wide_resident_per_cu(bf16, tnd, out);
     SMLA_DISPATCH(occupancy_lse_t, out);
 }
 

@@ -168,3 +168,25 @@ def test_lse_score_jump(smla, heads):
     d = np.abs(got.astype(np.float64) - want.astype(np.float64))
     assert (d <= 2e-5 * np.maximum(1.0, np.abs(want))).all(), float(d.max())
     assert np.abs(want).max() > 50  # the jump is really there
+
+
+@pytest.mark.parametrize("heads", [16, 128])
+def test_lse_scores_far_below_zero(smla, heads):
+    """Every score about -370 in log2 units (q all ones, every key near all
+    minus ones, scale 0.5): far below any fixed starting base, so the sums
+    must rebase downwards instead of underflowing to an lse of -inf. The
+    bar is relative, as for the score jump: |d| <= 2e-5 * max(1, |lse|)."""
+    p = C.gen("tiny", heads_q=heads, batch=1, seqlen_q=8, seqlen_k=300, topk=256, mask_mode=0,
+              seed=64)
+    p.q.fill_(1.0)
+    kk = p.k.reshape(-1, p.head_dim)
+    kk.copy_((-1.0 + 0.01 * torch.randn(kk.shape, generator=torch.Generator().manual_seed(5)))
+             .to(kk.dtype))
+    p.softmax_scale = 0.5
+    say(f"[lse] scores far below zero, G={heads}")
+    want, _ = oracle.lse(p)
+    got = run_lse(smla, p)
+    assert np.isfinite(want).all() and (want < -200).all()  # the case is really there
+    assert np.isfinite(got).all()
+    d = np.abs(got.astype(np.float64) - want.astype(np.float64))
+    assert (d <= 2e-5 * np.maximum(1.0, np.abs(want))).all(), float(d.max())
