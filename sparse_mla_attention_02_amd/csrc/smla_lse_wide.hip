@@ -57,14 +57,19 @@ __device__ __forceinline__ void lse_combine(float m, float l, float m2, float l2
 // operand from the ring), the ring read 8 steps ahead, the gather loads of
 // this wave's rows of later tiles (rows 7..15 of tile t+1 at steps 1..9,
 // rows 0..6 of tile t+2 at steps 25..31) and element s of the previous
-// tile's epilogue: in the first gap y = x - B, masked to -inf for an unused
-// entry (elements 0..15 are block 0's, 16..31 block 1's), and the sum of the
-// previous element's 2^y; in the second gap the maximum of y and 2^y. The
-// tile's workgroup barrier follows step 24's MFMAs (every wave has then read
-// its last operand of this tile and has its rows of the next one landed).
-// Bit 8 (e / 4) + 4 h + e % 4 of `pslots` says whether the previous tile's
-// element e of half h is a used entry.
-template <bool BF16, typename Mid2>
+// tile's epilogue, y = x - B of element e (elements 0..15 are block 0's,
+// 16..31 block 1's), its maximum and the sum of its 2^y. With MASK, y is set
+// to -inf for an unused entry: bit 8 (e / 4) + 4 h + e % 4 of `pslots` says
+// whether the previous tile's element e of half h is a used entry. The
+// masks fill the first gap, so that variant puts y of element s and the
+// term of element s - 1 in the first gap, the maximum and 2^y in the
+// second. Without MASK (every entry of the previous tile used) the first
+// gap holds the whole epilogue: y of element s, the maximum and 2^y of
+// element s - 1, the term of element s - 2; the second keeps the operand
+// read, the gather load and its wait. The tile's workgroup barrier follows
+// step 24's MFMAs (every wave has then read its last operand of this tile
+// and has its rows of the next one landed).
+template <bool BF16, bool MASK, typename Mid2>
 __device__ __forceinline__ void lse_tile(const uint4* __restrict__ cur,
                                          const uint4* __restrict__ nxt, uint4 (&ring)[8],
                                          const uint4* qa0, const uint4* qa1,
@@ -80,8 +85,15 @@ __device__ __forceinline__ void lse_tile(const uint4* __restrict__ cur,
     constexpr float kNegInf = -__builtin_inff();
     acc0 = f32x16_t{};
     acc1 = f32x16_t{};
-    const float nb0 = -b0, nb1 = -b1;
-    float y = 0.0f, ex = 0.0f;
+    float nb0 = -b0, nb1 = -b1;
+    // (each variant marks its negated bases with its own empty asm, so that
+    // the two variants' shifts are not one computation that the compiler
+    // could hoist above the branch choosing between them)
+    if (MASK)
+        asm volatile("; masked" : "+v"(nb0), "+v"(nb1));
+    else
+        asm volatile("; unmasked" : "+v"(nb0), "+v"(nb1));
+    float y = 0.0f, ex = 0.0f;  // y of the latest element, 2^y of the one before
     ymax0 = kNegInf;
     ymax1 = kNegInf;
     sum0 = 0.0f;
@@ -92,21 +104,34 @@ __device__ __forceinline__ void lse_tile(const uint4* __restrict__ cur,
         __builtin_amdgcn_sched_barrier(0);
         acc0 = mfma_32x32x16<BF16>(ring[s & 7], qa0[s], acc0);
         asm volatile("" ::"v"(acc0));
-        // first gap: element s, shifted by its block's base and masked, and
-        // the previous element's term
+        // first gap: y of element s (masked); the term of element s - 1
+        // (with MASK) or s - 2 (without), and without MASK the maximum and
+        // 2^y of element s - 1
+        const int ls = MASK ? s - 1 : s - 2;  // element whose term is added
+        if (ls >= 0 && ls < 16) {
+            sum0 += ex;
+            pin(sum0);
+        } else if (ls >= 16) {
+            sum1 += ex;
+            pin(sum1);
+        }
+        if (!MASK && s >= 1) {
+            if (s - 1 < 16) {
+                ymax0 = max_f32(ymax0, y);
+                pin(ymax0);
+            } else {
+                ymax1 = max_f32(ymax1, y);
+                pin(ymax1);
+            }
+            ex = __builtin_amdgcn_exp2f(y);
+            pin(ex);
+        }
         {
             const int e = s & 15;
             const float x = s < 16 ? prev0[e] : prev1[e];
-            y = select_lanes(used_lanes(pslots, e), __builtin_fmaf(x, c, s < 16 ? nb0 : nb1),
-                             kNegInf);
+            y = __builtin_fmaf(x, c, s < 16 ? nb0 : nb1);
+            if (MASK) y = select_lanes(used_lanes(pslots, e), y, kNegInf);
             pin(y);
-        }
-        if (s >= 1 && s <= 16) {
-            sum0 += ex;
-            pin(sum0);
-        } else if (s > 16) {
-            sum1 += ex;
-            pin(sum1);
         }
         if (s <= 8) {
             soa[s & 1] = __builtin_amdgcn_readlane(offa, s + 7);
@@ -118,17 +143,19 @@ __device__ __forceinline__ void lse_tile(const uint4* __restrict__ cur,
         __builtin_amdgcn_sched_barrier(0);
         acc1 = mfma_32x32x16<BF16>(ring[s & 7], qa1[s], acc1);
         asm volatile("" ::"v"(acc1));
-        // second gap: the element's maximum and term, the operand read 8
-        // steps ahead and the gather loads
-        if (s < 16) {
-            ymax0 = max_f32(ymax0, y);
-            pin(ymax0);
-        } else {
-            ymax1 = max_f32(ymax1, y);
-            pin(ymax1);
+        // second gap: with MASK the element's maximum and term; the operand
+        // read 8 steps ahead and the gather loads
+        if (MASK) {
+            if (s < 16) {
+                ymax0 = max_f32(ymax0, y);
+                pin(ymax0);
+            } else {
+                ymax1 = max_f32(ymax1, y);
+                pin(ymax1);
+            }
+            ex = __builtin_amdgcn_exp2f(y);
+            pin(ex);
         }
-        ex = __builtin_amdgcn_exp2f(y);
-        pin(ex);
         if (s == kLseBar) barrier_after_vmcnt(0);
         ring[(s + kLead) & 7] =
             s + kLead < kSteps ? cur[2 * (s + kLead)] : nxt[2 * (s + kLead - kSteps)];
@@ -143,6 +170,11 @@ __device__ __forceinline__ void lse_tile(const uint4* __restrict__ cur,
         mid2(s);
     }
     __builtin_amdgcn_sched_barrier(0);
+    if (!MASK) {  // element 30's term, element 31's maximum and term
+        sum1 += ex;
+        ymax1 = max_f32(ymax1, y);
+        ex = __builtin_amdgcn_exp2f(y);
+    }
     sum1 += ex;  // element 31's term
 }
 
@@ -402,24 +434,25 @@ __global__ __launch_bounds__(256, 1) void smla_lse_wide_kernel(KernelArgs a) {
         // Tile `tile` (parity P): `cc` holds its stream state, `oa` the gather
         // offsets of tile+1 (formed by tile-1); tile+2's offsets are formed in
         // step 18 into `ob`. The used entries of this tile's 32 keys per wave
-        // are read in step 14 and collected in step 16. After the tile, the
+        // are read in step 10 and collected in step 16. After the tile, the
         // previous tile's sums are added, or that tile is redone exactly
         // (rebased on its maximum) where a lane's scores lie more than
         // kLseLazy above its base (terms could overflow), or all of them more
         // than kLseLazy below it while its sum is still below 1 (terms could
         // underflow while nothing near the base has been seen; once the sum
         // is at least 1 such terms are below its rounding).
-        auto body = [&](auto P, auto STEADY, int tile, const Ctl& cc, int32_t oa, int32_t& ob,
-                        const f32x16_t& prev0, const f32x16_t& prev1, f32x16_t& acc0,
-                        f32x16_t& acc1) {
+        auto body = [&](auto P, auto STEADY, auto MK, int tile, const Ctl& cc, int32_t oa,
+                        int32_t& ob, const f32x16_t& prev0, const f32x16_t& prev1,
+                        f32x16_t& acc0, f32x16_t& acc1) {
             constexpr int par = decltype(P)::value;
             constexpr bool steady = decltype(STEADY)::value != 0;
+            constexpr bool mask = decltype(MK)::value != 0;
             const uint4* cur = kbuf[par] + (32 * kh + col) * kPitch + half;
             const uint4* nxt = kbuf[1 - par] + (32 * kh + col) * kPitch + half;
             int32_t kb = 0, jm = 0;
             uint32_t nslots = 0;
             float ym0, ym1, s0, s1;
-            lse_tile<BF16>(
+            lse_tile<BF16, mask>(
                 cur, nxt, ring, qa0, qa1, prev0, prev1, pslots, a.c_scale, B0, B1, ym0, ym1, s0,
                 s1, i32x4_t{cc.da[0], cc.da[1], cc.da[2], cc.da[3]},
                 i32x4_t{cc.db[0], cc.db[1], cc.db[2], cc.db[3]}, cc.m0a, cc.sa, oa, cc.m0b, cc.sb,
@@ -428,14 +461,16 @@ __global__ __launch_bounds__(256, 1) void smla_lse_wide_kernel(KernelArgs a) {
                     // (the tile number is pinned in the step, so that no part
                     // of the step's work is hoisted into an earlier step)
                     int32_t tl = tile;
-                    if (s == 12 || s == 14 || s == 16 || s == 18) pin_s(tl);
-                    if (s == 12) {
-                        kb = DENSE ? (tl + 2) * kLseKeys + my_slot
-                                   : irow[((tl + 2) & 31) * kLseKeys + my_slot];
-                    } else if (s == 14) {
+                    if (s == 10 || s == 12 || s == 16 || s == 18) pin_s(tl);
+                    if (s == 10) {
                         // this tile's key 32 kh + c, for lanes c and c + 32
+                        // (read six steps before its use: waiting for it
+                        // also waits for every operand read issued before)
                         jm = DENSE ? tl * kLseKeys + 32 * kh + col
                                    : irow[(tl & 31) * kLseKeys + 32 * kh + col];
+                    } else if (s == 12) {
+                        kb = DENSE ? (tl + 2) * kLseKeys + my_slot
+                                   : irow[((tl + 2) & 31) * kLseKeys + my_slot];
                     } else if (s == 16) {
                         nslots = (uint32_t)__builtin_amdgcn_ballot_w64(
                             ((tl * kLseKeys + 32 * kh + col) < ric.n) &
@@ -462,15 +497,24 @@ __global__ __launch_bounds__(256, 1) void smla_lse_wide_kernel(KernelArgs a) {
             }
             pslots = nslots;
         };
-        // Pairs of tiles with two more after them run the steady body; the
-        // last two or three tiles form their stream state at each boundary.
-        // Even tiles fill xa from xb, odd tiles xb from xa.
+        // Pairs of tiles with two more after them run the steady body, whose
+        // epilogue drops the masks when the previous tile's entries are all
+        // used (every tile of a row but its last, unless the index list
+        // holds invalid entries); the last two or three tiles form their
+        // stream state at each boundary. Even tiles fill xa from xb, odd
+        // tiles xb from xa.
         const Ctl cs0 = ctl_steady(Par<0>{}), cs1 = ctl_steady(Par<1>{});
         int32_t offb = 0;
         int tile = 0;
         for (; tile + 3 < ntiles; tile += 2) {
-            body(Par<0>{}, Par<1>{}, tile, cs0, offa, offb, xb0, xb1, xa0, xa1);
-            body(Par<1>{}, Par<1>{}, tile + 1, cs1, offb, offa, xa0, xa1, xb0, xb1);
+            if (pslots == ~0u)
+                body(Par<0>{}, Par<1>{}, Par<0>{}, tile, cs0, offa, offb, xb0, xb1, xa0, xa1);
+            else
+                body(Par<0>{}, Par<1>{}, Par<1>{}, tile, cs0, offa, offb, xb0, xb1, xa0, xa1);
+            if (pslots == ~0u)
+                body(Par<1>{}, Par<1>{}, Par<0>{}, tile + 1, cs1, offb, offa, xa0, xa1, xb0, xb1);
+            else
+                body(Par<1>{}, Par<1>{}, Par<1>{}, tile + 1, cs1, offb, offa, xa0, xa1, xb0, xb1);
         }
         // the next row's index list into L2 (one dword per 128-byte line, 8 KB
         // in one load, into the dummy row) before the row end loads it
@@ -478,10 +522,10 @@ __global__ __launch_bounds__(256, 1) void smla_lse_wide_kernel(KernelArgs a) {
             dma_dword(raw_desc(a.idx + rln * a.K, (uint32_t)a.K * 4u), dummy_lds, 0, voff16 << 3);
         for (; tile < ntiles; tile += 2) {
             const Ctl c0 = ctl_of(Par<0>{}, tile);
-            body(Par<0>{}, Par<0>{}, tile, c0, offa, offb, xb0, xb1, xa0, xa1);
+            body(Par<0>{}, Par<0>{}, Par<1>{}, tile, c0, offa, offb, xb0, xb1, xa0, xa1);
             if (tile + 1 >= ntiles) break;
             const Ctl c1 = ctl_of(Par<1>{}, tile + 1);
-            body(Par<1>{}, Par<0>{}, tile + 1, c1, offb, offa, xa0, xa1, xb0, xb1);
+            body(Par<1>{}, Par<0>{}, Par<1>{}, tile + 1, c1, offb, offa, xa0, xa1, xb0, xb1);
         }
         // Every wave has passed the last tile's barrier: the rows of the next
         // row's Q that the last tiles did not load go out now.

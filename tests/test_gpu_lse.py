@@ -190,3 +190,53 @@ def test_lse_scores_far_below_zero(smla, heads):
     assert np.isfinite(got).all()
     d = np.abs(got.astype(np.float64) - want.astype(np.float64))
     assert (d <= 2e-5 * np.maximum(1.0, np.abs(want))).all(), float(d.max())
+
+
+def test_lse_holes_in_long_rows(smla):
+    """Unused entries inside topk_length in the middle of long rows (128
+    heads, 24 tiles of 64 entries): a few -1 pads, a whole tile of -1 pads,
+    or half the entries pointing past the sequence. Tiles holding such
+    entries are summed with their masks, the full tiles around them without,
+    and a tile with no used entry adds nothing."""
+    p = C.gen("tiny", heads_q=128, batch=1, seqlen_q=48, seqlen_k=3000, topk=1536, mask_mode=0,
+              seed=71)
+    rng = np.random.Generator(np.random.PCG64(71))
+    R, K = p.rows, p.topk
+    idx = p.sparse_indices.reshape(R, K)
+    for r in range(R):
+        kind = r % 4
+        if kind == 1:
+            idx[r, rng.choice(K, 3, replace=False)] = -1
+        elif kind == 2:
+            t = int(rng.integers(1, K // 64 - 1))
+            idx[r, 64 * t:64 * t + 64] = -1
+        elif kind == 3:
+            idx[r, rng.choice(K, K // 2, replace=False)] = p.seqlen_k + 5
+    say("[lse] holes in long rows, G=128")
+    want, _ = oracle.lse(p)
+    got = run_lse(smla, p)
+    check_lse("holes", got, want)
+    check_end_to_end("holes", smla, p, got)
+
+
+@pytest.mark.parametrize("heads", [64, 128])
+def test_lse_score_jump_mid_row(smla, heads):
+    """Eight keys scaled by 100 in tile 9 of rows of 24 full tiles: the tile
+    that sums them lies in the steady part of the row and must rebase
+    exactly there. The bar is relative: |d| <= 2e-5 * max(1, |lse|)."""
+    p = C.gen("tiny", heads_q=heads, batch=1, seqlen_q=8, seqlen_k=3000, topk=1536,
+              mask_mode=0, seed=72)
+    idx = p.sparse_indices.reshape(p.rows, p.topk)
+    jump = np.arange(8) * 301
+    for r in range(p.rows):
+        late = np.isin(idx[r], jump)
+        rest = idx[r][~late]
+        idx[r] = np.concatenate([rest[:9 * 64], idx[r][late], rest[9 * 64:]])
+    p.k.reshape(-1, p.head_dim)[torch.from_numpy(jump)] *= 100
+    say(f"[lse] score jump in the middle of the row, G={heads}")
+    want, _ = oracle.lse(p)
+    got = run_lse(smla, p)
+    assert np.isfinite(got).all()
+    d = np.abs(got.astype(np.float64) - want.astype(np.float64))
+    assert (d <= 2e-5 * np.maximum(1.0, np.abs(want))).all(), float(d.max())
+    assert np.abs(want).max() > 50  # the jump is really there
