@@ -39,6 +39,12 @@ SOURCES = [
     ("smla_dispatch.cpp", []),
     ("smla_host.cpp", []),
 ]
+# Kernels laid out to keep every value in registers: the build fails if the
+# compiler gives any of them scratch memory (a spill there would put memory
+# waits into the MFMA pipeline without any other sign). The general kernel's
+# 128-head variants without the staged row keep two registers in scratch.
+NO_SCRATCH = {"smla_wide.hip", "smla_narrow.hip", "smla_lse_wide.hip", "smla_lse.hip"}
+RESOURCE_REMARKS = ["-Rpass-analysis=kernel-resource-usage"]
 # the source files of each kernel (its own file and the shared device code)
 KERNEL_SOURCES = {
     "smla_wide_kernel": ("smla_wide.hip", "smla_device.h", "smla_internal.h"),
@@ -68,21 +74,45 @@ def commands(out: str, tmp: str) -> tuple:
     compiles, objs = [], []
     for src, extra in SOURCES:
         obj = os.path.join(tmp, os.path.splitext(src)[0] + ".o")
-        compiles.append([cc, *COMMON, *extra, "-x", "hip", "-c", os.path.join(CSRC, src),
-                         "-o", obj])
+        remarks = RESOURCE_REMARKS if src in NO_SCRATCH else []
+        compiles.append([cc, *COMMON, *extra, *remarks, "-x", "hip", "-c",
+                         os.path.join(CSRC, src), "-o", obj])
         objs.append(obj)
     link = [cc, "--offload-arch=" + ARCH, "-shared", "-fPIC", *objs, "-o", out]
     return compiles, link
+
+
+def scratch_users(text: str) -> list:
+    """(kernel, bytes per lane) of every kernel with scratch memory, from
+    the compiler's kernel-resource-usage remarks."""
+    out, name = [], None
+    for line in text.splitlines():
+        if "remark:" not in line:
+            continue
+        body = line.split("remark:", 1)[1].strip()
+        if body.startswith("Function Name:"):
+            name = body.split(":", 1)[1].split()[0]
+        elif body.startswith("ScratchSize [bytes/lane]:"):
+            n = int(body.split(":", 1)[1].split()[0])
+            if n:
+                out.append((name, n))
+    return out
 
 
 def _run(cmd, verbose):
     if verbose:
         print(" ".join(cmd), flush=True)
     res = subprocess.run(cmd, capture_output=True, text=True)
-    msg = "\n".join(l for l in (res.stdout + res.stderr).splitlines()
-                    if "packed-fp32-ops" not in l)
+    lines = (res.stdout + res.stderr).splitlines()
+    msg = "\n".join(l for l in lines
+                    if "packed-fp32-ops" not in l and "kernel-resource-usage" not in l)
     if res.returncode != 0:
         raise RuntimeError("hipcc failed:\n" + msg)
+    if RESOURCE_REMARKS[0] in cmd:
+        spills = scratch_users("\n".join(lines))
+        if spills:
+            raise RuntimeError("kernels that must not use scratch memory do: " +
+                               ", ".join(f"{k} ({n} bytes per lane)" for k, n in spills))
     if verbose and msg.strip():
         print(msg, flush=True)
 

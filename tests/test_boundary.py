@@ -504,3 +504,22 @@ def test_log_lines_on_stderr():
     r = subprocess.run([os.sys.executable, "-c", code], cwd=ROOT, env=env,
                        capture_output=True, text=True, timeout=120)
     assert "smla:" not in r.stderr
+
+
+def test_build_reads_scratch_use_from_the_compiler_remarks():
+    """The build refuses pipelined kernels that the compiler gave scratch
+    memory; the remark parser finds each kernel's ScratchSize line."""
+    from sparse_mla_attention_02_amd import _build
+    text = "\n".join([
+        "a.hip:1:1: remark: Function Name: kern_a [-Rpass-analysis=kernel-resource-usage]",
+        "a.hip:1:1: remark:     VGPRs: 256 [-Rpass-analysis=kernel-resource-usage]",
+        "a.hip:1:1: remark:     ScratchSize [bytes/lane]: 0 [-Rpass-analysis=kernel-resource-usage]",
+        "a.hip:9:1: remark: Function Name: kern_b [-Rpass-analysis=kernel-resource-usage]",
+        "a.hip:9:1: remark:     ScratchSize [bytes/lane]: 12 [-Rpass-analysis=kernel-resource-usage]",
+        "a.hip:3:9: warning: something else",
+    ])
+    assert _build.scratch_users(text) == [("kern_b", 12)]
+    compiles, _ = _build.commands("/tmp/libx.so", "/tmp")
+    guarded = {os.path.basename(c[c.index("-c") + 1]) for c in compiles
+               if _build.RESOURCE_REMARKS[0] in c}
+    assert guarded == _build.NO_SCRATCH
