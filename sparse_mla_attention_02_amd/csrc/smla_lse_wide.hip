@@ -472,9 +472,12 @@ __global__ __launch_bounds__(256, 1) void smla_lse_wide_kernel(KernelArgs a) {
                         kb = DENSE ? (tl + 2) * kLseKeys + my_slot
                                    : irow[((tl + 2) & 31) * kLseKeys + my_slot];
                     } else if (s == 16) {
-                        nslots = (uint32_t)__builtin_amdgcn_ballot_w64(
-                            ((tl * kLseKeys + 32 * kh + col) < ric.n) &
-                            ((uint32_t)jm < (uint32_t)ric.vis));
+                        // (two ballots of one comparison each: their masks
+                        // are the comparisons' own results)
+                        nslots = (uint32_t)(__builtin_amdgcn_ballot_w64(
+                                                (tl * kLseKeys + 32 * kh + col) < ric.n) &
+                                            __builtin_amdgcn_ballot_w64((uint32_t)jm <
+                                                                        (uint32_t)ric.vis));
                     } else if (s == 18) {
                         // (a steady tile has tile+2; otherwise stream B takes
                         // the next row's Q, if there is one)
@@ -497,11 +500,11 @@ __global__ __launch_bounds__(256, 1) void smla_lse_wide_kernel(KernelArgs a) {
             }
             pslots = nslots;
         };
-        // Pairs of tiles with two more after them run the steady body, whose
-        // epilogue drops the masks when the previous tile's entries are all
-        // used (every tile of a row but its last, unless the index list
-        // holds invalid entries); the last two or three tiles form their
-        // stream state at each boundary. Even tiles fill xa from xb, odd
+        // Pairs of tiles with two more after them run the steady body; the
+        // last two or three tiles form their stream state at each boundary.
+        // Either drops the masks from its epilogue when the previous tile's
+        // entries are all used (every tile of a row but its last, unless the
+        // index list holds invalid entries). Even tiles fill xa from xb, odd
         // tiles xb from xa.
         const Ctl cs0 = ctl_steady(Par<0>{}), cs1 = ctl_steady(Par<1>{});
         int32_t offb = 0;
@@ -522,10 +525,16 @@ __global__ __launch_bounds__(256, 1) void smla_lse_wide_kernel(KernelArgs a) {
             dma_dword(raw_desc(a.idx + rln * a.K, (uint32_t)a.K * 4u), dummy_lds, 0, voff16 << 3);
         for (; tile < ntiles; tile += 2) {
             const Ctl c0 = ctl_of(Par<0>{}, tile);
-            body(Par<0>{}, Par<0>{}, Par<1>{}, tile, c0, offa, offb, xb0, xb1, xa0, xa1);
+            if (pslots == ~0u)
+                body(Par<0>{}, Par<0>{}, Par<0>{}, tile, c0, offa, offb, xb0, xb1, xa0, xa1);
+            else
+                body(Par<0>{}, Par<0>{}, Par<1>{}, tile, c0, offa, offb, xb0, xb1, xa0, xa1);
             if (tile + 1 >= ntiles) break;
             const Ctl c1 = ctl_of(Par<1>{}, tile + 1);
-            body(Par<1>{}, Par<0>{}, Par<1>{}, tile + 1, c1, offb, offa, xa0, xa1, xb0, xb1);
+            if (pslots == ~0u)
+                body(Par<1>{}, Par<0>{}, Par<0>{}, tile + 1, c1, offb, offa, xa0, xa1, xb0, xb1);
+            else
+                body(Par<1>{}, Par<0>{}, Par<1>{}, tile + 1, c1, offb, offa, xa0, xa1, xb0, xb1);
         }
         // Every wave has passed the last tile's barrier: the rows of the next
         // row's Q that the last tiles did not load go out now.
