@@ -323,25 +323,46 @@ __device__ __forceinline__ void dma_row(i32x4_t desc, uint32_t m0, int32_t soff,
 // after the first need neither an M0 write nor its wait state (the compiler
 // never writes M0 in the pipelined kernel; these are its only users while a
 // stream runs).
+// With NT the loads carry the non-temporal hint (rows read once).
+template <bool NT = false>
 __device__ __forceinline__ void dma_row_first(i32x4_t desc, uint32_t m0, int32_t soff,
                                               uint32_t voff, int32_t step) {
-    asm volatile(
-        "s_mov_b32 m0, %0\n\t"
-        "s_nop 0\n\t"
-        "buffer_load_dwordx4 %1, %2, %3 offen lds\n\t"
-        "s_add_u32 m0, m0, %4"
-        :
-        : "s"(m0), "v"(voff), "s"(desc), "s"(soff), "s"(step)
-        : "memory", "m0", "scc");
+    if constexpr (NT)
+        asm volatile(
+            "s_mov_b32 m0, %0\n\t"
+            "s_nop 0\n\t"
+            "buffer_load_dwordx4 %1, %2, %3 offen nt lds\n\t"
+            "s_add_u32 m0, m0, %4"
+            :
+            : "s"(m0), "v"(voff), "s"(desc), "s"(soff), "s"(step)
+            : "memory", "m0", "scc");
+    else
+        asm volatile(
+            "s_mov_b32 m0, %0\n\t"
+            "s_nop 0\n\t"
+            "buffer_load_dwordx4 %1, %2, %3 offen lds\n\t"
+            "s_add_u32 m0, m0, %4"
+            :
+            : "s"(m0), "v"(voff), "s"(desc), "s"(soff), "s"(step)
+            : "memory", "m0", "scc");
 }
+template <bool NT = false>
 __device__ __forceinline__ void dma_row_next(i32x4_t desc, int32_t soff, uint32_t voff,
                                              int32_t step) {
-    asm volatile(
-        "buffer_load_dwordx4 %0, %1, %2 offen lds\n\t"
-        "s_add_u32 m0, m0, %3"
-        :
-        : "v"(voff), "s"(desc), "s"(soff), "s"(step)
-        : "memory", "m0", "scc");
+    if constexpr (NT)
+        asm volatile(
+            "buffer_load_dwordx4 %0, %1, %2 offen nt lds\n\t"
+            "s_add_u32 m0, m0, %3"
+            :
+            : "v"(voff), "s"(desc), "s"(soff), "s"(step)
+            : "memory", "m0", "scc");
+    else
+        asm volatile(
+            "buffer_load_dwordx4 %0, %1, %2 offen lds\n\t"
+            "s_add_u32 m0, m0, %3"
+            :
+            : "v"(voff), "s"(desc), "s"(soff), "s"(step)
+            : "memory", "m0", "scc");
 }
 // The same with the non-temporal hint, for data read once (Q rows, index
 // lists): the key rows, which are gathered again and again, keep their

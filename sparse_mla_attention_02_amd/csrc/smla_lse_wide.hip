@@ -68,8 +68,10 @@ __device__ __forceinline__ void lse_combine(float m, float l, float m2, float l2
 // element s - 1, the term of element s - 2; the second keeps the operand
 // read, the gather load and its wait. The tile's workgroup barrier follows
 // step 24's MFMAs (every wave has then read its last operand of this tile
-// and has its rows of the next one landed).
-template <bool BF16, bool MASK, typename Mid2>
+// and has its rows of the next one landed). With NT stream B's loads carry
+// the non-temporal hint (as in the main call's kernel: the last tiles of a
+// row, where stream B loads the next row's Q).
+template <bool BF16, bool MASK, bool NT, typename Mid2>
 __device__ __forceinline__ void lse_tile(const uint4* __restrict__ cur,
                                          const uint4* __restrict__ nxt, uint4 (&ring)[8],
                                          const uint4* qa0, const uint4* qa1,
@@ -164,9 +166,9 @@ __device__ __forceinline__ void lse_tile(const uint4* __restrict__ cur,
         else if (s >= 2 && s <= 9)
             dma_row_next(desc_a, soa[(s - 1) & 1], voff, stepa);
         if (s == 25)  // stream B: row s - 25 of tile t+2
-            dma_row_first(desc_b, (uint32_t)m0b, sob[0], voff, stepb);
+            dma_row_first<NT>(desc_b, (uint32_t)m0b, sob[0], voff, stepb);
         else if (s >= 26)
-            dma_row_next(desc_b, sob[(s - 1) & 1], voff, stepb);
+            dma_row_next<NT>(desc_b, sob[(s - 1) & 1], voff, stepb);
         mid2(s);
     }
     __builtin_amdgcn_sched_barrier(0);
@@ -452,7 +454,7 @@ __global__ __launch_bounds__(256, 1) void smla_lse_wide_kernel(KernelArgs a) {
             int32_t kb = 0, jm = 0;
             uint32_t nslots = 0;
             float ym0, ym1, s0, s1;
-            lse_tile<BF16, mask>(
+            lse_tile<BF16, mask, !steady>(
                 cur, nxt, ring, qa0, qa1, prev0, prev1, pslots, a.c_scale, B0, B1, ym0, ym1, s0,
                 s1, i32x4_t{cc.da[0], cc.da[1], cc.da[2], cc.da[3]},
                 i32x4_t{cc.db[0], cc.db[1], cc.db[2], cc.db[3]}, cc.m0a, cc.sa, oa, cc.m0b, cc.sb,

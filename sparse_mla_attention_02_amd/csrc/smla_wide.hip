@@ -52,7 +52,11 @@ constexpr int kWideBufBytes = kWideKeys * kRowBytes;
 // stepb). Each stream has its own buffer descriptor: a stream whose tile
 // does not exist loads rows of the next query row's Q into the free buffer
 // instead, or (a step of 0) sends its loads to one dummy row. Each row
-// offset is read into a scalar register one step before its load.
+// offset is read into a scalar register one step before its load. With NT
+// (the last two or three tiles of a row) stream B's loads carry the
+// non-temporal hint: there they load the next row's Q, read once (in the
+// first of three, the last tile's key rows), and Q then does not push the
+// key rows, gathered again and again, out of L2.
 //
 // The workgroup barrier sits after the MFMAs of step kBar = 24: by then every
 // wave has read its last operand of tile t (step 31's, read in step 23) and
@@ -62,7 +66,7 @@ constexpr int kWideBufBytes = kWideKeys * kRowBytes;
 // the MFMA stream does not drain between tiles. `mid(s)` is the caller's
 // spread-out work, called at the end of step s.
 constexpr int kBarStep = 24;
-template <bool BF16, typename Mid1, typename Mid2>
+template <bool BF16, bool NT, typename Mid1, typename Mid2>
 __device__ __forceinline__ void wide_tile(const uint4* __restrict__ cur,
                                           const uint4* __restrict__ nxt, uint4 (&ring)[8],
                                           const uint4* qa0, const uint4* qa1,
@@ -139,9 +143,9 @@ __device__ __forceinline__ void wide_tile(const uint4* __restrict__ cur,
         else if (s >= 2 && s <= 9)
             dma_row_next(desc_a, soa[(s - 1) & 1], voff, stepa);
         if (s == 25)  // stream B: row s - 25 of tile t+2
-            dma_row_first(desc_b, (uint32_t)m0b, sob[0], voff, stepb);
+            dma_row_first<NT>(desc_b, (uint32_t)m0b, sob[0], voff, stepb);
         else if (s >= 26)
-            dma_row_next(desc_b, sob[(s - 1) & 1], voff, stepb);
+            dma_row_next<NT>(desc_b, sob[(s - 1) & 1], voff, stepb);
         mid2(s);
     }
     __builtin_amdgcn_sched_barrier(0);
@@ -478,7 +482,7 @@ __global__ __launch_bounds__(256, 1) void smla_wide_kernel(KernelArgs a) {
             const uint4* nxt = kbuf[1 - par] + (32 * kh + col) * kPitch + half;
             int32_t kb = 0, jv = -1, sdst = 0;
             float parts[2], hs = 0.0f, tot = 0.0f;
-            wide_tile<BF16>(
+            wide_tile<BF16, !steady>(
                 cur, nxt, ring, qa0, qa1, prev0, prev1, l2, a.c_scale, pt, pex, psum,
                 i32x4_t{cc.da[0], cc.da[1], cc.da[2], cc.da[3]},
                 i32x4_t{cc.db[0], cc.db[1], cc.db[2], cc.db[3]}, cc.m0a, cc.sa, oa, cc.m0b, cc.sb, ob, voff16,
