@@ -24,8 +24,11 @@ CPU oracle (fed the same lse) on the rows the CPU baseline evaluates, every
 row's sum is checked against 1, and the GPU lse against the oracle's lse on
 a row sample; ``parity`` reports the result and a mismatch makes the run
 exit with status 1. ``kernel_ms`` is the median of the per-launch HIP event
-times; ``clock_mhz`` is the GPU's graphics clock sampled with amdsmi during
-the timed region (null where amdsmi cannot read it).
+times; ``clock_mhz`` is the GPU's graphics clock from amdsmi's metrics table
+(the mean over the XCDs of each snapshot), over the snapshots the driver
+published while the untimed prewarm and warmup steps and the timed steps ran
+(it refreshes them about once per second; null where amdsmi cannot read
+them or none fell in that window).
 """
 
 from __future__ import annotations
@@ -145,18 +148,24 @@ def cpu_model():
 
 
 class ClockSampler:
-    """Samples the GPU's graphics clock (MHz) with amdsmi from a thread while
-    the timed region runs. Every failure leaves the figures null: the clock
-    is reported, never required."""
+    """Reads the GPU's graphics clocks (MHz) from amdsmi's metrics table in a
+    thread while the steps run. The driver refreshes the table about once per
+    second, so only snapshots that changed since the previous read count, and
+    only those published at least `settle_s` after the sampler started (the
+    clock needs load to rise). Every failure leaves the figures null: the
+    clock is reported, never required."""
 
-    def __init__(self, torch, dev_index=0, period_s=0.005):
-        self.samples = []
+    def __init__(self, torch, dev_index=0, period_s=0.02, settle_s=0.25):
+        self.snapshots = []  # mean clock over the XCDs, per fresh snapshot
         self.error = None
         self.period = period_s
+        self.settle = settle_s
         self._stop = threading.Event()
         self._thread = None
         self._smi = None
         self._h = None
+        self._last = None
+        self._t0 = None
         try:
             import amdsmi
             amdsmi.amdsmi_init()
@@ -180,20 +189,32 @@ class ClockSampler:
             self._smi = None
 
     def _read(self):
-        info = self._smi.amdsmi_get_clock_info(self._h, self._smi.AmdSmiClkType.GFX)
-        return float(info["clk"])
+        """(snapshot key, mean graphics clock over the XCDs) of the current
+        metrics table."""
+        m = self._smi.amdsmi_get_gpu_metrics_info(self._h)
+        clks = [float(c) for c in (m.get("current_gfxclks") or [])
+                if isinstance(c, (int, float)) and 0 < c < 0xffff]
+        if not clks:
+            clks = [float(m["current_gfxclk"])]
+        key = (m.get("system_clock_counter"), tuple(clks))
+        return key, float(np.mean(clks))
 
     def _loop(self):
         while not self._stop.is_set():
             try:
-                self.samples.append(self._read())
+                key, mhz = self._read()
             except Exception as e:  # noqa: BLE001
                 self.error = f"{type(e).__name__}: {e}"
                 return
+            if self._last is not None and key != self._last and \
+                    time.perf_counter() - self._t0 >= self.settle:
+                self.snapshots.append(mhz)
+            self._last = key
             self._stop.wait(self.period)
 
     def __enter__(self):
         if self._smi is not None:
+            self._t0 = time.perf_counter()
             self._thread = threading.Thread(target=self._loop, daemon=True)
             self._thread.start()
         return self
@@ -204,12 +225,16 @@ class ClockSampler:
             self._thread.join()
 
     def summary(self):
-        if not self.samples:
-            return {"median": None, "min": None, "max": None, "samples": 0,
-                    "source": "amdsmi gfx clock", "error": self.error}
-        a = np.array(self.samples)
-        return {"median": float(np.median(a)), "min": float(a.min()), "max": float(a.max()),
-                "samples": int(a.size), "source": "amdsmi gfx clock"}
+        src = "amdsmi gpu metrics, current_gfxclks averaged over the XCDs"
+        window = "prewarm, warmup and timed steps"
+        if not self.snapshots:
+            return {"median": None, "min": None, "max": None, "snapshots": 0, "source": src,
+                    "window": window,
+                    "error": self.error or "no metrics snapshot published in the window"}
+        a = np.array(self.snapshots)
+        return {"median": round(float(np.median(a)), 1), "min": round(float(a.min()), 1),
+                "max": round(float(a.max()), 1), "snapshots": int(a.size), "source": src,
+                "window": window}
 
 
 TOL = 2e-5          # per element, and per lse value
@@ -251,9 +276,11 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=200)
-    ap.add_argument("--prewarm-seconds", type=float, default=0.5,
+    ap.add_argument("--prewarm-seconds", type=float, default=1.5,
                     help="untimed steps run for this long before the warmup steps: an idle "
-                         "GPU takes on the order of 100 ms of load to reach its working clock")
+                         "GPU takes on the order of 100 ms of load to reach its working "
+                         "clock, and the clock figures come from metrics the driver "
+                         "refreshes about once per second")
     ap.add_argument("--workload", default="dsv32")
     ap.add_argument("--op", choices=("l1norm", "lse"), default="l1norm",
                     help="l1norm: the Softmax-L1Norm call (the hot path); lse: the GPU "
@@ -350,6 +377,9 @@ def main():
             after.record(stream)
         return md
 
+    # the graphics clock, read while the untimed and the timed steps run
+    clock = ClockSampler(torch, 0)
+    clock.__enter__()
     t_pre = time.perf_counter()
     n_pre = 0
     while time.perf_counter() - t_pre < args.prewarm_seconds:
@@ -366,14 +396,15 @@ def main():
     ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
           for _ in range(args.steps)]
     log(f"timing {args.steps} steps")
-    clock = ClockSampler(torch, 0)
     torch.cuda.synchronize()
-    with clock:
+    try:
         t0 = time.perf_counter()
         for i in range(args.steps):
             md = step(ev[i][0], ev[i][1])
         torch.cuda.synchronize()
         wall = time.perf_counter() - t0
+    finally:
+        clock.__exit__(None, None, None)
     kernel_ms = [a.elapsed_time(b) for a, b in ev]
     ms_step = wall * 1e3 / args.steps
     kms = float(np.median(kernel_ms))
