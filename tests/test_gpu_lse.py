@@ -192,14 +192,19 @@ def test_lse_scores_far_below_zero(smla, heads):
     assert (d <= 2e-5 * np.maximum(1.0, np.abs(want))).all(), float(d.max())
 
 
-def test_lse_holes_in_long_rows(smla):
+@pytest.mark.parametrize("layout", ["BSND", "TND"])
+def test_lse_holes_in_long_rows(smla, layout):
     """Unused entries inside topk_length in the middle of long rows (128
     heads, 24 tiles of 64 entries): a few -1 pads, a whole tile of -1 pads,
     or half the entries pointing past the sequence. Tiles holding such
     entries are summed with their masks, the full tiles around them without,
     and a tile with no used entry adds nothing."""
-    p = C.gen("tiny", heads_q=128, batch=1, seqlen_q=48, seqlen_k=3000, topk=1536, mask_mode=0,
-              seed=71)
+    if layout == "BSND":
+        p = C.gen("tiny", heads_q=128, batch=1, seqlen_q=48, seqlen_k=3000, topk=1536,
+                  mask_mode=0, seed=71)
+    else:
+        p = C.gen("tnd_varlen", heads_q=128, topk=1536, seqlens_q=(20, 28),
+                  seqlens_k=(3000, 2600), mask_mode=0, dtype="bf16", seed=73)
     rng = np.random.Generator(np.random.PCG64(71))
     R, K = p.rows, p.topk
     idx = p.sparse_indices.reshape(R, K)
@@ -211,8 +216,8 @@ def test_lse_holes_in_long_rows(smla):
             t = int(rng.integers(1, K // 64 - 1))
             idx[r, 64 * t:64 * t + 64] = -1
         elif kind == 3:
-            idx[r, rng.choice(K, K // 2, replace=False)] = p.seqlen_k + 5
-    say("[lse] holes in long rows, G=128")
+            idx[r, rng.choice(K, K // 2, replace=False)] = 5000
+    say(f"[lse] holes in long rows, G=128, {layout}")
     want, _ = oracle.lse(p)
     got = run_lse(smla, p)
     check_lse("holes", got, want)
