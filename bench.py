@@ -423,9 +423,14 @@ def main():
         roof = {"bound": "hbm", "achieved": round(k_gbps, 1), "peak": PEAK_HBM_GBPS,
                 "unit": "GB/s", "frac": round(k_gbps / PEAK_HBM_GBPS, 4)}
     if args.op == "lse":
-        # 65..128 heads with at most 2048 indices (or dense): the pipelined kernel
-        pipe = p.groups > 64 and (p.sparse_indices is None or p.topk <= 2048)
-        kernel = "smla_lse_wide_kernel" if pipe else "smla_lse_kernel"
+        # up to 64 heads: the small-head pipelined kernel; 65..128 heads with at
+        # most 2048 indices (or dense): the one for 65..128 heads
+        if p.groups <= 64:
+            kernel = "smla_lse_narrow_kernel"
+        elif p.sparse_indices is None or p.topk <= 2048:
+            kernel = "smla_lse_wide_kernel"
+        else:
+            kernel = "smla_lse_kernel"
     else:
         kernel = KERNELS.get(int(md[24]), "unknown")
     # (the committed counter summaries cover the S2-wide main call and the lse call)

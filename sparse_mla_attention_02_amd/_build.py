@@ -52,6 +52,7 @@ KERNEL_SOURCES = {
     "smla_l1norm_kernel": ("smla_general.hip", "smla_device.h", "smla_internal.h"),
     "smla_lse_kernel": ("smla_lse.hip", "smla_device.h", "smla_internal.h"),
     "smla_lse_wide_kernel": ("smla_lse_wide.hip", "smla_device.h", "smla_internal.h"),
+    "smla_lse_narrow_kernel": ("smla_narrow.hip", "smla_device.h", "smla_internal.h"),
 }
 EXAMPLE_SRC = os.path.join(CSRC, "example", "smla_example.cpp")
 EXAMPLE = os.path.join(PKG, "smla_example")

@@ -532,12 +532,12 @@ smla_status_t run_main(const char* call, const smla::KernelArgs& a, int32_t dtyp
 
 // Co-resident workgroups per CU of the lse kernel, queried once per variant.
 std::mutex g_lse_occ_mu;
-std::map<std::tuple<int, bool, bool, bool>, int> g_lse_occ;  // (ht, bf16, tnd, pipelined)
+std::map<std::tuple<int, bool, bool, int>, int> g_lse_occ;  // (ht, bf16, tnd, variant)
 
 hipError_t lse_capacity(int ht, bool bf16, bool tnd, int64_t G, int64_t topk, int* per_cu) {
     std::lock_guard<std::mutex> lk(g_lse_occ_mu);
-    const bool pipe = smla::lse_pipelined(G, topk);
-    auto it = g_lse_occ.find({ht, bf16, tnd, pipe});
+    const int var = smla::lse_variant(G, topk);
+    auto it = g_lse_occ.find({ht, bf16, tnd, var});
     if (it != g_lse_occ.end()) {
         *per_cu = it->second;
         return hipSuccess;
@@ -546,7 +546,7 @@ hipError_t lse_capacity(int ht, bool bf16, bool tnd, int64_t G, int64_t topk, in
     hipError_t e = smla::lse_resident_per_cu(ht, bf16, tnd, G, topk, &occ);
     if (e != hipSuccess) return e;
     if (occ <= 0) return hipErrorInvalidConfiguration;
-    g_lse_occ[{ht, bf16, tnd, pipe}] = occ;
+    g_lse_occ[{ht, bf16, tnd, var}] = occ;
     *per_cu = occ;
     return hipSuccess;
 }
@@ -634,9 +634,11 @@ smla_status_t smla_softmax_lse(
         const int64_t cap = (int64_t)m[22] * per_cu;
         a.num_wg = (int32_t)(a.R < cap ? a.R : cap);
     }
-    const bool pipe = smla::lse_pipelined(a.G, a.dense ? 0 : a.K);
-    log_launch("smla_softmax_lse", a, ht, dtype, pipe ? "smla_lse_wide_kernel" : "smla_lse_kernel",
-               a.num_wg, pipe ? 256 : 64 * (ht == 4 ? 2 : ht), stream);
+    const int var = smla::lse_variant(a.G, a.dense ? 0 : a.K);
+    log_launch("smla_softmax_lse", a, ht, dtype,
+               var == smla::kLseNarrow ? "smla_lse_narrow_kernel"
+               : var == smla::kLseWide ? "smla_lse_wide_kernel" : "smla_lse_kernel",
+               a.num_wg, var != smla::kLseGeneral ? 256 : 64 * (ht == 4 ? 2 : ht), stream);
     hipError_t e = smla::launch_lse(a, ht, bf16, tnd, static_cast<hipStream_t>(stream));
     if (e != hipSuccess)
         return fail(SMLA_ERR_RUNTIME, "kernel launch failed: %s", hipGetErrorString(e));

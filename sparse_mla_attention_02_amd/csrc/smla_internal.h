@@ -69,17 +69,23 @@ hipError_t wide_resident_per_cu(bool bf16, bool tnd, int* out);
 hipError_t launch_narrow(const KernelArgs& a, bool bf16, bool tnd, hipStream_t stream);
 hipError_t narrow_resident_per_cu(bool bf16, bool tnd, int* out);
 
-// The forward softmax_lse call: a.out receives (R, G) fp32. Rows of
-// 65..128 heads with at most kWideIndexCap indices (or dense rows) take the
-// pipelined kernel, other shapes the general one.
-inline bool lse_pipelined(int64_t G, int64_t topk) { return G > 64 && topk <= kWideIndexCap; }
+// The forward softmax_lse call: a.out receives (R, G) fp32. Rows of up to 64
+// heads take the pipelined small-head kernel (any K), rows of 65..128 heads
+// with at most kWideIndexCap indices (or dense rows) the pipelined kernel for
+// 65..128 heads, other shapes the general one.
+enum { kLseGeneral = 0, kLseWide = 1, kLseNarrow = 2 };
+inline int lse_variant(int64_t G, int64_t topk) {
+    return G <= 64 ? kLseNarrow : (topk <= kWideIndexCap ? kLseWide : kLseGeneral);
+}
 hipError_t launch_lse(const KernelArgs& a, int head_tiles, bool bf16, bool tnd,
                       hipStream_t stream);
 hipError_t launch_lse_wide(const KernelArgs& a, bool bf16, bool tnd, hipStream_t stream);
+hipError_t launch_lse_narrow(const KernelArgs& a, bool bf16, bool tnd, hipStream_t stream);
 
 // Co-resident workgroups per CU of the lse kernel used for (G, topk).
 hipError_t lse_resident_per_cu(int head_tiles, bool bf16, bool tnd, int64_t G, int64_t topk,
                                int* out);
 hipError_t lse_wide_resident_per_cu(bool bf16, bool tnd, int* out);
+hipError_t lse_narrow_resident_per_cu(bool bf16, bool tnd, int* out);
 
 }  // namespace smla

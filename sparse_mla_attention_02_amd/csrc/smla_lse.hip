@@ -398,13 +398,19 @@ hipError_t occupancy_lse_t(int* out) {
 }  // namespace
 
 hipError_t launch_lse(const KernelArgs& a, int ht, bool bf16, bool tnd, hipStream_t stream) {
-    if (lse_pipelined(a.G, a.dense ? 0 : a.K)) return launch_lse_wide(a, bf16, tnd, stream);
-    SMLA_DISPATCH(launch_lse_t, a, stream);
+    switch (lse_variant(a.G, a.dense ? 0 : a.K)) {
+        case kLseNarrow: return launch_lse_narrow(a, bf16, tnd, stream);
+        case kLseWide: return launch_lse_wide(a, bf16, tnd, stream);
+        default: SMLA_DISPATCH(launch_lse_t, a, stream);
+    }
 }
 
 hipError_t lse_resident_per_cu(int ht, bool bf16, bool tnd, int64_t G, int64_t topk, int* out) {
-    if (lse_pipelined(G, topk)) return lse_wide_resident_per_cu(bf16, tnd, out);
-    SMLA_DISPATCH(occupancy_lse_t, out);
+    switch (lse_variant(G, topk)) {
+        case kLseNarrow: return lse_narrow_resident_per_cu(bf16, tnd, out);
+        case kLseWide: return lse_wide_resident_per_cu(bf16, tnd, out);
+        default: SMLA_DISPATCH(occupancy_lse_t, out);
+    }
 }
 
 }  // namespace smla

@@ -92,6 +92,37 @@ __device__ __forceinline__ float quad_sum(float x) {
     return __builtin_bit_cast(float, (uint32_t)b[0]) + __builtin_bit_cast(float, (uint32_t)b[1]);
 }
 
+// max(a, b) in one instruction (fmaxf quiets both inputs for its NaN rules
+// first; the lse sums here take finite values or -inf, never NaN)
+__device__ __forceinline__ float nar_max(float a, float b) {
+    float r;
+    asm("v_max_f32 %0, %1, %2" : "=v"(r) : "v"(a), "v"(b));
+    return r;
+}
+
+// x of the lane that DPP control CTRL selects within the lane's row of 16
+template <int CTRL>
+__device__ __forceinline__ float dpp_f(float x) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(
+                                         0, __builtin_bit_cast(int, x), CTRL, 0xf, 0xf, false));
+}
+// Maximum and sum of x over each row of 16 lanes, the same bits in all 16:
+// lanes pair by xor 1 and xor 2 inside their quad, then with the mirror lane
+// in their half row and in their row (each step adds two equal-bit partial
+// results of the pair, in either order: the same sum).
+__device__ __forceinline__ float row16_max(float x) {
+    x = nar_max(x, dpp_f<0xB1>(x));   // quad_perm [1,0,3,2]
+    x = nar_max(x, dpp_f<0x4E>(x));   // quad_perm [2,3,0,1]
+    x = nar_max(x, dpp_f<0x141>(x));  // row_half_mirror
+    return nar_max(x, dpp_f<0x140>(x));  // row_mirror
+}
+__device__ __forceinline__ float row16_sum(float x) {
+    x = x + dpp_f<0xB1>(x);
+    x = x + dpp_f<0x4E>(x);
+    x = x + dpp_f<0x141>(x);
+    return x + dpp_f<0x140>(x);
+}
+
 // A row's decode in 32 bits (rows, key rows and columns number fewer than
 // 2^31, checked on the host): fewer scalar registers than RowInfo.
 struct NarRow {
@@ -139,14 +170,24 @@ __device__ __forceinline__ NarElem nar_elem_plus(int j, int d, int32_t R, int32_
     return e;
 }
 
-template <int NB, bool BF16, bool TND, bool DENSE>
-__global__ __launch_bounds__(256, 1) void smla_narrow_kernel(KernelArgs a) {
+// The kernel's body, for the main call (LSE false) and for the softmax_lse
+// call (LSE true: the same row walk, loads and waits; each lane keeps, per
+// score element, the running maximum M and sum L of 2^(x - M) over its keys,
+// in log2 units, and the row end combines the lanes and waves of each head
+// into lse = ln 2 (M + log2 L); there is no output row, and the value store of
+// each tile is kept, to an offset the buffer range drops, so that every tile
+// issues the same number of vector memory instructions as the waits count).
+template <int NB, bool BF16, bool TND, bool DENSE, bool LSE>
+__device__ __forceinline__ void narrow_body(const KernelArgs& a) {
     constexpr int NT = 256;
     constexpr int NE = NB * 4;             // scores per lane and tile
     constexpr int EPS = NE >= 16 ? 2 : 1;  // epilogue elements per step
     constexpr int NG = NE / EPS;           // epilogue groups: fma in step g, exp g+1, sum g+2
     constexpr int kSteps = kChunks / 4;    // 16 k-steps of 32 along D
     static_assert(NG + 2 <= 10, "the epilogue must end by step 9");
+    // LSE: below every score, in log2 units (a finite start keeps every
+    // rescale factor finite: an unused entry enters as -inf and adds 2^-inf)
+    constexpr float kLseFloor = -1.0e30f;
     // Loads per tile (index loads: one per wave; the dense case has none):
     // two index loads, 16 rows, one store, one lse load. A row start issues
     // as many after tile 1's rows: that load's lse, the next element's index
@@ -163,6 +204,7 @@ __global__ __launch_bounds__(256, 1) void smla_narrow_kernel(KernelArgs a) {
     __shared__ int32_t ixbuf[4][8][64];
     __shared__ float lsebuf[64];
     __shared__ uint4 dummy[64];  // loads with nothing to fetch
+    __shared__ float cmb[LSE ? 4 : 1][64][2];  // LSE: (M, L) per wave and head
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -192,9 +234,11 @@ __global__ __launch_bounds__(256, 1) void smla_narrow_kernel(KernelArgs a) {
             const int64_t r = row_of(a, it_next, blockIdx.x);
             ++it_next;
             if (r >= a.R) continue;
-            zero_span(a.out + r * a.W, 0, a.W, tid, NT);
+            if (!LSE) zero_span(a.out + r * a.W, 0, a.W, tid, NT);
             ri = nar_row(decode_row<TND>(a, r));
             T = __builtin_amdgcn_readfirstlane((ri.n + kNarKeys - 1) / kNarKeys);
+            // LSE: a row without a used entry has lse -inf
+            if (LSE && T == 0 && tid < a.G) a.out[r * a.G + tid] = -__builtin_inff();
             if (T > 0) return (int32_t)r;
         }
     };
@@ -290,7 +334,7 @@ __global__ __launch_bounds__(256, 1) void smla_narrow_kernel(KernelArgs a) {
     };
     // the lse of a Q element (wave 0; everything else loads into the dummy row)
     auto lse_dma = [&](NarElem e, const NarCtl& c) __attribute__((always_inline)) {
-        const bool isq = e.kind == kElemQ;
+        const bool isq = !LSE && e.kind == kElemQ;  // (LSE: no lse input; an empty load)
         dma_dword(uniform_desc(raw_desc(a.lse + (int64_t)(isq ? e.row : 0) * a.G,
                                         isq ? (uint32_t)a.G * 4u : 0u)),
                   (uint32_t)c.lm0, 0, voff4);
@@ -338,6 +382,7 @@ __global__ __launch_bounds__(256, 1) void smla_narrow_kernel(KernelArgs a) {
 
     uint4 qa[NB][kSteps];
     float l2[NE];
+    float lm[LSE ? NE : 1], ll[LSE ? NE : 1];  // LSE: per element, M and L of the row
     uint4 opa[kSteps], opb[kSteps];  // B operands of a tile, read a tile ahead
     f32x4_t xa[NB], xb[NB];
 
@@ -359,8 +404,14 @@ __global__ __launch_bounds__(256, 1) void smla_narrow_kernel(KernelArgs a) {
 #pragma unroll
         for (int e = 0; e < NE; ++e) {
             const int h = 16 * (e >> 2) + 4 * gq + (e & 3);
-            const float v = lsebuf[h];
-            l2[e] = h < a.G ? v * kLog2e : __builtin_inff();
+            if constexpr (LSE) {
+                lm[e] = kLseFloor;
+                ll[e] = 0.0f;
+                l2[e] = 0.0f;
+            } else {
+                const float v = lsebuf[h];
+                l2[e] = h < a.G ? v * kLog2e : __builtin_inff();
+            }
         }
 #pragma unroll
         for (int s = 0; s < kSteps; ++s) opa[s] = kbuf[qb ^ 1][my_slot * kPitch + 16 * gq + s];
@@ -393,7 +444,7 @@ __global__ __launch_bounds__(256, 1) void smla_narrow_kernel(KernelArgs a) {
         auto store_off = [&](int tile, int32_t j) __attribute__((always_inline)) -> int32_t {
             const int e = tile * kNarKeys + my_slot;
             const int32_t jj = DENSE ? e : j;
-            const bool st = (gq == 0) & (tile >= 0) & used_of(ri, tile, jj);
+            const bool st = !LSE & (gq == 0) & (tile >= 0) & used_of(ri, tile, jj);
             const int32_t c = a.kwide ? e : ri.col0 + jj;
             return st ? (int32_t)((uint32_t)c * 4u) : 0x7ffffff0;
         };
@@ -430,6 +481,9 @@ __global__ __launch_bounds__(256, 1) void smla_narrow_kernel(KernelArgs a) {
             }
             int32_t jg = 0, ov = 0, js = 0, so[4];
             float tt[EPS], ee[EPS], sum = 0.0f, tot = 0.0f, val = 0.0f;
+            bool uprev = false;             // LSE: tile t-1's key of this lane is used
+            // LSE: an element's score, new maximum and rescale factors
+            float ly[2], lmn[2], ld1[2], ld2[2];
             auto work = [&](int s, int b) __attribute__((always_inline)) {
                 if (s == 0 && b == 0) {
                     // the loads of tile t-1 (or, at tile 0, as many of the
@@ -448,8 +502,66 @@ __global__ __launch_bounds__(256, 1) void smla_narrow_kernel(KernelArgs a) {
                         for (int k = 0; k < 4; ++k) nop[4 * s + k] = nsrc[4 * s + k];
                     }
                 }
+                // LSE: the lane's key of tile t-1 is used (its index was read
+                // in step 0); each element of tile t-1: its scaled score y
+                // (-inf if unused), the new maximum, the two rescale factors,
+                // the sum. With four head blocks one element per step (steps
+                // 1..15, two in step 15), spread over the step's four gaps;
+                // with fewer, EPS elements per step from step 2, after the
+                // step's last MFMA.
+                if constexpr (LSE) {
+                    if (s == 1 && b == (NB == 4 ? 0 : 3)) {
+                        uprev = (t >= 1) & used_of(ri, t - 1, js);
+                    }
+                    auto first_half = [&](int e, int k) __attribute__((always_inline)) {
+                        ly[k] = uprev ? prev[e >> 2][e & 3] * a.c_scale : -__builtin_inff();
+                        lmn[k] = nar_max(lm[e], ly[k]);
+                        pin(ly[k]);
+                        pin(lmn[k]);
+                    };
+                    auto second_half = [&](int e, int k) __attribute__((always_inline)) {
+                        const float d1 = __builtin_amdgcn_exp2f(lm[e] - lmn[k]);
+                        const float d2 = __builtin_amdgcn_exp2f(ly[k] - lmn[k]);
+                        ll[e] = __builtin_fmaf(ll[e], d1, d2);
+                        lm[e] = lmn[k];
+                        pin(ll[e]);
+                        pin(lm[e]);
+                    };
+                    if constexpr (NB == 4) {
+                        static_assert(NE == 16, "four head blocks: 16 elements");
+#pragma unroll
+                        for (int k = 0; k < 2; ++k) {
+                            const int e = k == 0 ? s - 1 : 15;
+                            if ((k == 0 && s >= 1) || (k == 1 && s == 15)) {
+                                if (b == 0) {
+                                    first_half(e, k);
+                                } else if (b == 1) {
+                                    ld1[k] = __builtin_amdgcn_exp2f(lm[e] - lmn[k]);
+                                    pin(ld1[k]);
+                                } else if (b == 2) {
+                                    ld2[k] = __builtin_amdgcn_exp2f(ly[k] - lmn[k]);
+                                    pin(ld2[k]);
+                                } else {
+                                    ll[e] = __builtin_fmaf(ll[e], ld1[k], ld2[k]);
+                                    lm[e] = lmn[k];
+                                    pin(ll[e]);
+                                    pin(lm[e]);
+                                }
+                            }
+                        }
+                    } else if (b == 3) {
+#pragma unroll
+                        for (int k = 0; k < EPS; ++k) {
+                            const int e = EPS * (s - 2) + k;
+                            if (s >= 2 && e < NE) {
+                                first_half(e, k);
+                                second_half(e, k);
+                            }
+                        }
+                    }
+                }
                 // epilogue of tile t-1: sum (group s-2), exp2 (s-1), fma (s)
-                if ((NB == 4 && b <= 1) || (NB < 4 && b == 3)) {
+                if (!LSE && ((NB == 4 && b <= 1) || (NB < 4 && b == 3))) {
                     constexpr int kPer = NB == 4 ? 1 : EPS;
 #pragma unroll
                     for (int k0 = 0; k0 < kPer; ++k0) {
@@ -464,7 +576,7 @@ __global__ __launch_bounds__(256, 1) void smla_narrow_kernel(KernelArgs a) {
                         }
                     }
                 }
-                if ((NB == 4 && b >= 2) || (NB < 4 && b == 3)) {
+                if (!LSE && ((NB == 4 && b >= 2) || (NB < 4 && b == 3))) {
                     constexpr int kPer = NB == 4 ? 1 : EPS;
 #pragma unroll
                     for (int k0 = 0; k0 < kPer; ++k0) {
@@ -476,7 +588,7 @@ __global__ __launch_bounds__(256, 1) void smla_narrow_kernel(KernelArgs a) {
                         }
                     }
                 }
-                if (b == (NB == 4 ? 2 : 3)) {
+                if (!LSE && b == (NB == 4 ? 2 : 3)) {
                     if (s == 10) {
                         tot = quad_sum(sum);
                         pin(tot);
@@ -587,11 +699,59 @@ __global__ __launch_bounds__(256, 1) void smla_narrow_kernel(KernelArgs a) {
                 sum += __builtin_amdgcn_exp2f(__builtin_fmaf(x[e >> 2][e & 3], a.c_scale, -l2[e]));
             return quad_sum(sum) * a.inv_g;
         };
-        const float v = (ntiles & 1) ? last_value(xa) : last_value(xb);
-        waitcnt_vm_lgkm0<0>();
-        const int32_t js = idx_read(kJsSlot0 + ((ntiles - 1) & 3));
-        __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, v), orsrc,
-                                              store_off(ntiles - 1, js), 0, 0);
+        if constexpr (LSE) {
+            // the last tile's scores into M, L; then the 16 lanes of each
+            // group (one key each, the same heads) combine in registers, the
+            // four waves (their keys) through LDS (wave 0 first), and lanes
+            // below G write the row's lse
+            waitcnt_vm_lgkm0<0>();
+            const int32_t js = idx_read(kJsSlot0 + ((ntiles - 1) & 3));
+            const bool ul = used_of(ri, ntiles - 1, js);
+            auto last_update = [&](const f32x4_t(&x)[NB]) __attribute__((always_inline)) {
+#pragma unroll
+                for (int e = 0; e < NE; ++e) {
+                    const float y = ul ? x[e >> 2][e & 3] * a.c_scale : -__builtin_inff();
+                    const float mn = nar_max(lm[e], y);
+                    ll[e] = __builtin_fmaf(ll[e], __builtin_amdgcn_exp2f(lm[e] - mn),
+                                           __builtin_amdgcn_exp2f(y - mn));
+                    lm[e] = mn;
+                }
+            };
+            if (ntiles & 1)
+                last_update(xa);
+            else
+                last_update(xb);
+            auto combine = [](float m1, float l1, float m2, float l2v, float& m, float& l) {
+                m = nar_max(m1, m2);
+                l = l1 * __builtin_amdgcn_exp2f(m1 - m) + l2v * __builtin_amdgcn_exp2f(m2 - m);
+            };
+#pragma unroll
+            for (int e = 0; e < NE; ++e) {
+                // the group's maximum, each lane's sum rescaled to it, summed
+                const float m = row16_max(lm[e]);
+                ll[e] = row16_sum(ll[e] * __builtin_amdgcn_exp2f(lm[e] - m));
+                lm[e] = m;
+                if (n == 0) {
+                    const int h = 16 * (e >> 2) + 4 * gq + (e & 3);
+                    cmb[wave][h][0] = lm[e];
+                    cmb[wave][h][1] = ll[e];
+                }
+            }
+            lds_barrier();
+            if (tid < a.G) {
+                float m = cmb[0][tid][0], l = cmb[0][tid][1];
+#pragma unroll
+                for (int w = 1; w < 4; ++w) combine(m, l, cmb[w][tid][0], cmb[w][tid][1], m, l);
+                a.out[(int64_t)row * a.G + tid] =
+                    l > 0.0f ? (m + __builtin_amdgcn_logf(l)) * kLn2 : -__builtin_inff();
+            }
+        } else {
+            const float v = (ntiles & 1) ? last_value(xa) : last_value(xb);
+            waitcnt_vm_lgkm0<0>();
+            const int32_t js = idx_read(kJsSlot0 + ((ntiles - 1) & 3));
+            __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, v), orsrc,
+                                                  store_off(ntiles - 1, js), 0, 0);
+        }
         if (rn >= R) break;
         // the next row: its Q is element k + 1 + ntiles
         qb = (qb + 1 + ntiles) & 1;
@@ -608,6 +768,17 @@ __global__ __launch_bounds__(256, 1) void smla_narrow_kernel(KernelArgs a) {
     waitcnt_vm_lgkm0<0>();
 }
 
+template <int NB, bool BF16, bool TND, bool DENSE>
+__global__ __launch_bounds__(256, 1) void smla_narrow_kernel(KernelArgs a) {
+    narrow_body<NB, BF16, TND, DENSE, false>(a);
+}
+
+// The softmax_lse call for up to 64 heads on the same pipeline.
+template <int NB, bool BF16, bool TND, bool DENSE>
+__global__ __launch_bounds__(256, 1) void smla_lse_narrow_kernel(KernelArgs a) {
+    narrow_body<NB, BF16, TND, DENSE, true>(a);
+}
+
 template <int NB, bool BF16, bool TND>
 hipError_t launch_narrow_nb(const KernelArgs& a, hipStream_t stream) {
     if (a.dense)
@@ -617,6 +788,31 @@ hipError_t launch_narrow_nb(const KernelArgs& a, hipStream_t stream) {
         hipLaunchKernelGGL((smla_narrow_kernel<NB, BF16, TND, false>), dim3(a.num_wg),
                            dim3(256), 0, stream, a);
     return hipGetLastError();
+}
+
+template <int NB, bool BF16, bool TND>
+hipError_t launch_lse_narrow_nb(const KernelArgs& a, hipStream_t stream) {
+    if (a.dense)
+        hipLaunchKernelGGL((smla_lse_narrow_kernel<NB, BF16, TND, true>), dim3(a.num_wg),
+                           dim3(256), 0, stream, a);
+    else
+        hipLaunchKernelGGL((smla_lse_narrow_kernel<NB, BF16, TND, false>), dim3(a.num_wg),
+                           dim3(256), 0, stream, a);
+    return hipGetLastError();
+}
+
+template <bool BF16, bool TND>
+hipError_t launch_lse_narrow_t(const KernelArgs& a, hipStream_t stream) {
+    if (a.G <= 16) return launch_lse_narrow_nb<1, BF16, TND>(a, stream);
+    if (a.G <= 32) return launch_lse_narrow_nb<2, BF16, TND>(a, stream);
+    return launch_lse_narrow_nb<4, BF16, TND>(a, stream);
+}
+
+template <bool BF16, bool TND>
+hipError_t occupancy_lse_narrow_t(int* out) {
+    return hipOccupancyMaxActiveBlocksPerMultiprocessor(
+        out, reinterpret_cast<const void*>(&smla_lse_narrow_kernel<4, BF16, TND, false>), 256,
+        0);
 }
 
 template <bool BF16, bool TND>
@@ -640,6 +836,14 @@ hipError_t launch_narrow(const KernelArgs& a, bool bf16, bool tnd, hipStream_t s
 
 hipError_t narrow_resident_per_cu(bool bf16, bool tnd, int* out) {
     SMLA_DISPATCH2(occupancy_narrow_t, out);
+}
+
+hipError_t launch_lse_narrow(const KernelArgs& a, bool bf16, bool tnd, hipStream_t stream) {
+    SMLA_DISPATCH2(launch_lse_narrow_t, a, stream);
+}
+
+hipError_t lse_narrow_resident_per_cu(bool bf16, bool tnd, int* out) {
+    SMLA_DISPATCH2(occupancy_lse_narrow_t, out);
 }
 
 }  // namespace smla
