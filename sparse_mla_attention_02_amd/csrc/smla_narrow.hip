@@ -39,7 +39,12 @@ namespace {
 // element k has been read (a tile's operands, or a row start's Q), element
 // k + 2 is loaded into the same place, and has about two tiles to land. Q
 // (up to 64 heads, one buffer) is loaded by the waves together, so a row
-// start has two workgroup barriers: Q landed, Q read.
+// start has two workgroup barriers: Q landed, Q read. Rows of up to 16
+// heads keep Q in a place of its own instead, loaded one row ahead by wave
+// 0, and the stream holds key tiles only ([tiles of r0, tiles of r1, ...]);
+// such a row has at least two tiles (a second one without a used entry when
+// needed), so that the three rows decoded ahead always cover the five
+// elements a tile plans ahead.
 //
 // The tile loop is laid out against the issue costs measured for one wave
 // per SIMD: a v_mfma_f32_16x16x32 issues every 16.5 cycles and leaves room
@@ -145,23 +150,27 @@ struct NarElem {
     NarRow ri;
 };
 
-// The element d after element j of row r0 (j = 0: the row's Q, j = i + 1:
-// its tile i) in the stream over rows r0, r1, r2 (T tiles each; R: none).
-// Without branches, and everything by value (a choice between captured
-// references would keep the row state in memory).
+// The element d after element j of row r0 in the stream over rows r0, r1,
+// r2 (T tiles each; R: none). Each row's Q comes first (j = 0: the row's Q,
+// j = i + 1: its tile i), unless QS (the rows' Q has a place of its own):
+// then the stream holds key tiles only (j = i: tile i). Without branches,
+// and everything by value (a choice between captured references would keep
+// the row state in memory).
+template <bool QS>
 __device__ __forceinline__ NarElem nar_elem_plus(int j, int d, int32_t R, int32_t r0, int T0,
                                                  NarRow i0, int32_t r1, int T1, NarRow i1,
                                                  int32_t r2, int T2, NarRow i2) {
-    const int x0 = j + d;          // offset from r0's Q
-    const int x1 = x0 - (T0 + 1);  // from r1's Q
-    const int x2 = x1 - (T1 + 1);  // from r2's Q
-    const bool in0 = (r0 < R) & (x0 <= T0);
-    const bool in1 = !in0 & (r1 < R) & (x1 <= T1);
-    const bool in2 = !in0 & !in1 & (r2 < R) & (x2 <= T2);
+    constexpr int kQ = QS ? 0 : 1;  // a row's elements besides its tiles
+    const int x0 = j + d;           // offset from r0's first element
+    const int x1 = x0 - (T0 + kQ);  // from r1's
+    const int x2 = x1 - (T1 + kQ);  // from r2's
+    const bool in0 = (r0 < R) & (x0 < T0 + kQ);
+    const bool in1 = !in0 & (r1 < R) & (x1 < T1 + kQ);
+    const bool in2 = !in0 & !in1 & (r2 < R) & (x2 < T2 + kQ);
     const int x = in0 ? x0 : (in1 ? x1 : x2);
     NarElem e;
-    e.kind = (in0 | in1 | in2) ? (x == 0 ? kElemQ : kElemKeys) : kElemNone;
-    e.tile = x - 1;
+    e.kind = (in0 | in1 | in2) ? ((!QS && x == 0) ? kElemQ : kElemKeys) : kElemNone;
+    e.tile = x - kQ;
     e.row = in0 ? r0 : (in1 ? r1 : (in2 ? r2 : R));
     e.ri.kbase = in0 ? i0.kbase : (in1 ? i1.kbase : i2.kbase);
     e.ri.col0 = in0 ? i0.col0 : (in1 ? i1.col0 : i2.col0);
@@ -197,7 +206,14 @@ __device__ __forceinline__ void narrow_body(const KernelArgs& a) {
     constexpr int kRowStartTail = 1 + kIdx + 16 + 1 + kIdx;
     static_assert(kRowStartTail == kTileLoads, "one wait count for every tile");
     constexpr int kJsSlot0 = 4;  // index slots 4..7: the stores' indices, by tile
+    // Rows of up to 16 heads (QS) keep their Q (16 KB) in a place of its own
+    // and the stream holds key tiles only: a row start then finds its tiles
+    // 0 and 1 already loaded, reads tile 0 and Q, and loads one element
+    // (tile 2) instead of two. More heads put their Q in one of the two tile
+    // buffers (there is no room for a third).
+    constexpr bool QS = NB == 1;
     __shared__ uint4 kbuf[2][kNarKeys * kPitch];
+    __shared__ uint4 qbuf[QS ? 16 * kPitch : 1];
     // per wave: the indices of the next loads' tiles (ring of 4, by load
     // number) and of the tiles whose values are stored next (ring of 4, by
     // tile)
@@ -215,6 +231,7 @@ __device__ __forceinline__ void narrow_body(const KernelArgs& a) {
     const uint4* __restrict__ q4 = static_cast<const uint4*>(a.q);
     const char* __restrict__ kbytes = static_cast<const char*>(a.k);
     const uint32_t kbuf_lds = lds_addr(kbuf);
+    const uint32_t qbuf_lds = lds_addr(qbuf);
     const uint32_t ix_lds = lds_addr(&ixbuf[wave][0][0]);
     const uint32_t lse_lds = lds_addr(lsebuf);
     const uint32_t dummy_lds = lds_addr(dummy);
@@ -237,6 +254,10 @@ __device__ __forceinline__ void narrow_body(const KernelArgs& a) {
             if (!LSE) zero_span(a.out + r * a.W, 0, a.W, tid, NT);
             ri = nar_row(decode_row<TND>(a, r));
             T = __builtin_amdgcn_readfirstlane((ri.n + kNarKeys - 1) / kNarKeys);
+            // QS: at least two tiles (the second without a used entry), so
+            // that three decoded rows cover the five stream elements a tile
+            // plans ahead
+            if (QS && T == 1) T = 2;
             // LSE: a row without a used entry has lse -inf
             if (LSE && T == 0 && tid < a.G) a.out[r * a.G + tid] = -__builtin_inff();
             if (T > 0) return (int32_t)r;
@@ -253,7 +274,7 @@ __device__ __forceinline__ void narrow_body(const KernelArgs& a) {
     }
 
     auto elem_plus = [&](int j, int d) __attribute__((always_inline)) -> NarElem {
-        return nar_elem_plus(j, d, R, rc, Tc, ric, rn, Tn, rin, rnn, Tnn, rinn);
+        return nar_elem_plus<QS>(j, d, R, rc, Tc, ric, rn, Tn, rin, rnn, Tnn, rinn);
     };
     auto keys_elem = [&](int tile) __attribute__((always_inline)) -> NarElem {
         NarElem e;
@@ -355,14 +376,54 @@ __device__ __forceinline__ void narrow_body(const KernelArgs& a) {
         for (int i = 1; i < 16; ++i) dma_row_next(c.d, so[i], voff16, c.step);
         lse_dma(e, c);
     };
+    // QS: row `row`'s Q (its G head rows; rows past G read zeros) and its
+    // lse into their places, by wave 0 (the other waves issue nothing here:
+    // the waits that follow count only what is older than a tile's loads)
+    auto q_load = [&](int32_t row) __attribute__((always_inline)) {
+        if constexpr (QS) {
+            if (wave == 0) {
+                const bool live = row < R;
+                const i32x4_t dq =
+                    uniform_desc(raw_desc(q4 + (int64_t)(live ? row : 0) * a.G * kChunks,
+                                          live ? (uint32_t)a.G * 1024u : 0u));
+                const uint32_t m0 =
+                    (uint32_t)__builtin_amdgcn_readfirstlane((int32_t)(live ? qbuf_lds : dummy_lds));
+                const int32_t step = live ? kRowBytes : 0;
+                dma_row_first<true>(dq, m0, 0, voff16, step);
+#pragma unroll
+                for (int i = 1; i < 16; ++i) dma_row_next<true>(dq, i * 1024, voff16, step);
+                const bool lv = !LSE && live;
+                dma_dword(uniform_desc(raw_desc(a.lse + (int64_t)(lv ? row : 0) * a.G,
+                                                lv ? (uint32_t)a.G * 4u : 0u)),
+                          (uint32_t)__builtin_amdgcn_readfirstlane(
+                              (int32_t)(lv ? lse_lds : dummy_lds)),
+                          0, voff4);
+            }
+        }
+    };
 
     // ---- start: Q of the first row into buffer 0, its tile 0 into buffer 1,
     // the indices of the row start's two loads (load numbers 0 and 1) into
-    // their slots
-    int qb = 0;        // buffer holding the current row's Q
-    int ip = 0;        // load number of the current row's first load
-    NarElem pe0, pe1;  // the elements of loads ip and ip + 1
-    {
+    // their slots. QS: Q into its place, tiles 0 and 1 into buffers 0 and 1,
+    // the indices of the next two loads (tiles 2 and 3, load numbers 0 and
+    // 1) into their slots.
+    int qb = QS ? 1 : 0;  // tile t of the current row is in buffer (qb + 1 + t) & 1
+    int ip = 0;           // load number of the next load
+    NarElem pe0, pe1;     // the elements of loads ip and ip + 1
+    if constexpr (QS) {
+        const NarElem e0 = elem_plus(0, 0), e1 = elem_plus(0, 1);
+        pe0 = elem_plus(0, 2);
+        pe1 = elem_plus(0, 3);
+        idx_prefetch(rn);
+        idx_dma(kJsSlot0 + 3, e0.row, e0.tile, e0.kind == kElemKeys);
+        idx_dma(kJsSlot0 + 2, e1.row, e1.tile, e1.kind == kElemKeys);
+        idx_dma(0, pe0.row, pe0.tile, pe0.kind == kElemKeys);
+        idx_dma(1, pe1.row, pe1.tile, pe1.kind == kElemKeys);
+        q_load(rc);
+        waitcnt_vm_lgkm0<0>();
+        issue_now(e0, kJsSlot0 + 3, 0);
+        issue_now(e1, kJsSlot0 + 2, 1);
+    } else {
         NarElem eq;
         eq.kind = kElemQ;
         eq.tile = 0;
@@ -388,6 +449,49 @@ __device__ __forceinline__ void narrow_body(const KernelArgs& a) {
 
     bool find_rnn = false;
     for (;;) {
+        if constexpr (QS) {
+            // ---- row start, QS. rnn (found now: its rows are zero-filled
+            // before the wait below covers the stores). Row rc's Q and lse
+            // (loaded at the previous row start) and its tiles 0 and 1 (by
+            // the previous row's tiles, or the row start before) have landed
+            // (every wave's loads: wait, then barrier); read Q and tile 0,
+            // then load tile 2 into tile 0's place and the next row's Q and
+            // lse into theirs.
+            if (find_rnn) rnn = rn < R ? next_row(rinn, Tnn) : R;
+            find_rnn = false;
+            waitcnt_vm_lgkm0<0>();
+            asm volatile("s_barrier" ::: "memory");
+#pragma unroll
+            for (int s = 0; s < kSteps; ++s) qa[0][s] = qbuf[n * kPitch + 16 * gq + s];
+#pragma unroll
+            for (int e = 0; e < NE; ++e) {
+                const int h = 4 * gq + (e & 3);
+                if constexpr (LSE) {
+                    lm[e] = kLseFloor;
+                    ll[e] = 0.0f;
+                    l2[e] = 0.0f;
+                } else {
+                    const float v = lsebuf[h];
+                    l2[e] = h < a.G ? v * kLog2e : __builtin_inff();
+                }
+            }
+#pragma unroll
+            for (int s = 0; s < kSteps; ++s)
+                opa[s] = kbuf[(qb + 1) & 1][my_slot * kPitch + 16 * gq + s];
+            waitcnt_vm_lgkm0<63>();
+            asm volatile("s_barrier" ::: "memory");
+            {
+                const NarElem e2 = elem_plus(0, 4);
+                idx_dma((ip + 2) & 3, e2.row, e2.tile, e2.kind == kElemKeys);
+                issue_now(pe0, ip & 3, (qb + 1) & 1);
+                pe0 = pe1;
+                pe1 = e2;
+                ++ip;
+            }
+            q_load(rn);
+            idx_dma(kJsSlot0, rc, 0, true);
+            idx_prefetch(rnn);
+        } else {
         // ---- row start. rnn (found now: its rows are zero-filled before the
         // wait below covers the stores), then Q, lse and tile 0 of row rc
         // have landed (every wave's loads: wait, then barrier); read them,
@@ -433,6 +537,7 @@ __device__ __forceinline__ void narrow_body(const KernelArgs& a) {
             pe1 = e5;
             ip += 2;
         }
+        }
         const NarRow ri = ric;
         const int ntiles = Tc;
         const int32_t row = rc;
@@ -468,7 +573,7 @@ __device__ __forceinline__ void narrow_body(const KernelArgs& a) {
             const uint4* nsrc = &kbuf[nb][my_slot * kPitch + 16 * gq];
             // this load, and the load two on (its indices are loaded now)
             const NarElem E = steady ? keys_elem(t + 3) : pe0;
-            const NarElem Enew = steady ? keys_elem(t + 5) : elem_plus(t + 2, 4);
+            const NarElem Enew = steady ? keys_elem(t + 5) : elem_plus(t + (QS ? 1 : 2), 4);
             NarCtl C;
             if constexpr (steady) {
                 C.d = kdesc;
@@ -676,8 +781,8 @@ __device__ __forceinline__ void narrow_body(const KernelArgs& a) {
         if (t > 0) {
             // (tile t reads tile t+1, element t + 2 of the row: its load is
             // two elements on)
-            pe0 = elem_plus(t + 2, 2);
-            pe1 = elem_plus(t + 2, 3);
+            pe0 = elem_plus(t + (QS ? 1 : 2), 2);
+            pe1 = elem_plus(t + (QS ? 1 : 2), 3);
         }
         for (; t + 2 < ntiles; t += 2) {
             tile_body(Par<1>{}, Par<0>{}, t, opa, opb, xb, xa);
@@ -753,8 +858,9 @@ __device__ __forceinline__ void narrow_body(const KernelArgs& a) {
                                                   store_off(ntiles - 1, js), 0, 0);
         }
         if (rn >= R) break;
-        // the next row: its Q is element k + 1 + ntiles
-        qb = (qb + 1 + ntiles) & 1;
+        // the next row: its Q is element k + 1 + ntiles (QS: its tile 0 is
+        // element k + ntiles, k = this row's tile 0)
+        qb = (qb + (QS ? 0 : 1) + ntiles) & 1;
         rc = rn;
         ric = rin;
         Tc = Tn;
