@@ -254,10 +254,10 @@ __device__ __forceinline__ void narrow_body(const KernelArgs& a) {
             if (!LSE) zero_span(a.out + r * a.W, 0, a.W, tid, NT);
             ri = nar_row(decode_row<TND>(a, r));
             T = __builtin_amdgcn_readfirstlane((ri.n + kNarKeys - 1) / kNarKeys);
-            // QS: at least two tiles (the second without a used entry), so
-            // that three decoded rows cover the five stream elements a tile
-            // plans ahead
-            if (QS && T == 1) T = 2;
+            // QS: at least three tiles (the others without a used entry), so
+            // that the rows decoded ahead cover the five stream elements a
+            // tile plans ahead, a row's last tile included
+            if (QS && T > 0 && T < 3) T = 3;
             // LSE: a row without a used entry has lse -inf
             if (LSE && T == 0 && tid < a.G) a.out[r * a.G + tid] = -__builtin_inff();
             if (T > 0) return (int32_t)r;
@@ -292,8 +292,9 @@ __device__ __forceinline__ void narrow_body(const KernelArgs& a) {
         if constexpr (!DENSE) {
             const i32x4_t d = uniform_desc(raw_desc(a.idx + (int64_t)(live ? row : 0) * a.K,
                                                     live ? (uint32_t)a.K * 4u : 0u));
+            // (slot < 0: nothing to keep, into the dummy row)
             dma_dword(d, (uint32_t)__builtin_amdgcn_readfirstlane(
-                             (int32_t)(ix_lds + (uint32_t)slot * 256u)),
+                             (int32_t)(slot < 0 ? dummy_lds : ix_lds + (uint32_t)slot * 256u)),
                       0, (uint32_t)(tile * kNarKeys + my_slot) * 4u);
         }
     };
@@ -448,18 +449,24 @@ __device__ __forceinline__ void narrow_body(const KernelArgs& a) {
     f32x4_t xa[NB], xb[NB];
 
     bool find_rnn = false;
+    bool first = true;      // QS: the workgroup's first row
+    bool prev_odd = false;  // QS: the previous row had an odd number of tiles
     for (;;) {
         if constexpr (QS) {
             // ---- row start, QS. rnn (found now: its rows are zero-filled
-            // before the wait below covers the stores). Row rc's Q and lse
-            // (loaded at the previous row start) and its tiles 0 and 1 (by
-            // the previous row's tiles, or the row start before) have landed
-            // (every wave's loads: wait, then barrier); read Q and tile 0,
-            // then load tile 2 into tile 0's place and the next row's Q and
-            // lse into theirs.
+            // before the next row start's wait covers the stores). Row rc's Q
+            // and lse were loaded at the previous row start, followed by at
+            // least a tile's loads, so a wait that leaves the last tile's in
+            // flight covers them (the first row: everything); the workgroup
+            // reads them, and once it has, wave 0 loads the next row's. Tile 0
+            // was read by the previous row's last tile into the register set
+            // of its parity (the first row: read here, and its tile 2 loaded).
             if (find_rnn) rnn = rn < R ? next_row(rinn, Tnn) : R;
             find_rnn = false;
-            waitcnt_vm_lgkm0<0>();
+            if (first)
+                waitcnt_vm_lgkm0<0>();
+            else
+                waitcnt_vm_lgkm0<kTileLoads>();
             asm volatile("s_barrier" ::: "memory");
 #pragma unroll
             for (int s = 0; s < kSteps; ++s) qa[0][s] = qbuf[n * kPitch + 16 * gq + s];
@@ -475,12 +482,17 @@ __device__ __forceinline__ void narrow_body(const KernelArgs& a) {
                     l2[e] = h < a.G ? v * kLog2e : __builtin_inff();
                 }
             }
+            if (first) {
 #pragma unroll
-            for (int s = 0; s < kSteps; ++s)
-                opa[s] = kbuf[(qb + 1) & 1][my_slot * kPitch + 16 * gq + s];
+                for (int s = 0; s < kSteps; ++s)
+                    opa[s] = kbuf[(qb + 1) & 1][my_slot * kPitch + 16 * gq + s];
+            } else if (prev_odd) {
+#pragma unroll
+                for (int s = 0; s < kSteps; ++s) opa[s] = opb[s];
+            }
             waitcnt_vm_lgkm0<63>();
             asm volatile("s_barrier" ::: "memory");
-            {
+            if (first) {
                 const NarElem e2 = elem_plus(0, 4);
                 idx_dma((ip + 2) & 3, e2.row, e2.tile, e2.kind == kElemKeys);
                 issue_now(pe0, ip & 3, (qb + 1) & 1);
@@ -491,6 +503,7 @@ __device__ __forceinline__ void narrow_body(const KernelArgs& a) {
             q_load(rn);
             idx_dma(kJsSlot0, rc, 0, true);
             idx_prefetch(rnn);
+            first = false;
         } else {
         // ---- row start. rnn (found now: its rows are zero-filled before the
         // wait below covers the stores), then Q, lse and tile 0 of row rc
@@ -733,7 +746,8 @@ __device__ __forceinline__ void narrow_body(const KernelArgs& a) {
                         // tile t+1's stores and of the load two on, the 16
                         // rows (two per step, the store of tile t-1's values
                         // in step 13), the lse of a Q element
-                        idx_dma(kJsSlot0 + ((t + 1) & 3), row, t + 1, true);
+                        idx_dma((!QS || t + 1 < ntiles) ? kJsSlot0 + ((t + 1) & 3) : -1, row,
+                                t + 1, true);
                         idx_dma((ip + 2) & 3, Enew.row, Enew.tile, Enew.kind == kElemKeys);
                         dma_row_first(C.d, (uint32_t)C.m0, so[0], voff16, C.step);
                         dma_row_next(C.d, so[1], voff16, C.step);
@@ -788,11 +802,20 @@ __device__ __forceinline__ void narrow_body(const KernelArgs& a) {
             tile_body(Par<1>{}, Par<0>{}, t, opa, opb, xb, xa);
             tile_body(Par<1>{}, Par<0>{}, t + 1, opb, opa, xa, xb);
         }
+        // a row's last tile (QS, when a row follows: it reads that row's
+        // tile 0 and loads on)
+        const bool more_last = QS && rn < R;
         if (t + 1 < ntiles) {
             tile_body(Par<1>{}, Par<0>{}, t, opa, opb, xb, xa);
-            tile_body(Par<0>{}, Par<0>{}, t + 1, opb, opa, xa, xb);
+            if (more_last)
+                tile_body(Par<1>{}, Par<0>{}, t + 1, opb, opa, xa, xb);
+            else
+                tile_body(Par<0>{}, Par<0>{}, t + 1, opb, opa, xa, xb);
         } else {
-            tile_body(Par<0>{}, Par<0>{}, t, opa, opb, xb, xa);
+            if (more_last)
+                tile_body(Par<1>{}, Par<0>{}, t, opa, opb, xb, xa);
+            else
+                tile_body(Par<0>{}, Par<0>{}, t, opa, opb, xb, xa);
         }
         // the last tile's epilogue, then its stores once its indices landed
         // (the register set is picked by a branch: a reference chosen at run
@@ -809,7 +832,12 @@ __device__ __forceinline__ void narrow_body(const KernelArgs& a) {
             // group (one key each, the same heads) combine in registers, the
             // four waves (their keys) through LDS (wave 0 first), and lanes
             // below G write the row's lse
-            waitcnt_vm_lgkm0<0>();
+            // (the last tile's indices are older than its loads; with no
+            // loads of its own, wait for everything)
+            if (more_last)
+                waitcnt_vm_lgkm0<kTileLoads>();
+            else
+                waitcnt_vm_lgkm0<0>();
             const int32_t js = idx_read(kJsSlot0 + ((ntiles - 1) & 3));
             const bool ul = used_of(ri, ntiles - 1, js);
             auto last_update = [&](const f32x4_t(&x)[NB]) __attribute__((always_inline)) {
@@ -852,7 +880,10 @@ __device__ __forceinline__ void narrow_body(const KernelArgs& a) {
             }
         } else {
             const float v = (ntiles & 1) ? last_value(xa) : last_value(xb);
-            waitcnt_vm_lgkm0<0>();
+            if (more_last)
+                waitcnt_vm_lgkm0<kTileLoads>();
+            else
+                waitcnt_vm_lgkm0<0>();
             const int32_t js = idx_read(kJsSlot0 + ((ntiles - 1) & 3));
             __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, v), orsrc,
                                                   store_off(ntiles - 1, js), 0, 0);
@@ -861,6 +892,7 @@ __device__ __forceinline__ void narrow_body(const KernelArgs& a) {
         // the next row: its Q is element k + 1 + ntiles (QS: its tile 0 is
         // element k + ntiles, k = this row's tile 0)
         qb = (qb + (QS ? 0 : 1) + ntiles) & 1;
+        prev_odd = (ntiles & 1) != 0;
         rc = rn;
         ric = rin;
         Tc = Tn;
