@@ -245,3 +245,37 @@ def test_lse_score_jump_mid_row(smla, heads):
     d = np.abs(got.astype(np.float64) - want.astype(np.float64))
     assert (d <= 2e-5 * np.maximum(1.0, np.abs(want))).all(), float(d.max())
     assert np.abs(want).max() > 50  # the jump is really there
+
+
+# used entries per row: 0, 1, 2 and both sides of every multiple of 64 up to
+# 704 (1 .. 12 key tiles), in a shuffled order
+LSE_LENGTHS = sorted({0, 1, 2} | {v for m in range(64, 705, 64) for v in (m - 1, m, m + 1)
+                                   if v <= 704})
+
+
+@pytest.mark.parametrize("budget", (3, 7), ids=("cores3", "cores7"))
+@pytest.mark.parametrize("heads,layout", [(16, "BSND"), (16, "TND"), (33, "BSND"),
+                                           (64, "TND")],
+                         ids=["g16_bsnd", "g16_tnd", "g33_bsnd", "g64_tnd"])
+def test_lse_rows_of_every_length_few_workgroups(smla, heads, layout, budget):
+    """Rows of every tile count, split over a few workgroups, so that each
+    workgroup walks many rows and meets every transition between row lengths
+    (for up to 16 heads the key-tile stream runs on from row to row, and
+    short rows count extra tiles without a used entry); every row's lse
+    against the oracle's."""
+    rng = np.random.Generator(np.random.PCG64(80 + heads))
+    n = len(LSE_LENGTHS)
+    if layout == "BSND":
+        p = C.gen("tiny", heads_q=heads, batch=1, seqlen_q=2 * n, seqlen_k=800, topk=704,
+                  mask_mode=0, seed=81)
+    else:
+        p = C.gen("tnd_varlen", heads_q=heads, topk=704, mask_mode=0, seqlens_q=(n, n),
+                  seqlens_k=(800, 760), dtype="fp16", seed=82)
+    p = C.clone(p)
+    tl = np.resize(np.array(LSE_LENGTHS, dtype=np.int32), p.rows)
+    rng.shuffle(tl)
+    p.topk_length = tl.reshape(p.topk_length.shape)
+    say(f"[lse lengths] G={heads} {layout} R={p.rows} K={p.topk} cores={budget}")
+    want, _ = oracle.lse(p)
+    got = run_lse(smla, p, core_budget=budget)
+    check_lse(f"lengths g{heads} {layout} cores{budget}", got, want)
