@@ -41,10 +41,11 @@ namespace {
 // (up to 64 heads, one buffer) is loaded by the waves together, so a row
 // start has two workgroup barriers: Q landed, Q read. Rows of up to 16
 // heads keep Q in a place of its own instead, loaded one row ahead by wave
-// 0, and the stream holds key tiles only ([tiles of r0, tiles of r1, ...]);
-// such a row has at least two tiles (a second one without a used entry when
-// needed), so that the three rows decoded ahead always cover the five
-// elements a tile plans ahead.
+// 0, and the stream holds key tiles only ([tiles of r0, tiles of r1, ...]):
+// a row's last tile reads the next row's tile 0 and loads on. Such a row has
+// at least three tiles (the others without a used entry when needed), so
+// that the three rows decoded ahead always cover the five elements a tile
+// plans ahead.
 //
 // The tile loop is laid out against the issue costs measured for one wave
 // per SIMD: a v_mfma_f32_16x16x32 issues every 16.5 cycles and leaves room
@@ -200,17 +201,19 @@ __device__ __forceinline__ void narrow_body(const KernelArgs& a) {
     // Loads per tile (index loads: one per wave; the dense case has none):
     // two index loads, 16 rows, one store, one lse load. A row start issues
     // as many after tile 1's rows: that load's lse, the next element's index
-    // load, rows and lse, the index-list prefetch.
+    // load, rows and lse, the index-list prefetch. (QS: a row's tile 1 was
+    // loaded by the previous row's tiles, and the waits after a row start
+    // need only at least that many operations after each load they cover.)
     constexpr int kIdx = DENSE ? 0 : 1;
     constexpr int kTileLoads = 2 * kIdx + 16 + 1 + 1;
     constexpr int kRowStartTail = 1 + kIdx + 16 + 1 + kIdx;
     static_assert(kRowStartTail == kTileLoads, "one wait count for every tile");
     constexpr int kJsSlot0 = 4;  // index slots 4..7: the stores' indices, by tile
     // Rows of up to 16 heads (QS) keep their Q (16 KB) in a place of its own
-    // and the stream holds key tiles only: a row start then finds its tiles
-    // 0 and 1 already loaded, reads tile 0 and Q, and loads one element
-    // (tile 2) instead of two. More heads put their Q in one of the two tile
-    // buffers (there is no room for a third).
+    // and the stream holds key tiles only: a row's last tile reads the next
+    // row's tile 0 and loads on, and a row start reads only Q and lse. More
+    // heads put their Q in one of the two tile buffers (there is no room for
+    // a third).
     constexpr bool QS = NB == 1;
     __shared__ uint4 kbuf[2][kNarKeys * kPitch];
     __shared__ uint4 qbuf[QS ? 16 * kPitch : 1];
