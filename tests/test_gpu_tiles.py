@@ -20,7 +20,9 @@ same for every head count):
   zero-fills each row and stores values directly (double-buffered index
   lists; sparse, dense TND, K-wide dense);
 * up to 64 heads (16, 33, 64), up to 2048 indices per row, and more than
-  2048 (the variant without the LDS row).
+  2048 (the variant without the LDS row);
+* up to 16 heads, whose Q has a place of its own and whose key-tile stream
+  runs on across rows (5 heads, sparse; 16 heads, dense causal rows).
 
 Bar: |gpu - oracle| <= 2e-5 per element on every row, and every row with a
 used entry sums to 1 within 1e-4 (the derivation is in test_gpu_parity).
@@ -123,6 +125,15 @@ def cases():
         C.gen("tnd_varlen", heads_q=16, topk=3000, mask_mode=0, seqlens_q=(90, 60),
               seqlens_k=(3100, 3500), seed=71), seed=9,
         lens=lengths(32, 3000)[::4] + [3000])))
+    # up to 16 heads (Q in a place of its own, the key-tile stream running on
+    # across rows, short rows counting extra tiles): fewer heads than a block
+    # of 16, and dense causal rows of 1 .. 5 tiles
+    cs.append(("bsnd_fp16_g5_k700", with_lengths(
+        C.gen("tiny", heads_q=5, batch=2, seqlen_q=len(LENGTHS[:40]), seqlen_k=760,
+              topk=700, mask_mode=0, dtype="fp16", seed=74), seed=11,
+        lens=[v for v in LENGTHS if v <= 700])))
+    cs.append(("dense_bsnd_g16_causal", C.gen("tiny", heads_q=16, batch=1, seqlen_q=300,
+                                               seqlen_k=300, topk=0, mask_mode=3, seed=75)))
     cs.append(("bsnd_bf16_g128_k2600", with_lengths(
         C.gen("tiny", heads_q=128, batch=1, seqlen_q=80, seqlen_k=2700, topk=2600,
               mask_mode=0, seed=72), seed=10, lens=lengths(32, 2600)[::5] + [2600])))
