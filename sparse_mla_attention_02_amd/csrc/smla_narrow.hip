@@ -209,6 +209,10 @@ __device__ __forceinline__ void narrow_body(const KernelArgs& a) {
     constexpr int kRowStartTail = 1 + kIdx + 16 + 1 + kIdx;
     static_assert(kRowStartTail == kTileLoads, "one wait count for every tile");
     constexpr int kJsSlot0 = 4;  // index slots 4..7: the stores' indices, by tile
+    // value stores of BSND rows with the non-temporal hint (a row's values land
+    // a few to a 128-byte line; TND rows land about nine to a line, which the
+    // default policy merges in L2 first: measured 3% faster that way)
+    constexpr int kStorePolicy = TND ? 0 : 2;
     // Rows of up to 16 heads (QS) keep their Q (16 KB) in a place of its own
     // and the stream holds key tiles only: a row's last tile reads the next
     // row's tile 0 and loads on, and a row start reads only Q and lse. More
@@ -762,7 +766,7 @@ __device__ __forceinline__ void narrow_body(const KernelArgs& a) {
                 }
                 if (b == 3 && s == 13)
                     __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, val),
-                                                          orsrc, store_off(t - 1, js), 0, 0);
+                                                          orsrc, store_off(t - 1, js), 0, kStorePolicy);
                 if (more && b == 3 && s == 15) lse_dma(E, C);
             };
 #pragma unroll
@@ -889,7 +893,7 @@ __device__ __forceinline__ void narrow_body(const KernelArgs& a) {
                 waitcnt_vm_lgkm0<0>();
             const int32_t js = idx_read(kJsSlot0 + ((ntiles - 1) & 3));
             __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, v), orsrc,
-                                                  store_off(ntiles - 1, js), 0, 0);
+                                                  store_off(ntiles - 1, js), 0, kStorePolicy);
         }
         if (rn >= R) break;
         // the next row: its Q is element k + 1 + ntiles (QS: its tile 0 is
